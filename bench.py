@@ -1,0 +1,240 @@
+"""Benchmark of the MoE FFN hot path on one MI355X.
+
+A step is one full moe_ffn_forward call (router -> top-k -> expert grouping
+-> gate/up -> down -> combine) over one batch of synthetic tokens whose
+inputs are already resident in HBM.  The default workload is single-token
+decode with GELU-GLU experts (T=1, H=2816, I=704, E=128, top-8, bf16
+weights, f32 activations); --workload selects another.
+
+Decode steps rotate over a pool of distinct token vectors, so consecutive
+steps select different experts and the weights stream from HBM rather than
+from the 256 MB Infinity Cache (the full expert set is 1.5 GB).
+
+Prints one JSON line.  Fields beyond the common contract:
+  roofline      dominant kernel: algorithmic bytes (decode) or flops
+                (prefill) per launch over its average launch time, measured
+                with hipEvents on the launch stream in a second pass over
+                the same steps
+  cpu_baseline  the float64 CPU oracle timed on a bounded sample of tokens
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE FFN tokens/s; HBM GB/s at T=1, MFMA TFLOP/s at T=4096"
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--workload", default="decode_geglu_t1")
+    ap.add_argument("--pool", type=int, default=64, help="distinct token batches to rotate")
+    ap.add_argument("--eager", action="store_true", help="no HIP graph replay")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def bytes_per_weight(wf):
+    return {0: 4.0, 1: 2.0, 2: 0.5 + 4.0 / 32}[wf]
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (this build has no multi-GPU path); "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import mixture_experts_ffn_gemv_amd as M
+    from moe_synth import CONFIGS, generate, WF_U4
+    from moe_synth.generator import x_rows
+    from moe_synth.device import desc_kwargs, weights_kwargs
+
+    cfg = CONFIGS[args.workload]
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    inp = generate(cfg, backend="torch", device=dev)
+    desc = M.make_desc(**desc_kwargs(cfg))
+    w = M.make_weights(**weights_kwargs(inp))
+    T = cfg.T
+    decode = T <= 32
+    P = args.pool if decode else 1
+    # token pool: pool[0] is the generated x, the rest are fresh draws
+    xs = [inp.x]
+    for a in range(1, P):
+        xs.append(x_rows(cfg, range(T), 1000 + a, backend="torch", device=dev))
+    ws = M.alloc_workspace(desc, T, dev)
+    out = torch.empty((T, cfg.H), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        M.moe_ffn_forward(desc, xs[i % P], w, out=out, workspace=ws)
+
+    # realized expert load of pool[0] (for the algorithmic byte / flop counts)
+    r = M.moe_route(desc, xs[0], w, workspace=ws)
+    torch.cuda.synchronize()
+    counts = r.counts.cpu().numpy()
+    touched = int((counts > 0).sum())
+
+    graphs = None
+    if not args.eager:
+        graphs = []
+        s = torch.cuda.Stream()
+        s.wait_stream(stream)
+        with torch.cuda.stream(s):
+            for i in range(3):
+                step(i)
+        stream.wait_stream(s)
+        torch.cuda.synchronize()
+        for i in range(P):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(i)
+            graphs.append(g)
+        torch.cuda.synchronize()
+
+    def run(i):
+        if graphs is not None:
+            graphs[i % P].replay()
+        else:
+            step(i)
+
+    for i in range(args.warmup):
+        run(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        run(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    tokens_per_s = T * args.steps / elapsed
+
+    # ---- per-kernel durations: hipEvents around each launch, eager pass ------
+    M.timing_reset()
+    M.timing_enable(True)
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    kt = M.timing_read()
+    M.timing_enable(False)
+    kernel_ms = {k: v[1] / v[0] for k, v in kt.items()}
+
+    H, I, E, k = cfg.H, cfg.I, cfg.E, cfg.k
+    bpw = bytes_per_weight(cfg.weight_format)
+    if decode:
+        # selected-expert gate+up weight bytes streamed by one gate/up launch
+        dom = "gemv_gateup"
+        alg = touched * 2 * I * H * bpw + (2 * cfg.Is * H * bpw if cfg.shared else 0)
+        achieved = alg / (kernel_ms[dom] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": None, "algorithmic_bytes_per_launch": alg,
+                "avg_launch_us": round(kernel_ms[dom] * 1e3, 2)}
+        step_bytes = touched * 3 * I * H * bpw + (3 * cfg.Is * H * bpw if cfg.shared else 0)
+        extra = {"path_weight_bytes": step_bytes,
+                 "path_gbs": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1)}
+    else:
+        dom = "gemm_gateup"
+        R = T * k
+        fl = 2.0 * (R * 2 * I * H + (T * 2 * cfg.Is * H if cfg.shared else 0))
+        achieved = fl / (kernel_ms[dom] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1),
+                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "algorithmic_flops_per_launch": fl, "avg_launch_us": round(kernel_ms[dom] * 1e3, 2)}
+        tot = 2.0 * T * (k * 3 * I * H + (3 * cfg.Is * H if cfg.shared else 0) + (E + 1) * H)
+        extra = {"path_flops": tot, "path_tflops": round(tot / (ms_per_step * 1e-3) / 1e12, 1)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, inp, xs, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if cfg.weight_format == 1 and cfg.act_dtype == 1 else "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "T": T, "H": H, "I": I, "E": E, "top_k": k,
+                   "activation": ["silu", "gelu_tanh"][cfg.act],
+                   "weights": ["f32", "bf16", "u4_g32"][cfg.weight_format],
+                   "activations": ["f32", "bf16"][cfg.act_dtype],
+                   "shared_expert": cfg.Is if cfg.shared else 0,
+                   "touched_experts": touched, "token_pool": P,
+                   "launch": "eager" if graphs is None else "hipgraph",
+                   "parallelism": "single-gpu"},
+        "roofline": roof,
+        "kernels_us": {k2: round(v * 1e3, 2) for k2, v in kernel_ms.items()},
+        **extra,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def _host_copy(inp):
+    """numpy copy (storage format) of every input tensor, made before timing."""
+    from moe_synth.device import host_views
+    from moe_synth import U4Weights
+    hv = host_views(inp)
+    for name in ("x", "router", "router_bias", "gate", "up", "down", "shared_gate_inp",
+                 "shared_gate", "shared_up", "shared_down"):
+        v = getattr(hv, name)
+        if v is None:
+            continue
+        if isinstance(v, U4Weights):
+            setattr(hv, name, U4Weights(v.codes[:], v.scales[:], v.mins[:], v.K, v.group))
+        else:
+            setattr(hv, name, v[:])
+    return hv
+
+
+def cpu_baseline(cfg, inp, xs, seconds):
+    """The float64 CPU oracle, as it stands, on a bounded sample of tokens."""
+    from threadpoolctl import threadpool_info
+    from moe_synth.device import HostView
+    from oracle import moe_ffn, WeightSource
+
+    host = _host_copy(inp) if cfg.E * cfg.I * cfg.H * 3 <= (1 << 31) else None
+    if host is None:
+        from moe_synth.device import host_views
+        host = host_views(inp)     # too large to copy whole: slices are read on demand
+    n_done = 0
+    t_total = 0.0
+    j = 0
+    while t_total < seconds:
+        host.x = HostView(xs[j % len(xs)])[:]
+        for tok in range(cfg.T):
+            src = WeightSource(host, cache=False)
+            t0 = time.perf_counter()
+            moe_ffn(host, tokens=[tok], src=src)
+            t_total += time.perf_counter() - t0
+            n_done += 1
+            if t_total >= seconds:
+                break
+        j += 1
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": round(n_done / t_total, 3), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{n_done} tokens of {cfg.name} (drawn from the benchmark's token pool), "
+                      f"one float64 oracle call per token with its experts decoded per call; "
+                      f"inputs copied to host memory before timing"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,204 @@
+/*
+ * moe_ffn.h -- C ABI of the MI355X (gfx950) mixture-of-experts FFN library.
+ *
+ * The library computes the MoE feed-forward layer of a decoder block, in
+ * the op order that hf2q's qwen35/gpu_ffn.rs states in its module header
+ * ("MoE FFN op order"):
+ *
+ *   1. router logits      l[t,e] = x[t,:] . router[e,:] (+ router_bias[e])
+ *   2. routing            softmax over the E logits, the top_k experts by
+ *                         probability (ties: lower expert index first),
+ *                         weights renormalised over the selected experts
+ *                         (hf2q softmax_topk_renorm_cpu)
+ *   3. routed experts     for each selected expert e of token t:
+ *                         h = act(gate[e] x) * (up[e] x),  y = down[e] h
+ *                         (act = SiLU, or the tanh form of GELU used by
+ *                         mlx-native's moe_dispatch.rs)
+ *   4. combine            out[t] = sum_j w[t,j] * y[t,j]
+ *   5. shared expert      out[t] += sigmoid(x . shared_gate_inp)
+ *                                   * shared_down(silu(shared_gate x) *
+ *                                                 (shared_up x))
+ *
+ * Layouts are row-major with the last index contiguous; weight matrices are
+ * [out, in] (y = W x), the stacked-expert layout of hf2q's
+ * MoeFfnWeightsGpu and of ferrum-kernels' validate_participant bindings.
+ * Routed expert weights are stacked densely: expert e of gate/up starts at
+ * element e*I*H, expert e of down at e*H*I.
+ *
+ * Memory: every pointer argument is caller-owned device memory (hipMalloc
+ * or equivalent), except the moe_desc / moe_weights structs and the
+ * `bytes` out-parameter, which are host memory read (or written) during
+ * the call only.  The library allocates nothing per call: scratch comes
+ * from the caller's workspace, sized by moe_workspace_size (the affine
+ * workspace formula of ferrum-kernels' MoeWorkspaceLayout).
+ *
+ * Streams: calls enqueue work on `stream` (a hipStream_t; NULL = the
+ * default stream) and return without synchronising.  Buffers must stay
+ * valid until that work completes.
+ *
+ * Errors: all validation happens on the host before the first enqueue; a
+ * call that returns anything but MOE_OK has enqueued nothing and written
+ * nothing (the error-path contract of mlx-native's rejects_size_mismatch
+ * test).  moe_last_error() then returns a thread-local message.  A HIP
+ * launch failure after enqueueing started returns MOE_HIP_ERROR.
+ */
+#ifndef MOE_FFN_H
+#define MOE_FFN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_FFN_ABI_VERSION 1
+
+/* Limits (ferrum-kernels moe.rs route dispatch: at most 256 experts and
+ * 32 experts per token). */
+#define MOE_MAX_EXPERTS 256
+#define MOE_MAX_TOP_K 32
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_INVALID_ARGUMENT = 1,    /* null pointer, bad size, k > E, ...       */
+  MOE_UNSUPPORTED = 2,         /* valid but not implemented (alignment...) */
+  MOE_WORKSPACE_TOO_SMALL = 3, /* ws_bytes < moe_workspace_size(...)       */
+  MOE_HIP_ERROR = 4            /* a HIP launch failed                      */
+} moe_status;
+
+typedef enum moe_weight_format {
+  MOE_WEIGHTS_F32 = 0,
+  MOE_WEIGHTS_BF16 = 1,
+  /* affine 4-bit, groups of 32 along K: w = code * scale + min, the
+   * (scale, bias) form hf2q's dispatch_moe_id_routed passes to its affine
+   * quantized matmul.  codes: uint8 [E, N, K/2], element 2i in the low
+   * nibble of byte i, element 2i+1 in the high nibble; scales and mins:
+   * IEEE fp16 [E, N, K/32]. */
+  MOE_WEIGHTS_U4_G32 = 2
+} moe_weight_format;
+
+typedef enum moe_activation {
+  MOE_ACT_SILU = 0,       /* z / (1 + exp(-z))                              */
+  MOE_ACT_GELU_TANH = 1   /* 0.5 z (1 + tanh(0.7978845608 (z + 0.044715 z^3))) */
+} moe_activation;
+
+typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Shape and format attributes (ferrum-kernels MoeAttributes). */
+typedef struct moe_desc {
+  int32_t hidden;              /* H                                          */
+  int32_t intermediate;        /* I, routed experts                          */
+  int32_t num_experts;         /* E, 1..256                                  */
+  int32_t top_k;               /* k, 1..min(E, 32)                           */
+  int32_t activation;          /* moe_activation (routed experts)            */
+  int32_t weight_format;       /* moe_weight_format (routed and shared)      */
+  int32_t act_dtype;           /* moe_dtype of x                             */
+  int32_t router_dtype;        /* moe_dtype of router and shared_gate_inp    */
+  int32_t normalize_topk;      /* 1: renormalise the k weights; 0: raw probs */
+  int32_t has_shared_expert;   /* 0 or 1                                     */
+  int32_t shared_intermediate; /* Is (ignored without a shared expert)       */
+  int32_t group_size;          /* 32 for MOE_WEIGHTS_U4_G32, else ignored    */
+} moe_desc;
+
+typedef struct moe_u4_matrix {
+  const uint8_t* codes;    /* [E, N, K/2]  */
+  const uint16_t* scales;  /* fp16 bits [E, N, K/32] */
+  const uint16_t* mins;    /* fp16 bits [E, N, K/32] */
+} moe_u4_matrix;
+
+/* Device pointers to the layer's weights. */
+typedef struct moe_weights {
+  const void* router;          /* [E, H], router_dtype                       */
+  const float* router_bias;    /* [E] f32, or NULL                           */
+  const void* gate;            /* [E, I, H] f32/bf16 (NULL for u4)           */
+  const void* up;              /* [E, I, H]                                  */
+  const void* down;            /* [E, H, I]                                  */
+  moe_u4_matrix gate_u4;       /* used when weight_format == U4_G32          */
+  moe_u4_matrix up_u4;
+  moe_u4_matrix down_u4;
+  const void* shared_gate_inp; /* [H], router_dtype (shared expert only)     */
+  const void* shared_gate;     /* [Is, H], f32/bf16                          */
+  const void* shared_up;       /* [Is, H]                                    */
+  const void* shared_down;     /* [H, Is]                                    */
+} moe_weights;
+
+/* ABI version (MOE_FFN_ABI_VERSION of the built library). */
+int32_t moe_abi_version(void);
+
+/* Thread-local description of the last failure on this thread ("" if none). */
+const char* moe_last_error(void);
+
+/*
+ * moe_workspace_size: bytes of scratch a call with `num_tokens` tokens
+ * needs.  The size is affine in num_tokens (fixed part + per-token part),
+ * as ferrum-kernels' workspace formula is.  Host only; enqueues nothing.
+ * Errors: MOE_INVALID_ARGUMENT for a bad descriptor, num_tokens < 0 or a
+ * NULL `bytes`.
+ */
+moe_status moe_workspace_size(const moe_desc* desc, int64_t num_tokens,
+                              size_t* bytes);
+
+/*
+ * moe_route: steps 1-2 plus the expert grouping of the routes.
+ *
+ *   x              [T, H] act_dtype
+ *   topk_ids       [T, k] int32 out: slot j holds the j-th most probable
+ *                  expert (lower index first among equal probabilities)
+ *   topk_w         [T, k] f32 out: routing weights (sum to 1 per token when
+ *                  normalize_topk)
+ *   expert_counts  [E] int32 out or NULL: routes that chose each expert
+ *   expert_offsets [E+1] int32 out or NULL: exclusive prefix sum of counts
+ *   route_perm     [T*k] int32 out or NULL: the flat routes r = t*k + j
+ *                  grouped by expert, stable in r (the stable argsort of the
+ *                  flat expert ids that DS4Server's gather_sort builds):
+ *                  route_perm[expert_offsets[e] + i] is the i-th route,
+ *                  in increasing r, that chose expert e.
+ *   ws, ws_bytes   workspace, at least moe_workspace_size(desc, T) bytes
+ *
+ * Only weights->router, weights->router_bias and (with a shared expert)
+ * weights->shared_gate_inp are read.  T = 0 is a no-op.
+ */
+moe_status moe_route(const moe_desc* desc, int64_t num_tokens, const void* x,
+                     const moe_weights* weights, int32_t* topk_ids,
+                     float* topk_w, int32_t* expert_counts,
+                     int32_t* expert_offsets, int32_t* route_perm, void* ws,
+                     size_t ws_bytes, void* stream);
+
+/*
+ * moe_ffn_forward: the whole layer, steps 1-5.
+ *
+ *   x            [T, H] act_dtype
+ *   out          [T, H] f32 out (the f32 accumulator/output convention of
+ *                mlx-native's moe_weighted_sum_seq)
+ *   topk_ids_out [T, k] int32 out or NULL (as in moe_route)
+ *   topk_w_out   [T, k] f32 out or NULL
+ *   ws, ws_bytes workspace, at least moe_workspace_size(desc, T) bytes
+ *
+ * `out` must not alias x, the weights or the workspace.  T = 0 is a no-op.
+ */
+moe_status moe_ffn_forward(const moe_desc* desc, int64_t num_tokens,
+                           const void* x, const moe_weights* weights,
+                           float* out, int32_t* topk_ids_out,
+                           float* topk_w_out, void* ws, size_t ws_bytes,
+                           void* stream);
+
+/*
+ * Kernel timing, for measurement.  While enabled, every kernel the library
+ * launches is bracketed by a pair of hipEvents recorded on the call's
+ * stream.  moe_timing_read synchronises those events and returns, per
+ * kernel name (at most `max_entries`), the number of launches and the
+ * summed event-to-event milliseconds since the last reset; it returns the
+ * number of entries written, or -1 on error.  Not for use under graph
+ * capture.  Intended for benchmarks only.
+ */
+moe_status moe_timing_enable(int32_t enable);
+int32_t moe_timing_read(char* names, int32_t name_stride, int64_t* launches,
+                        double* total_ms, int32_t max_entries);
+moe_status moe_timing_reset(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_FFN_H */

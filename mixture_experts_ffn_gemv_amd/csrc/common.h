@@ -1,0 +1,84 @@
+// Shared device helpers for the gfx950 MoE FFN kernels: storage decode,
+// activations, wave-level reductions and the workspace plan shared by the
+// host launcher and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define MOE_MAX_EXPERTS_DEV 256
+
+namespace moe {
+
+constexpr int kWave = 64;
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+enum WeightFormat : int { WF_F32 = 0, WF_BF16 = 1, WF_U4 = 2 };
+enum Act : int { ACT_SILU = 0, ACT_GELU_TANH = 1 };
+
+// ------------------------------------------------------------ storage decode
+__device__ __forceinline__ float bf16lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t v) {
+  return __uint_as_float(static_cast<uint32_t>(v) << 16);
+}
+// f32 -> bf16 bits, round to nearest even (finite values).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+__device__ __forceinline__ float f16_to_f32(uint16_t v) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, v));
+}
+
+// ---------------------------------------------------------------- activations
+__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
+__device__ __forceinline__ float gelu_tanh_f(float z) {
+  // 0.5 z (1 + tanh(u)) with tanh(u) = 1 - 2 / (1 + e^{2u})
+  const float u = 0.7978845608f * (z + 0.044715f * z * z * z);
+  const float t = 1.0f - 2.0f / (1.0f + __expf(2.0f * u));
+  return 0.5f * z * (1.0f + t);
+}
+template <int ACT>
+__device__ __forceinline__ float act_f(float z) {
+  if constexpr (ACT == ACT_SILU) return silu_f(z);
+  else return gelu_tanh_f(z);
+}
+__device__ __forceinline__ float sigmoid_f(float z) { return 1.0f / (1.0f + __expf(-z)); }
+
+// ------------------------------------------------------------ wave reductions
+// Sum over aligned groups of `width` lanes (width a power of two <= 64).
+template <int WIDTH>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int o = WIDTH / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) { return group_sum<64>(v); }
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  const int l = threadIdx.x & 63;
+  return l == 0 ? 0ull : (~0ull >> (64 - l));
+}
+
+// ------------------------------------------------------------------ loads
+__device__ __forceinline__ u32x4 ld16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ u32x4 ld16_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+}  // namespace moe

@@ -1,0 +1,559 @@
+// Host side of the MoE FFN C ABI (include/moe_ffn.h): descriptor
+// validation, workspace plan, kernel selection and launches on the
+// caller's stream.  The library allocates no device memory.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/moe_ffn.h"
+#include "common.h"
+#include "gemm.h"
+#include "gemv.h"
+#include "route.h"
+
+namespace {
+
+using namespace moe;
+
+thread_local std::string g_err;
+
+moe_status fail(moe_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+// Largest token count that takes the GEMV (decode) path when the MFMA
+// path is available.
+constexpr int64_t kDecodeMaxTokens = 32;
+
+size_t align_up(size_t v, size_t a = 256) { return (v + a - 1) / a * a; }
+
+struct Plan {
+  int64_t T = 0, R = 0;
+  int E = 0, k = 0, H = 0, I = 0, Is = 0, G = 0, ncols = 0;
+  bool shared = false;
+  bool mfma = false;       // prefill path (bf16 MFMA grouped GEMM)
+  int nblk = 0;            // permutation blocks
+  int max_tiles = 0;       // grouped-GEMM route tiles (upper bound)
+  int max_groups = 0;      // active groups (upper bound)
+  // workspace offsets
+  size_t o_logits, o_ids, o_wts, o_sgate, o_bhist, o_boff, o_counts, o_offsets, o_active,
+      o_nactive, o_ntiles, o_perm, o_pos, o_rowtok, o_tgroup, o_tm0, o_h, o_hs, o_y, o_ys;
+  size_t total = 0;
+};
+
+int epc_of(int wf) { return wf == MOE_WEIGHTS_F32 ? 4 : (wf == MOE_WEIGHTS_BF16 ? 8 : 32); }
+
+moe_status check_desc(const moe_desc* d) {
+  if (!d) return fail(MOE_INVALID_ARGUMENT, "desc is NULL");
+  if (d->hidden <= 0 || d->intermediate <= 0)
+    return fail(MOE_INVALID_ARGUMENT, "hidden (%d) and intermediate (%d) must be positive",
+                d->hidden, d->intermediate);
+  if (d->num_experts < 1 || d->num_experts > MOE_MAX_EXPERTS)
+    return fail(MOE_INVALID_ARGUMENT, "num_experts %d outside 1..%d", d->num_experts,
+                MOE_MAX_EXPERTS);
+  if (d->top_k < 1 || d->top_k > d->num_experts || d->top_k > MOE_MAX_TOP_K)
+    return fail(MOE_INVALID_ARGUMENT, "top_k %d outside 1..min(num_experts=%d, %d)", d->top_k,
+                d->num_experts, MOE_MAX_TOP_K);
+  if (d->activation != MOE_ACT_SILU && d->activation != MOE_ACT_GELU_TANH)
+    return fail(MOE_INVALID_ARGUMENT, "unknown activation %d", d->activation);
+  if (d->weight_format < MOE_WEIGHTS_F32 || d->weight_format > MOE_WEIGHTS_U4_G32)
+    return fail(MOE_INVALID_ARGUMENT, "unknown weight_format %d", d->weight_format);
+  if ((d->act_dtype != MOE_F32 && d->act_dtype != MOE_BF16) ||
+      (d->router_dtype != MOE_F32 && d->router_dtype != MOE_BF16))
+    return fail(MOE_INVALID_ARGUMENT, "act_dtype/router_dtype must be MOE_F32 or MOE_BF16");
+  if (d->normalize_topk != 0 && d->normalize_topk != 1)
+    return fail(MOE_INVALID_ARGUMENT, "normalize_topk must be 0 or 1");
+  if (d->has_shared_expert != 0 && d->has_shared_expert != 1)
+    return fail(MOE_INVALID_ARGUMENT, "has_shared_expert must be 0 or 1");
+  if (d->has_shared_expert && d->shared_intermediate <= 0)
+    return fail(MOE_INVALID_ARGUMENT, "shared_intermediate must be positive");
+  if (d->has_shared_expert && d->weight_format == MOE_WEIGHTS_U4_G32)
+    return fail(MOE_UNSUPPORTED, "a shared expert with 4-bit weights is not supported");
+  if (d->weight_format == MOE_WEIGHTS_U4_G32 && d->group_size != 32)
+    return fail(MOE_UNSUPPORTED, "4-bit weights need group_size 32 (got %d)", d->group_size);
+  const int mult = 32;
+  if (d->hidden % mult || d->intermediate % mult ||
+      (d->has_shared_expert && d->shared_intermediate % mult))
+    return fail(MOE_UNSUPPORTED, "hidden, intermediate and shared_intermediate must be multiples of %d",
+                mult);
+  return MOE_OK;
+}
+
+Plan make_plan(const moe_desc* d, int64_t T) {
+  Plan p;
+  p.T = T;
+  p.E = d->num_experts;
+  p.k = d->top_k;
+  p.H = d->hidden;
+  p.I = d->intermediate;
+  p.shared = d->has_shared_expert != 0;
+  p.Is = p.shared ? d->shared_intermediate : 0;
+  p.R = T * p.k;
+  p.G = p.E + (p.shared ? 1 : 0);
+  p.ncols = p.G;
+  p.mfma = d->weight_format == MOE_WEIGHTS_BF16 && d->act_dtype == MOE_BF16 &&
+           d->router_dtype == MOE_BF16 && p.H % 64 == 0 && p.I % 64 == 0 &&
+           (!p.shared || p.Is % 64 == 0) && T > kDecodeMaxTokens;
+  p.nblk = (int)((p.R + kPermBlock - 1) / kPermBlock);
+  p.max_tiles = (int)((p.R + kTileT - 1) / kTileT) + p.E + (p.shared ? (int)((T + kTileT - 1) / kTileT) : 0);
+  p.max_groups = (int)std::min<int64_t>(p.E, p.R) + (p.shared ? 1 : 0);
+  const size_t es = p.mfma ? 2 : 4;  // h / y element size
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t r = o; o = align_up(o + bytes); return r; };
+  p.o_logits = take((size_t)T * p.ncols * 4);
+  p.o_ids = take((size_t)p.R * 4);
+  p.o_wts = take((size_t)p.R * 4);
+  p.o_sgate = take((size_t)T * 4);
+  p.o_bhist = take((size_t)p.nblk * p.E * 4);
+  p.o_boff = take((size_t)p.nblk * p.E * 4);
+  p.o_counts = take((size_t)p.G * 4);
+  p.o_offsets = take((size_t)(p.E + 1) * 4);
+  p.o_active = take((size_t)p.G * 4);
+  p.o_nactive = take(4);
+  p.o_ntiles = take(4);
+  p.o_perm = take((size_t)p.R * 4);
+  p.o_pos = take((size_t)p.R * 4);
+  p.o_rowtok = take((size_t)p.R * 4);
+  p.o_tgroup = take((size_t)p.max_tiles * 4);
+  p.o_tm0 = take((size_t)p.max_tiles * 4);
+  p.o_h = take((size_t)p.R * p.I * es);
+  p.o_hs = take((size_t)T * p.Is * es);
+  p.o_y = take((size_t)p.R * p.H * es);
+  p.o_ys = take((size_t)(p.shared ? T : 0) * p.H * es);
+  p.total = o;
+  return p;
+}
+
+bool aligned16(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; }
+
+// ---------------------------------------------------------------- timing
+struct TimingRec {
+  const char* name;
+  hipEvent_t a, b;
+};
+std::mutex g_tmu;
+bool g_timing = false;
+std::vector<TimingRec> g_pending;
+std::vector<hipEvent_t> g_evpool;
+std::map<std::string, std::pair<int64_t, double>> g_tsum;
+
+hipEvent_t ev_get() {
+  if (!g_evpool.empty()) {
+    hipEvent_t e = g_evpool.back();
+    g_evpool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+template <class F>
+moe_status launch(const char* name, hipStream_t s, F&& f) {
+  hipEvent_t a = nullptr, b = nullptr;
+  if (g_timing) {
+    std::lock_guard<std::mutex> lk(g_tmu);
+    a = ev_get();
+    b = ev_get();
+    if (a) (void)hipEventRecord(a, s);
+  }
+  f();
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(MOE_HIP_ERROR, "launch of %s failed: %s", name, hipGetErrorString(e));
+  if (g_timing && a && b) {
+    (void)hipEventRecord(b, s);
+    std::lock_guard<std::mutex> lk(g_tmu);
+    g_pending.push_back({name, a, b});
+  }
+  return MOE_OK;
+}
+
+#define MOE_TRY(x)                      \
+  do {                                  \
+    moe_status st__ = (x);              \
+    if (st__ != MOE_OK) return st__;    \
+  } while (0)
+
+template <typename T>
+T* wsp(void* ws, size_t off) {
+  return reinterpret_cast<T*>(reinterpret_cast<uint8_t*>(ws) + off);
+}
+
+// ------------------------------------------------------------ launch steps
+moe_status run_router(const moe_desc* d, const Plan& p, const void* x, const moe_weights* w,
+                      void* ws, hipStream_t s) {
+  float* logits = wsp<float>(ws, p.o_logits);
+  const int T = (int)p.T;
+  if (p.mfma) {
+    GemmParams g{};
+    g.w0 = static_cast<const uint16_t*>(w->router);
+    g.sw0 = static_cast<const uint16_t*>(w->shared_gate_inp);
+    g.bias = w->router_bias;
+    g.act = static_cast<const uint16_t*>(x);
+    g.out = logits;
+    g.E = p.E; g.T = T; g.H = p.H; g.I = p.I; g.Is = p.Is; g.ncols = p.ncols;
+    dim3 grid((T + kTileT - 1) / kTileT, (p.ncols + kTileW - 1) / kTileW);
+    return launch("router_mfma", s, [&] { k_gemm<GM_ROUTER, 0><<<grid, 256, 0, s>>>(g); });
+  }
+  const bool xb = d->act_dtype == MOE_BF16, rb = d->router_dtype == MOE_BF16;
+  dim3 grid(p.ncols);
+  return launch("router_gemv", s, [&] {
+    if (xb && rb)
+      k_router_gemv<uint16_t, 1><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(x), w->router,
+          w->router_bias, w->shared_gate_inp, logits, T, p.H, p.E, p.ncols);
+    else if (xb)
+      k_router_gemv<uint16_t, 0><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(x), w->router,
+          w->router_bias, w->shared_gate_inp, logits, T, p.H, p.E, p.ncols);
+    else if (rb)
+      k_router_gemv<float, 1><<<grid, 256, 0, s>>>(static_cast<const float*>(x), w->router,
+          w->router_bias, w->shared_gate_inp, logits, T, p.H, p.E, p.ncols);
+    else
+      k_router_gemv<float, 0><<<grid, 256, 0, s>>>(static_cast<const float*>(x), w->router,
+          w->router_bias, w->shared_gate_inp, logits, T, p.H, p.E, p.ncols);
+  });
+}
+
+moe_status run_route_and_group(const moe_desc* d, const Plan& p, void* ws, int32_t* user_ids,
+                               float* user_w, int32_t* user_counts, int32_t* user_offsets,
+                               int32_t* user_perm, hipStream_t s) {
+  const int T = (int)p.T, R = (int)p.R;
+  MOE_TRY(launch("topk", s, [&] {
+    k_topk<<<(T + 3) / 4, 256, 0, s>>>(wsp<float>(ws, p.o_logits), T, p.E, p.k, p.ncols,
+                                       d->normalize_topk, p.shared ? 1 : 0, wsp<int32_t>(ws, p.o_ids),
+                                       wsp<float>(ws, p.o_wts), user_ids, user_w,
+                                       wsp<float>(ws, p.o_sgate));
+  }));
+  MOE_TRY(launch("perm_hist", s, [&] {
+    k_perm_hist<<<p.nblk, 256, 0, s>>>(wsp<int32_t>(ws, p.o_ids), R, p.E, wsp<int32_t>(ws, p.o_bhist));
+  }));
+  ScanOut so;
+  so.counts = wsp<int32_t>(ws, p.o_counts);
+  so.offsets = wsp<int32_t>(ws, p.o_offsets);
+  so.block_off = wsp<int32_t>(ws, p.o_boff);
+  so.active = wsp<int32_t>(ws, p.o_active);
+  so.n_active = wsp<int32_t>(ws, p.o_nactive);
+  so.tile_group = wsp<int32_t>(ws, p.o_tgroup);
+  so.tile_m0 = wsp<int32_t>(ws, p.o_tm0);
+  so.n_tiles = wsp<int32_t>(ws, p.o_ntiles);
+  so.user_counts = user_counts;
+  so.user_offsets = user_offsets;
+  MOE_TRY(launch("perm_scan", s, [&] {
+    k_perm_scan<<<1, 256, 0, s>>>(wsp<int32_t>(ws, p.o_bhist), p.nblk, p.E, T, p.shared ? 1 : 0,
+                                  kTileT, p.mfma ? 1 : 0, so);
+  }));
+  return launch("perm_scatter", s, [&] {
+    k_perm_scatter<<<p.nblk, 64, 0, s>>>(wsp<int32_t>(ws, p.o_ids), R, p.E, p.k,
+                                         wsp<int32_t>(ws, p.o_boff), wsp<int32_t>(ws, p.o_perm),
+                                         wsp<int32_t>(ws, p.o_pos), wsp<int32_t>(ws, p.o_rowtok),
+                                         user_perm);
+  });
+}
+
+MatStack mat_of(const moe_desc* d, const void* dense, const moe_u4_matrix& q) {
+  MatStack m{};
+  if (d->weight_format == MOE_WEIGHTS_U4_G32) {
+    m.p = q.codes;
+    m.sc = q.scales;
+    m.mn = q.mins;
+  } else {
+    m.p = static_cast<const uint8_t*>(dense);
+  }
+  return m;
+}
+
+// rows per wave for a GEMV whose rows have `cpr` 16-byte chunks: the most
+// lanes per row that still leave each lane >= 8 chunks (8 lanes minimum).
+int pick_rw(int cpr, bool pairs) {
+  const int opts[4] = {1, 2, 4, 8};
+  for (int i = pairs ? 1 : 0; i < 4; ++i) {
+    const int lpr = 64 / opts[i];
+    if (cpr / lpr >= 8) return opts[i];
+  }
+  return 8;
+}
+
+template <int WF, int ACT, typename XT>
+void launch_gateup_rw(int rw, dim3 grid, hipStream_t s, const GemvGateUpParams& gp) {
+  switch (rw) {
+    case 2: k_dec_gateup<WF, ACT, XT, 2><<<grid, 256, 0, s>>>(gp); break;
+    case 4: k_dec_gateup<WF, ACT, XT, 4><<<grid, 256, 0, s>>>(gp); break;
+    default: k_dec_gateup<WF, ACT, XT, 8><<<grid, 256, 0, s>>>(gp); break;
+  }
+}
+template <int WF, typename XT>
+void launch_gateup_act(int act, int rw, dim3 grid, hipStream_t s, const GemvGateUpParams& gp) {
+  if (act == MOE_ACT_SILU) launch_gateup_rw<WF, ACT_SILU, XT>(rw, grid, s, gp);
+  else launch_gateup_rw<WF, ACT_GELU_TANH, XT>(rw, grid, s, gp);
+}
+template <int WF>
+void launch_gateup_x(bool xbf16, int act, int rw, dim3 grid, hipStream_t s,
+                     const GemvGateUpParams& gp) {
+  if (xbf16) launch_gateup_act<WF, uint16_t>(act, rw, grid, s, gp);
+  else launch_gateup_act<WF, float>(act, rw, grid, s, gp);
+}
+template <int WF>
+void launch_down_rw(int rw, dim3 grid, hipStream_t s, const GemvDownParams& dp) {
+  switch (rw) {
+    case 1: k_dec_down<WF, 1><<<grid, 256, 0, s>>>(dp); break;
+    case 2: k_dec_down<WF, 2><<<grid, 256, 0, s>>>(dp); break;
+    case 4: k_dec_down<WF, 4><<<grid, 256, 0, s>>>(dp); break;
+    default: k_dec_down<WF, 8><<<grid, 256, 0, s>>>(dp); break;
+  }
+}
+
+moe_status run_experts_gemv(const moe_desc* d, const Plan& p, const void* x,
+                            const moe_weights* w, float* out, void* ws, hipStream_t s) {
+  const int wf = d->weight_format;
+  const int epc = epc_of(wf);
+  GroupInfo gi;
+  gi.counts = wsp<int32_t>(ws, p.o_counts);
+  gi.offsets = wsp<int32_t>(ws, p.o_offsets);
+  gi.active = wsp<int32_t>(ws, p.o_active);
+  gi.n_active = wsp<int32_t>(ws, p.o_nactive);
+  gi.row_token = wsp<int32_t>(ws, p.o_rowtok);
+  gi.E = p.E;
+  gi.T = (int)p.T;
+
+  GemvGateUpParams gp;
+  gp.gate = mat_of(d, w->gate, w->gate_u4);
+  gp.up = mat_of(d, w->up, w->up_u4);
+  gp.sgate = MatStack{static_cast<const uint8_t*>(w->shared_gate), nullptr, nullptr};
+  gp.sup = MatStack{static_cast<const uint8_t*>(w->shared_up), nullptr, nullptr};
+  gp.x = x;
+  gp.h = wsp<float>(ws, p.o_h);
+  gp.hs = wsp<float>(ws, p.o_hs);
+  gp.gi = gi;
+  gp.H = p.H;
+  gp.I = p.I;
+  gp.Is = p.Is;
+  const int rw_gu = pick_rw(p.H / epc, true);
+  const int maxN = std::max(p.I, p.Is);
+  dim3 g1(p.max_groups, (maxN + kGemvWaves * (rw_gu / 2) - 1) / (kGemvWaves * (rw_gu / 2)));
+  const bool xb = d->act_dtype == MOE_BF16;
+  MOE_TRY(launch("gemv_gateup", s, [&] {
+    if (wf == MOE_WEIGHTS_F32) launch_gateup_x<WF_F32>(xb, d->activation, rw_gu, g1, s, gp);
+    else if (wf == MOE_WEIGHTS_BF16) launch_gateup_x<WF_BF16>(xb, d->activation, rw_gu, g1, s, gp);
+    else launch_gateup_x<WF_U4>(xb, d->activation, rw_gu, g1, s, gp);
+  }));
+
+  GemvDownParams dp;
+  dp.down = mat_of(d, w->down, w->down_u4);
+  dp.sdown = MatStack{static_cast<const uint8_t*>(w->shared_down), nullptr, nullptr};
+  dp.h = gp.h;
+  dp.hs = gp.hs;
+  dp.y = wsp<float>(ws, p.o_y);
+  dp.ys = wsp<float>(ws, p.o_ys);
+  dp.gi = gi;
+  dp.H = p.H;
+  dp.I = p.I;
+  dp.Is = p.Is;
+  const int minK = p.shared ? std::min(p.I, p.Is) : p.I;
+  const int rw_d = pick_rw(minK / epc, false);
+  dim3 g2(p.max_groups, (p.H + kGemvWaves * rw_d - 1) / (kGemvWaves * rw_d));
+  MOE_TRY(launch("gemv_down", s, [&] {
+    if (wf == MOE_WEIGHTS_F32) launch_down_rw<WF_F32>(rw_d, g2, s, dp);
+    else if (wf == MOE_WEIGHTS_BF16) launch_down_rw<WF_BF16>(rw_d, g2, s, dp);
+    else launch_down_rw<WF_U4>(rw_d, g2, s, dp);
+  }));
+
+  const size_t nthr = (size_t)p.T * (p.H / 4);
+  return launch("combine", s, [&] {
+    k_combine<float><<<(unsigned)((nthr + 255) / 256), 256, 0, s>>>(
+        dp.y, dp.ys, wsp<float>(ws, p.o_wts), wsp<int32_t>(ws, p.o_pos), wsp<float>(ws, p.o_sgate),
+        out, (int)p.T, p.H, p.k, p.shared ? 1 : 0);
+  });
+}
+
+moe_status run_experts_mfma(const moe_desc* d, const Plan& p, const void* x,
+                            const moe_weights* w, float* out, void* ws, hipStream_t s) {
+  GemmParams g{};
+  g.counts = wsp<int32_t>(ws, p.o_counts);
+  g.offsets = wsp<int32_t>(ws, p.o_offsets);
+  g.row_token = wsp<int32_t>(ws, p.o_rowtok);
+  g.tile_group = wsp<int32_t>(ws, p.o_tgroup);
+  g.tile_m0 = wsp<int32_t>(ws, p.o_tm0);
+  g.n_tiles = wsp<int32_t>(ws, p.o_ntiles);
+  g.E = p.E; g.T = (int)p.T; g.H = p.H; g.I = p.I; g.Is = p.Is; g.ncols = p.ncols;
+
+  GemmParams gu = g;
+  gu.w0 = static_cast<const uint16_t*>(w->gate);
+  gu.w1 = static_cast<const uint16_t*>(w->up);
+  gu.sw0 = static_cast<const uint16_t*>(w->shared_gate);
+  gu.sw1 = static_cast<const uint16_t*>(w->shared_up);
+  gu.act = static_cast<const uint16_t*>(x);
+  gu.out = wsp<uint16_t>(ws, p.o_h);
+  gu.sout = wsp<uint16_t>(ws, p.o_hs);
+  const int maxN = std::max(p.I, p.Is);
+  dim3 g1(p.max_tiles, (maxN + kTileW / 2 - 1) / (kTileW / 2));
+  MOE_TRY(launch("gemm_gateup", s, [&] {
+    if (d->activation == MOE_ACT_SILU) k_gemm<GM_GATEUP, ACT_SILU><<<g1, 256, 0, s>>>(gu);
+    else k_gemm<GM_GATEUP, ACT_GELU_TANH><<<g1, 256, 0, s>>>(gu);
+  }));
+
+  GemmParams gd = g;
+  gd.w0 = static_cast<const uint16_t*>(w->down);
+  gd.sw0 = static_cast<const uint16_t*>(w->shared_down);
+  gd.act = wsp<uint16_t>(ws, p.o_h);
+  gd.sact = wsp<uint16_t>(ws, p.o_hs);
+  gd.out = wsp<uint16_t>(ws, p.o_y);
+  gd.sout = wsp<uint16_t>(ws, p.o_ys);
+  dim3 g2(p.max_tiles, (p.H + kTileW - 1) / kTileW);
+  MOE_TRY(launch("gemm_down", s, [&] { k_gemm<GM_DOWN, 0><<<g2, 256, 0, s>>>(gd); }));
+
+  const size_t nthr = (size_t)p.T * (p.H / 4);
+  return launch("combine", s, [&] {
+    k_combine<uint16_t><<<(unsigned)((nthr + 255) / 256), 256, 0, s>>>(
+        wsp<uint16_t>(ws, p.o_y), wsp<uint16_t>(ws, p.o_ys), wsp<float>(ws, p.o_wts),
+        wsp<int32_t>(ws, p.o_pos), wsp<float>(ws, p.o_sgate), out, (int)p.T, p.H, p.k,
+        p.shared ? 1 : 0);
+  });
+}
+
+moe_status check_common(const moe_desc* d, int64_t T, const void* x, const moe_weights* w,
+                        void* ws, size_t ws_bytes, bool full, Plan* plan) {
+  MOE_TRY(check_desc(d));
+  if (T < 0) return fail(MOE_INVALID_ARGUMENT, "num_tokens %lld is negative", (long long)T);
+  if (T * d->top_k > INT32_MAX || T > INT32_MAX / 4)
+    return fail(MOE_UNSUPPORTED, "num_tokens %lld too large", (long long)T);
+  if (!w) return fail(MOE_INVALID_ARGUMENT, "weights is NULL");
+  *plan = make_plan(d, T);
+  if (T == 0) return MOE_OK;
+  if (!x) return fail(MOE_INVALID_ARGUMENT, "x is NULL");
+  if (!w->router) return fail(MOE_INVALID_ARGUMENT, "weights->router is NULL");
+  if (d->has_shared_expert && !w->shared_gate_inp)
+    return fail(MOE_INVALID_ARGUMENT, "weights->shared_gate_inp is NULL");
+  if (full) {
+    if (d->weight_format == MOE_WEIGHTS_U4_G32) {
+      const moe_u4_matrix* ms[3] = {&w->gate_u4, &w->up_u4, &w->down_u4};
+      for (const moe_u4_matrix* m : ms) {
+        if (!m->codes || !m->scales || !m->mins)
+          return fail(MOE_INVALID_ARGUMENT, "a 4-bit weight pointer is NULL");
+        if (!aligned16(m->codes)) return fail(MOE_UNSUPPORTED, "4-bit codes must be 16-byte aligned");
+      }
+    } else {
+      if (!w->gate || !w->up || !w->down)
+        return fail(MOE_INVALID_ARGUMENT, "gate/up/down weight pointer is NULL");
+      if (!aligned16(w->gate) || !aligned16(w->up) || !aligned16(w->down))
+        return fail(MOE_UNSUPPORTED, "expert weights must be 16-byte aligned");
+    }
+    if (d->has_shared_expert) {
+      if (!w->shared_gate || !w->shared_up || !w->shared_down)
+        return fail(MOE_INVALID_ARGUMENT, "shared expert weight pointer is NULL");
+      if (!aligned16(w->shared_gate) || !aligned16(w->shared_up) || !aligned16(w->shared_down))
+        return fail(MOE_UNSUPPORTED, "shared expert weights must be 16-byte aligned");
+    }
+  }
+  if (!aligned16(x) || !aligned16(w->router) ||
+      (d->has_shared_expert && !aligned16(w->shared_gate_inp)))
+    return fail(MOE_UNSUPPORTED, "x, router and shared_gate_inp must be 16-byte aligned");
+  if (!ws) return fail(MOE_INVALID_ARGUMENT, "workspace is NULL");
+  if (!aligned16(ws)) return fail(MOE_UNSUPPORTED, "workspace must be 16-byte aligned");
+  if (ws_bytes < plan->total)
+    return fail(MOE_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", ws_bytes, plan->total);
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_abi_version(void) { return MOE_FFN_ABI_VERSION; }
+
+const char* moe_last_error(void) { return g_err.c_str(); }
+
+moe_status moe_workspace_size(const moe_desc* desc, int64_t num_tokens, size_t* bytes) {
+  g_err.clear();
+  MOE_TRY(check_desc(desc));
+  if (num_tokens < 0) return fail(MOE_INVALID_ARGUMENT, "num_tokens is negative");
+  if (!bytes) return fail(MOE_INVALID_ARGUMENT, "bytes is NULL");
+  *bytes = make_plan(desc, num_tokens).total;
+  return MOE_OK;
+}
+
+moe_status moe_route(const moe_desc* desc, int64_t num_tokens, const void* x,
+                     const moe_weights* weights, int32_t* topk_ids, float* topk_w,
+                     int32_t* expert_counts, int32_t* expert_offsets, int32_t* route_perm,
+                     void* ws, size_t ws_bytes, void* stream) {
+  g_err.clear();
+  Plan p;
+  MOE_TRY(check_common(desc, num_tokens, x, weights, ws, ws_bytes, false, &p));
+  if (num_tokens == 0) return MOE_OK;
+  if (!topk_ids || !topk_w) return fail(MOE_INVALID_ARGUMENT, "topk_ids/topk_w is NULL");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  MOE_TRY(run_router(desc, p, x, weights, ws, s));
+  return run_route_and_group(desc, p, ws, topk_ids, topk_w, expert_counts, expert_offsets,
+                             route_perm, s);
+}
+
+moe_status moe_ffn_forward(const moe_desc* desc, int64_t num_tokens, const void* x,
+                           const moe_weights* weights, float* out, int32_t* topk_ids_out,
+                           float* topk_w_out, void* ws, size_t ws_bytes, void* stream) {
+  g_err.clear();
+  Plan p;
+  MOE_TRY(check_common(desc, num_tokens, x, weights, ws, ws_bytes, true, &p));
+  if (num_tokens == 0) return MOE_OK;
+  if (!out) return fail(MOE_INVALID_ARGUMENT, "out is NULL");
+  if (!aligned16(out)) return fail(MOE_UNSUPPORTED, "out must be 16-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  MOE_TRY(run_router(desc, p, x, weights, ws, s));
+  MOE_TRY(run_route_and_group(desc, p, ws, topk_ids_out, topk_w_out, nullptr, nullptr, nullptr, s));
+  if (p.mfma) return run_experts_mfma(desc, p, x, weights, out, ws, s);
+  return run_experts_gemv(desc, p, x, weights, out, ws, s);
+}
+
+moe_status moe_timing_enable(int32_t enable) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  g_timing = enable != 0;
+  return MOE_OK;
+}
+
+static void drain_pending() {
+  for (auto& r : g_pending) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.b) == hipSuccess && hipEventElapsedTime(&ms, r.a, r.b) == hipSuccess) {
+      auto& e = g_tsum[r.name];
+      e.first += 1;
+      e.second += ms;
+    }
+    g_evpool.push_back(r.a);
+    g_evpool.push_back(r.b);
+  }
+  g_pending.clear();
+}
+
+int32_t moe_timing_read(char* names, int32_t name_stride, int64_t* launches, double* total_ms,
+                        int32_t max_entries) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  if (!names || name_stride < 2 || !launches || !total_ms || max_entries < 0) return -1;
+  drain_pending();
+  int32_t n = 0;
+  for (auto& kv : g_tsum) {
+    if (n >= max_entries) break;
+    std::snprintf(names + (size_t)n * name_stride, name_stride, "%s", kv.first.c_str());
+    launches[n] = kv.second.first;
+    total_ms[n] = kv.second.second;
+    ++n;
+  }
+  return n;
+}
+
+moe_status moe_timing_reset(void) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  drain_pending();
+  g_tsum.clear();
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,98 @@
+"""Runs one workload through the HIP library (via the C ABI binding) and the
+CPU oracle on the same seeded inputs, and compares them."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+import mixture_experts_ffn_gemv_amd as M
+from moe_synth import generate, WF_F32, WF_BF16, WF_U4, DT_BF16
+from moe_synth.device import desc_kwargs, weights_kwargs, host_views
+from oracle import moe_oracle as O
+from oracle.cases import enforce_margin
+
+TOL = {WF_F32: 1e-4, WF_BF16: 2e-2, WF_U4: 3e-2}
+W_TOL = 1e-5
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def rel_err(gpu, ref):
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    return float(np.abs(gpu - ref).max() / max(np.abs(ref).max(), 1e-300))
+
+
+class Case:
+    """Device inputs + descriptor + weights for one configuration."""
+
+    def __init__(self, cfg, device="cuda", normalize=True):
+        import torch
+        self.cfg = cfg
+        self.normalize = normalize
+        log(f"[case] generate {cfg.name} T={cfg.T} H={cfg.H} I={cfg.I} E={cfg.E} k={cfg.k}")
+        self.dev = generate(cfg, backend="torch", device=device)
+        self.redraws = enforce_margin(self.dev)
+        torch.cuda.synchronize()
+        self.desc = M.make_desc(**desc_kwargs(cfg, normalize_topk=normalize))
+        self.weights = M.make_weights(**weights_kwargs(self.dev))
+        self.host = host_views(self.dev)
+
+    def forward(self):
+        import torch
+        log(f"[gpu] moe_ffn_forward {self.cfg.name}")
+        out, ids, w = M.moe_ffn_forward(self.desc, self.dev.x, self.weights, return_routing=True)
+        torch.cuda.synchronize()
+        return out.cpu().numpy(), ids.cpu().numpy(), w.cpu().numpy()
+
+    def route(self):
+        import torch
+        log(f"[gpu] moe_route {self.cfg.name}")
+        r = M.moe_route(self.desc, self.dev.x, self.weights)
+        torch.cuda.synchronize()
+        return {k: getattr(r, k).cpu().numpy() for k in ("ids", "weights", "counts", "offsets",
+                                                          "perm")}
+
+    # ---------------------------------------------------------------- oracle
+    def oracle_routing(self):
+        src = O.WeightSource(self.host, cache=False)
+        cfg = self.cfg
+        X = O.decode_matrix(self.host.x[:], cfg.act_dtype == DT_BF16)
+        L = O.router_logits(X, src.router(), src.router_bias())
+        ids, w = O.route(L, cfg.k, self.normalize)
+        return ids, w
+
+    def oracle_outputs(self, tokens, cache=True):
+        src = O.WeightSource(self.host, cache=cache)
+        r = O.moe_ffn(self.host, tokens=tokens, normalize=self.normalize, src=src)
+        return r["out"]
+
+
+def check_case(case: Case, sample_tokens=None, check_route=True):
+    """Full comparison; returns a dict of the measured errors."""
+    cfg = case.cfg
+    out, ids, w = case.forward()
+    ref_ids, ref_w = case.oracle_routing()
+    assert (ids == ref_ids).all(), f"routing ids differ at {np.argwhere(ids != ref_ids)[:5]}"
+    werr = float(np.abs(w - ref_w).max())
+    assert werr <= W_TOL, f"routing weights differ by {werr}"
+    res = {"w_err": werr}
+    if check_route:
+        r = case.route()
+        assert (r["ids"] == ref_ids).all()
+        assert float(np.abs(r["weights"] - ref_w).max()) <= W_TOL
+        cnt, off, perm, _ = O.permutation(ref_ids, cfg.E)
+        assert (r["counts"] == cnt).all(), "expert counts differ"
+        assert (r["offsets"] == off).all(), "expert offsets differ"
+        assert (r["perm"] == perm).all(), "route permutation differs"
+    toks = list(range(cfg.T)) if sample_tokens is None else sorted(set(sample_tokens))
+    ref = case.oracle_outputs(toks, cache=cfg.T * cfg.H * cfg.I < (1 << 26))
+    err = rel_err(out[toks], ref)
+    log(f"[parity] {cfg.name}: rel err {err:.3e} on {len(toks)} tokens, w err {werr:.2e}")
+    assert err <= TOL[cfg.weight_format], f"{cfg.name}: rel err {err} > {TOL[cfg.weight_format]}"
+    assert np.isfinite(out).all()
+    res["out_err"] = err
+    return res
