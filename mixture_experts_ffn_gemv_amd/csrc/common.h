@@ -7,6 +7,7 @@
 #include <stdint.h>
 
 #define MOE_MAX_EXPERTS_DEV 256
+#define MOE_MAX_TOP_K_DEV 32
 
 namespace moe {
 
@@ -66,7 +67,49 @@ __device__ __forceinline__ float wave_max(float v) {
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
   return v;
 }
-__device__ __forceinline__ float wave_sum(float v) { return group_sum<64>(v); }
+// DPP row operations: xor-1 and xor-2 quad permutes, then the 8-lane
+// half-mirror and the 16-lane mirror leave every lane of a 16-lane row with
+// the row's reduction; four readlanes combine the rows.  All lanes must be
+// active.  The result is wave-uniform.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, true);
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+__device__ __forceinline__ float readlane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_f<kDppXor1>(v);
+  v += dpp_f<kDppXor2>(v);
+  v += dpp_f<kDppHalfMirror>(v);
+  v += dpp_f<kDppMirror>(v);
+  return (readlane_f(v, 0) + readlane_f(v, 16)) + (readlane_f(v, 32) + readlane_f(v, 48));
+}
+// (value, index) arg-max over the wave: larger value wins, the lower index
+// on equal values.  Wave-uniform result.
+__device__ __forceinline__ void argmax_step(float& bv, int& bi, float pv, int pi) {
+  if (pv > bv || (pv == bv && pi < bi)) { bv = pv; bi = pi; }
+}
+__device__ __forceinline__ void wave_argmax(float& bv, int& bi) {
+  argmax_step(bv, bi, dpp_f<kDppXor1>(bv), dpp_i<kDppXor1>(bi));
+  argmax_step(bv, bi, dpp_f<kDppXor2>(bv), dpp_i<kDppXor2>(bi));
+  argmax_step(bv, bi, dpp_f<kDppHalfMirror>(bv), dpp_i<kDppHalfMirror>(bi));
+  argmax_step(bv, bi, dpp_f<kDppMirror>(bv), dpp_i<kDppMirror>(bi));
+  float v = readlane_f(bv, 0);
+  int i = __builtin_amdgcn_readlane(bi, 0);
+#pragma unroll
+  for (int r = 16; r < 64; r += 16) argmax_step(v, i, readlane_f(bv, r), __builtin_amdgcn_readlane(bi, r));
+  bv = v;
+  bi = i;
+}
 
 __device__ __forceinline__ uint64_t lanemask_lt() {
   const int l = threadIdx.x & 63;

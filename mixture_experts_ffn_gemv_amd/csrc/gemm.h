@@ -205,9 +205,13 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
         const int f = n0 + arow[i] + rsub;   // arow[i] < 64 here: gate rows
         if (f < Nw) {
           const f32x4 gv = acc[i][j], uv = acc[i + 2][j];
+          float hv[4];
+#pragma unroll
+          for (int v = 0; v < 4; ++v)   // the shared expert is always SwiGLU
+            hv[v] = (shared ? silu_f(gv[v]) : act_f<ACT>(gv[v])) * uv[v];
           u32x2 pk;
-          pk[0] = pack_bf16x2(act_f<ACT>(gv[0]) * uv[0], act_f<ACT>(gv[1]) * uv[1]);
-          pk[1] = pack_bf16x2(act_f<ACT>(gv[2]) * uv[2], act_f<ACT>(gv[3]) * uv[3]);
+          pk[0] = pack_bf16x2(hv[0], hv[1]);
+          pk[1] = pack_bf16x2(hv[2], hv[3]);
           *reinterpret_cast<u32x2*>(outp + f) = pk;
         }
       }

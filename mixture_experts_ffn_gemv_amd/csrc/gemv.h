@@ -153,7 +153,8 @@ __global__ __launch_bounds__(256) void k_dec_gateup(GemvGateUpParams p) {
       const float gsum = group_sum<LPR>(acc[r]);
       const float usum = __shfl(gsum, (lane + LPR) & 63, 64);
       if (!is_up && li == 0 && fvalid && r0 + r < count) {
-        const float hv = act_f<ACT>(gsum) * usum;
+        // the shared expert is always SwiGLU
+        const float hv = (shared ? silu_f(gsum) : act_f<ACT>(gsum)) * usum;
         if (shared) p.hs[(size_t)(r0 + r) * N + f] = hv;
         else p.h[(size_t)(base + r0 + r) * N + f] = hv;
       }

@@ -14,6 +14,7 @@
 #include "../../include/moe_ffn.h"
 #include "common.h"
 #include "gemm.h"
+#include "decode.h"
 #include "gemv.h"
 #include "route.h"
 
@@ -44,6 +45,8 @@ struct Plan {
   int E = 0, k = 0, H = 0, I = 0, Is = 0, G = 0, ncols = 0;
   bool shared = false;
   bool mfma = false;       // prefill path (bf16 MFMA grouped GEMM)
+  bool small = false;      // decode path (T <= 32, GEMV kernels, one-workgroup routing)
+  int rc = 0;              // decode: routes staged in LDS per pass
   int nblk = 0;            // permutation blocks
   int max_tiles = 0;       // grouped-GEMM route tiles (upper bound)
   int max_groups = 0;      // active groups (upper bound)
@@ -106,6 +109,10 @@ Plan make_plan(const moe_desc* d, int64_t T) {
   p.mfma = d->weight_format == MOE_WEIGHTS_BF16 && d->act_dtype == MOE_BF16 &&
            d->router_dtype == MOE_BF16 && p.H % 64 == 0 && p.I % 64 == 0 &&
            (!p.shared || p.Is % 64 == 0) && T > kDecodeMaxTokens;
+  p.small = !p.mfma && T <= kSmallMaxTokens &&
+            std::max(p.I, p.Is) / epc_of(d->weight_format) <= 64 * 8;
+  p.rc = (int)std::max<int64_t>(1, std::min<int64_t>({(int64_t)kRCMax, std::max<int64_t>(T, 1),
+                                                      (int64_t)(16384 / p.H)}));
   p.nblk = (int)((p.R + kPermBlock - 1) / kPermBlock);
   p.max_tiles = (int)((p.R + kTileT - 1) / kTileT) + p.E + (p.shared ? (int)((T + kTileT - 1) / kTileT) : 0);
   p.max_groups = (int)std::min<int64_t>(p.E, p.R) + (p.shared ? 1 : 0);
@@ -229,6 +236,27 @@ moe_status run_route_and_group(const moe_desc* d, const Plan& p, void* ws, int32
                                float* user_w, int32_t* user_counts, int32_t* user_offsets,
                                int32_t* user_perm, hipStream_t s) {
   const int T = (int)p.T, R = (int)p.R;
+  if (p.small) {
+    SmallRouteOut o;
+    o.ids = wsp<int32_t>(ws, p.o_ids);
+    o.wts = wsp<float>(ws, p.o_wts);
+    o.sgate = wsp<float>(ws, p.o_sgate);
+    o.counts = wsp<int32_t>(ws, p.o_counts);
+    o.offsets = wsp<int32_t>(ws, p.o_offsets);
+    o.active = wsp<int32_t>(ws, p.o_active);
+    o.n_active = wsp<int32_t>(ws, p.o_nactive);
+    o.perm = wsp<int32_t>(ws, p.o_perm);
+    o.pos_of_route = wsp<int32_t>(ws, p.o_pos);
+    o.user_ids = user_ids;
+    o.user_w = user_w;
+    o.user_counts = user_counts;
+    o.user_offsets = user_offsets;
+    o.user_perm = user_perm;
+    return launch("route_small", s, [&] {
+      k_route_small<<<1, 256, 0, s>>>(wsp<float>(ws, p.o_logits), T, p.E, p.k, p.ncols,
+                                      d->normalize_topk, p.shared ? 1 : 0, o);
+    });
+  }
   MOE_TRY(launch("topk", s, [&] {
     k_topk<<<(T + 3) / 4, 256, 0, s>>>(wsp<float>(ws, p.o_logits), T, p.E, p.k, p.ncols,
                                        d->normalize_topk, p.shared ? 1 : 0, wsp<int32_t>(ws, p.o_ids),
@@ -376,6 +404,97 @@ moe_status run_experts_gemv(const moe_desc* d, const Plan& p, const void* x,
   });
 }
 
+// chunks per lane per K block for the decode GEMVs: the smallest supported
+// count covering a row of `cpr` 16-byte chunks, at most 8
+int pick_u(int cpr) {
+  const int need = (cpr + 63) / 64;
+  const int opts[6] = {1, 2, 3, 4, 6, 8};
+  for (int o : opts)
+    if (o >= need) return o;
+  return 8;
+}
+
+template <int WF, int ACT, bool DIRECT>
+void launch_gu3_u(int u, dim3 grid, size_t lds, hipStream_t s, const Dec2Params& dp) {
+  switch (u) {
+    case 1: k_dec_gateup3<WF, ACT, 1, DIRECT><<<grid, 256, lds, s>>>(dp); break;
+    case 2: k_dec_gateup3<WF, ACT, 2, DIRECT><<<grid, 256, lds, s>>>(dp); break;
+    case 3: k_dec_gateup3<WF, ACT, 3, DIRECT><<<grid, 256, lds, s>>>(dp); break;
+    case 4: k_dec_gateup3<WF, ACT, 4, DIRECT><<<grid, 256, lds, s>>>(dp); break;
+    case 6: k_dec_gateup3<WF, ACT, 6, DIRECT><<<grid, 256, lds, s>>>(dp); break;
+    default: k_dec_gateup3<WF, ACT, 8, DIRECT><<<grid, 256, lds, s>>>(dp); break;
+  }
+}
+template <int WF, int ACT>
+void launch_gu3(bool direct, int u, dim3 grid, size_t lds, hipStream_t s, const Dec2Params& dp) {
+  if (direct) launch_gu3_u<WF, ACT, true>(u, grid, 0, s, dp);
+  else launch_gu3_u<WF, ACT, false>(u, grid, lds, s, dp);
+}
+template <int WF>
+void launch_dn3(int u, dim3 grid, hipStream_t s, const Dec2Params& dp) {
+  switch (u) {
+    case 1: k_dec_down3<WF, 1><<<grid, 256, 0, s>>>(dp); break;
+    case 2: k_dec_down3<WF, 2><<<grid, 256, 0, s>>>(dp); break;
+    case 3: k_dec_down3<WF, 3><<<grid, 256, 0, s>>>(dp); break;
+    case 4: k_dec_down3<WF, 4><<<grid, 256, 0, s>>>(dp); break;
+    case 6: k_dec_down3<WF, 6><<<grid, 256, 0, s>>>(dp); break;
+    default: k_dec_down3<WF, 8><<<grid, 256, 0, s>>>(dp); break;
+  }
+}
+
+moe_status run_experts_small(const moe_desc* d, const Plan& p, const void* x,
+                             const moe_weights* w, float* out, void* ws, hipStream_t s) {
+  const int wf = d->weight_format;
+  const int epc = epc_of(wf);
+  Dec2Params dp;
+  dp.gate = mat_of(d, w->gate, w->gate_u4);
+  dp.up = mat_of(d, w->up, w->up_u4);
+  dp.down = mat_of(d, w->down, w->down_u4);
+  dp.sgate = MatStack{static_cast<const uint8_t*>(w->shared_gate), nullptr, nullptr};
+  dp.sup = MatStack{static_cast<const uint8_t*>(w->shared_up), nullptr, nullptr};
+  dp.sdown = MatStack{static_cast<const uint8_t*>(w->shared_down), nullptr, nullptr};
+  dp.x = x;
+  dp.x_bf16 = d->act_dtype == MOE_BF16 ? 1 : 0;
+  dp.h = wsp<float>(ws, p.o_h);
+  dp.hs = wsp<float>(ws, p.o_hs);
+  dp.counts = wsp<int32_t>(ws, p.o_counts);
+  dp.offsets = wsp<int32_t>(ws, p.o_offsets);
+  dp.active = wsp<int32_t>(ws, p.o_active);
+  dp.n_active = wsp<int32_t>(ws, p.o_nactive);
+  dp.perm = wsp<int32_t>(ws, p.o_perm);
+  dp.wts = wsp<float>(ws, p.o_wts);
+  dp.sgate_val = wsp<float>(ws, p.o_sgate);
+  dp.out = out;
+  dp.T = (int)p.T; dp.E = p.E; dp.k = p.k; dp.H = p.H; dp.I = p.I; dp.Is = p.Is; dp.rc = p.rc;
+
+  const int u1 = pick_u(p.H / epc);
+  const bool direct = p.T == 1;
+  const int maxN = std::max(p.I, p.Is);
+  dim3 g1(p.max_groups, (maxN + kGUWaves - 1) / kGUWaves);
+  const size_t lds = (size_t)p.rc * p.H * 4;
+  MOE_TRY(launch("gemv_gateup", s, [&] {
+    const bool silu = d->activation == MOE_ACT_SILU;
+    if (wf == MOE_WEIGHTS_F32) {
+      if (silu) launch_gu3<WF_F32, ACT_SILU>(direct, u1, g1, lds, s, dp);
+      else launch_gu3<WF_F32, ACT_GELU_TANH>(direct, u1, g1, lds, s, dp);
+    } else if (wf == MOE_WEIGHTS_BF16) {
+      if (silu) launch_gu3<WF_BF16, ACT_SILU>(direct, u1, g1, lds, s, dp);
+      else launch_gu3<WF_BF16, ACT_GELU_TANH>(direct, u1, g1, lds, s, dp);
+    } else {
+      if (silu) launch_gu3<WF_U4, ACT_SILU>(direct, u1, g1, lds, s, dp);
+      else launch_gu3<WF_U4, ACT_GELU_TANH>(direct, u1, g1, lds, s, dp);
+    }
+  }));
+  const int maxK = std::max(p.I, p.Is);
+  const int u2 = pick_u(maxK / epc);
+  dim3 g2((p.H + kDownRPW - 1) / kDownRPW);
+  return launch("gemv_down_combine", s, [&] {
+    if (wf == MOE_WEIGHTS_F32) launch_dn3<WF_F32>(u2, g2, s, dp);
+    else if (wf == MOE_WEIGHTS_BF16) launch_dn3<WF_BF16>(u2, g2, s, dp);
+    else launch_dn3<WF_U4>(u2, g2, s, dp);
+  });
+}
+
 moe_status run_experts_mfma(const moe_desc* d, const Plan& p, const void* x,
                             const moe_weights* w, float* out, void* ws, hipStream_t s) {
   GemmParams g{};
@@ -458,6 +577,9 @@ moe_status check_common(const moe_desc* d, int64_t T, const void* x, const moe_w
   if (!aligned16(x) || !aligned16(w->router) ||
       (d->has_shared_expert && !aligned16(w->shared_gate_inp)))
     return fail(MOE_UNSUPPORTED, "x, router and shared_gate_inp must be 16-byte aligned");
+  if (!plan->mfma && d->hidden > 16384)
+    return fail(MOE_UNSUPPORTED, "hidden %d > 16384 needs bf16 weights and activations and more "
+                "than %d tokens", d->hidden, (int)kDecodeMaxTokens);
   if (!ws) return fail(MOE_INVALID_ARGUMENT, "workspace is NULL");
   if (!aligned16(ws)) return fail(MOE_UNSUPPORTED, "workspace must be 16-byte aligned");
   if (ws_bytes < plan->total)
@@ -510,6 +632,7 @@ moe_status moe_ffn_forward(const moe_desc* desc, int64_t num_tokens, const void*
   MOE_TRY(run_router(desc, p, x, weights, ws, s));
   MOE_TRY(run_route_and_group(desc, p, ws, topk_ids_out, topk_w_out, nullptr, nullptr, nullptr, s));
   if (p.mfma) return run_experts_mfma(desc, p, x, weights, out, ws, s);
+  if (p.small) return run_experts_small(desc, p, x, weights, out, ws, s);
   return run_experts_gemv(desc, p, x, weights, out, ws, s);
 }
 

@@ -87,12 +87,12 @@ __global__ __launch_bounds__(256) void k_topk(
   if (t >= T) return;
   const float* l = logits + (size_t)t * ncols;
   float v[4];
-  bool taken[4];
+  unsigned taken = 0;  // bit q: candidate q of this lane is used up (or absent)
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int e = lane + 64 * q;
     v[q] = (e < E) ? l[e] : -INFINITY;
-    taken[q] = (e >= E);
+    if (e >= E) taken |= 1u << q;
   }
   int my_id = 0;
   float my_val = -INFINITY;
@@ -101,15 +101,10 @@ __global__ __launch_bounds__(256) void k_topk(
     int bi = 0x7FFFFFFF;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      if (!taken[q] && (v[q] > bv || bi == 0x7FFFFFFF)) { bv = v[q]; bi = lane + 64 * q; }
+      if (!((taken >> q) & 1u) && (v[q] > bv || bi == 0x7FFFFFFF)) { bv = v[q]; bi = lane + 64 * q; }
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float pv = __shfl_xor(bv, o, 64);
-      const int pi = __shfl_xor(bi, o, 64);
-      if (pv > bv || (pv == bv && pi < bi)) { bv = pv; bi = pi; }
-    }
-    if ((bi & 63) == lane) taken[bi >> 6] = true;
+    wave_argmax(bv, bi);
+    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
     if (lane == j) { my_id = bi; my_val = bv; }
   }
   const float lmax = __shfl(my_val, 0, 64);
