@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--eager", action="store_true", help="no HIP graph replay")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="first run one plain device copy of this many MiB (a kernel of known "
+                         "traffic, to scale hardware byte counters)")
     return ap.parse_args()
 
 
@@ -68,6 +71,14 @@ def main():
     cfg = CONFIGS[args.workload]
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if args.calib_copy_mb:
+        n = args.calib_copy_mb << 18  # float32 elements
+        src = torch.ones(n, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     inp = generate(cfg, backend="torch", device=dev)
     desc = M.make_desc(**desc_kwargs(cfg))
     w = M.make_weights(**weights_kwargs(inp))
@@ -91,9 +102,10 @@ def main():
     counts = r.counts.cpu().numpy()
     touched = int((counts > 0).sum())
 
-    graphs = None
+    # HIP graph of the whole pool rotation (P consecutive steps): one replay
+    # runs P steps back to back, so the per-replay launch cost is amortised
+    graph = None
     if not args.eager:
-        graphs = []
         s = torch.cuda.Stream()
         s.wait_stream(stream)
         with torch.cuda.stream(s):
@@ -101,25 +113,27 @@ def main():
                 step(i)
         stream.wait_stream(s)
         torch.cuda.synchronize()
-        for i in range(P):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(P):
                 step(i)
-            graphs.append(g)
         torch.cuda.synchronize()
 
-    def run(i):
-        if graphs is not None:
-            graphs[i % P].replay()
-        else:
+    def run_steps(n):
+        """n consecutive steps: whole-pool graph replays, then single eager steps."""
+        i = 0
+        if graph is not None:
+            while n - i >= P:
+                graph.replay()
+                i += P
+        while i < n:
             step(i)
+            i += 1
 
-    for i in range(args.warmup):
-        run(i)
+    run_steps(args.warmup)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        run(i)
+    run_steps(args.steps)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / args.steps
@@ -137,10 +151,15 @@ def main():
 
     H, I, E, k = cfg.H, cfg.I, cfg.E, cfg.k
     bpw = bytes_per_weight(cfg.weight_format)
-    if decode:
+    if decode and "fused_experts" in kernel_ms:
+        # one launch streams every selected expert's gate, up and down rows
+        dom = "fused_experts"
+        alg = touched * 3 * I * H * bpw + (3 * cfg.Is * H * bpw if cfg.shared else 0)
+    elif decode:
         # selected-expert gate+up weight bytes streamed by one gate/up launch
         dom = "gemv_gateup"
         alg = touched * 2 * I * H * bpw + (2 * cfg.Is * H * bpw if cfg.shared else 0)
+    if decode:
         achieved = alg / (kernel_ms[dom] * 1e-3) / 1e9
         roof = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -177,7 +196,7 @@ def main():
                    "activations": ["f32", "bf16"][cfg.act_dtype],
                    "shared_expert": cfg.Is if cfg.shared else 0,
                    "touched_experts": touched, "token_pool": P,
-                   "launch": "eager" if graphs is None else "hipgraph",
+                   "launch": "eager" if graph is None else f"hipgraph x{P} steps",
                    "parallelism": "single-gpu"},
         "roofline": roof,
         "kernels_us": {k2: round(v * 1e3, 2) for k2, v in kernel_ms.items()},

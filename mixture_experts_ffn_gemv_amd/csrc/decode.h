@@ -68,6 +68,73 @@ __device__ __forceinline__ void wave_topk(const float* __restrict__ l, int E, in
   my_w = ex / denom;
 }
 
+constexpr int kRoutedMaxTokens = 4;
+constexpr int kRoutedMaxRoutes = kRoutedMaxTokens * MOE_MAX_TOP_K_DEV;
+
+struct RoutedLds {
+  int ids[kRoutedMaxRoutes];      // expert of route r = t*k + j
+  float w[kRoutedMaxRoutes];      // routing weight of route r
+  int perm[kRoutedMaxRoutes];     // routes grouped by expert, stable
+  int first[kRoutedMaxRoutes];    // route r is its expert's first route
+  int gexp[MOE_MAX_EXPERTS_DEV];  // expert of touched slot s (ascending)
+  int gstart[MOE_MAX_EXPERTS_DEV + 1];
+  int nrouted;
+  float sg[kRoutedMaxTokens];     // shared-expert gate per token
+};
+
+// Routing of T <= 4 tokens by one workgroup into LDS (wave t handles token t),
+// then the stable grouping of the R = T*k routes by expert with O(R^2)
+// rank counting: few barriers, no scan.
+__device__ __forceinline__ void route_tokens_lds(const float* __restrict__ logits, int T, int E,
+                                                 int k, int ncols, int normalize, int has_shared,
+                                                 RoutedLds& L) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int R = T * k;
+  if (wave < T) {
+    const float* l = logits + (size_t)wave * ncols;
+    int id;
+    float w;
+    wave_topk(l, E, k, normalize, lane, id, w);
+    if (lane < k) {
+      L.ids[wave * k + lane] = id;
+      L.w[wave * k + lane] = w;
+    }
+    if (lane == 0) L.sg[wave] = has_shared ? sigmoid_f(l[E]) : 0.f;
+  }
+  __syncthreads();
+  // stable position of each route in expert order, and first-of-expert flags
+  if (tid < R) {
+    const int e = L.ids[tid];
+    int less = 0, first = 1;
+    for (int r2 = 0; r2 < R; ++r2) {
+      const int e2 = L.ids[r2];
+      less += (e2 < e) || (e2 == e && r2 < tid);
+      first &= !(e2 == e && r2 < tid);
+    }
+    L.perm[less] = tid;
+    L.first[tid] = first;
+  }
+  __syncthreads();
+  if (tid < R && L.first[tid]) {
+    const int e = L.ids[tid];
+    int slot = 0, start = 0;
+    for (int r2 = 0; r2 < R; ++r2) {
+      const int e2 = L.ids[r2];
+      slot += (e2 < e) && L.first[r2];
+      start += (e2 < e);
+    }
+    L.gexp[slot] = e;
+    L.gstart[slot] = start;
+  }
+  if (tid == 0) {
+    int n = 0;
+    for (int r2 = 0; r2 < R; ++r2) n += L.first[r2];
+    L.nrouted = n;
+    L.gstart[n] = R;
+  }
+  __syncthreads();
+}
+
 struct SmallRouteOut {
   int32_t* ids;          // [R]
   float* wts;            // [R]
@@ -92,8 +159,47 @@ __global__ __launch_bounds__(256) void k_route_small(const float* __restrict__ l
   __shared__ int s_cnt[256];
   __shared__ int s_sc[256];
   __shared__ int s_sa[256];
+  __shared__ RoutedLds L;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int R = T * k;
+  if (T <= kRoutedMaxTokens) {
+    route_tokens_lds(logits, T, E, k, ncols, normalize, has_shared, L);
+    for (int r = tid; r < R; r += 256) {
+      o.ids[r] = L.ids[r];
+      o.wts[r] = L.w[r];
+      o.perm[r] = L.perm[r];
+      o.pos_of_route[L.perm[r]] = r;
+      if (o.user_ids) o.user_ids[r] = L.ids[r];
+      if (o.user_w) o.user_w[r] = L.w[r];
+      if (o.user_perm) o.user_perm[r] = L.perm[r];
+    }
+    // per-expert counts and offsets over all E experts
+    for (int e = tid; e <= E; e += 256) {
+      int less = 0, eq = 0;
+      for (int r = 0; r < R; ++r) {
+        less += L.ids[r] < e;
+        eq += L.ids[r] == e;
+      }
+      o.offsets[e] = less;
+      if (o.user_offsets) o.user_offsets[e] = less;
+      if (e < E) {
+        o.counts[e] = eq;
+        if (o.user_counts) o.user_counts[e] = eq;
+      }
+    }
+    const int nrouted = L.nrouted;
+    for (int sl = tid; sl < nrouted; sl += 256) o.active[sl] = L.gexp[sl];
+    if (tid < T && has_shared) o.sgate[tid] = L.sg[tid];
+    if (tid == 0) {
+      int na = nrouted;
+      if (has_shared) {
+        o.counts[E] = T;
+        o.active[na++] = E;
+      }
+      *o.n_active = na;
+    }
+    return;
+  }
   s_cnt[tid] = 0;
   for (int t = wave; t < T; t += 4) {
     const float* l = logits + (size_t)t * ncols;

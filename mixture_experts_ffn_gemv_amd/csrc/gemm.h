@@ -1,17 +1,19 @@
 // bf16 MFMA grouped GEMM for many tokens per expert (prefill).
 //
 // Each workgroup computes a 128 (weight rows) x 128 (routes) tile of
-// C^T = W . X^T over K in steps of 64, with v_mfma_f32_16x16x32_bf16 and
-// f32 accumulation.  Weights are the MFMA "A" operand, the gathered route
-// activations the "B" operand, so each lane ends up holding four
-// consecutive output features of one route: epilogue stores are 8-byte
-// contiguous runs of a route's row.
+// C^T = W . X^T over K in steps of 64, with v_mfma_f32_32x32x16_bf16 and
+// f32 accumulation (on gfx950 the 32x32x16 form sustains about 90% of the
+// bf16 peak with one wave per SIMD, the 16x16x32 form about half of it).
+// Each wave owns a 64 x 64 sub-tile: 2 x 2 blocks of 32x32.  Weights are
+// the MFMA "A" operand, the gathered route activations the "B" operand, so
+// each lane ends up holding runs of four consecutive output features of one
+// route: epilogue stores are 8-byte contiguous pieces of a route's row.
 //
 // The route tiles come from a flat list (group, first row) built after the
 // expert grouping, so a skewed load only changes the number of tiles, not
 // their shape.  A and B tiles are staged through LDS (double-buffered, the
-// 16-byte chunks of each 128-byte row XOR-swizzled by row & 7 so the
-// ds_read_b128 fragment loads are bank-conflict free).
+// 16-byte chunks of each 128-byte row XOR-swizzled so the ds_read_b128
+// fragment loads are bank-conflict free, see swz).
 //
 // Modes:
 //   GATEUP : rows 0..63 of the weight tile are gate rows n0..n0+63, rows
@@ -54,7 +56,38 @@ struct GemmParams {
   int E, T, H, I, Is, ncols;
 };
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * 64 + ((chunk ^ (row & 7)) << 3); }
+// LDS tiles are rows of 64 bf16 (128 bytes = 8 chunks of 16 bytes).  A
+// ds_read_b128 is served 16 lanes at a time over a 256-byte bank window, and a
+// fragment read touches one chunk of 16 consecutive rows: XOR-ing the chunk
+// index with (row >> 1) & 7 puts the 8 even rows (and the 8 odd rows) on 8
+// different chunks, so the 16 lanes hit 16 distinct bank groups.
+__device__ __forceinline__ int swz(int row, int chunk) {
+  return row * 64 + ((chunk ^ ((row >> 1) & 7)) << 3);
+}
+
+// Hardware deals workgroups round-robin over the 8 XCDs (block b -> XCD b%8).
+// xcd_remap turns the dispatch index into a logical index such that each
+// XCD receives a contiguous range of logical tiles.
+__device__ __forceinline__ int xcd_remap(int b, int total) {
+  const int q = total / 8, r = total % 8, x = b % 8, i = b / 8;
+  return (x < r) ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
+}
+
+// Grouped order over (route tile, weight tile): groups of kGroupT route tiles
+// x all weight tiles, route tiles fastest.  With the XCD remap, the ~64
+// workgroups resident on one XCD cover about kGroupT route tiles x 8 weight
+// tiles, so each weight slice is fetched into that XCD's L2 once for up to
+// kGroupT route tiles of the same expert, and each gathered route tile once
+// for 8 weight slices.
+constexpr int kGroupT = 8;
+__device__ __forceinline__ void grouped_tile(int L, int ntt, int nnt, int& tt, int& nt) {
+  const int gsz = kGroupT * nnt;
+  const int grp = L / gsz, r = L - grp * gsz;
+  const int t0 = grp * kGroupT;
+  const int gt = min(kGroupT, ntt - t0);  // last group may be narrower
+  tt = t0 + r % gt;
+  nt = r / gt;
+}
 
 template <int MODE, int ACT>
 __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
@@ -66,12 +99,18 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
 
   // ---- tile -> (group, rows, weights) --------------------------------------
   int g, m0, count, base;
+  int nt_override = blockIdx.y;
   bool shared;
   if constexpr (MODE == GM_ROUTER) {
     g = 0; shared = false; m0 = blockIdx.x * kTileT; count = p.T; base = 0;
     if (m0 >= count) return;
   } else {
-    const int ti = blockIdx.x;
+    // grid is (max route tiles, weight tiles); see grouped_tile
+    const int ntt = gridDim.x, nnt = gridDim.y;
+    const int L = xcd_remap(blockIdx.y * ntt + blockIdx.x, ntt * nnt);
+    int ti, ntile;
+    grouped_tile(L, ntt, nnt, ti, ntile);
+    nt_override = ntile;
     if (ti >= *p.n_tiles) return;
     g = p.tile_group[ti];
     m0 = p.tile_m0[ti];
@@ -84,7 +123,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
   else if constexpr (MODE == GM_DOWN) { K = shared ? p.Is : p.I; Nw = p.H; }
   else { K = p.H; Nw = p.ncols; }
   const int nstep = (MODE == GM_GATEUP) ? kTileW / 2 : kTileW;
-  const int n0 = blockIdx.y * nstep;
+  const int n0 = nt_override * nstep;
   if (n0 >= Nw) return;
 
   // ---- per-thread global load assignments (4 chunks of A, 4 of B) ----------
@@ -97,37 +136,33 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
     const int row = q >> 3, ck = q & 7;
     a_lds[i] = swz(row, ck);
     b_lds[i] = swz(row, ck);
-    // weight row
-    const uint16_t* wp = nullptr;
+    // weight row; rows past the end are clamped to the last valid row (their
+    // results are never stored), so the loads need no branch
+    const uint16_t* wp;
     if constexpr (MODE == GM_GATEUP) {
-      const int f = n0 + (row & 63);
-      if (f < Nw) {
-        const uint16_t* m = (row < 64) ? (shared ? p.sw0 : p.w0) : (shared ? p.sw1 : p.w1);
-        wp = m + ((shared ? 0 : (size_t)g * Nw) + f) * (size_t)K;
-      }
+      const int f = min(n0 + (row & 63), Nw - 1);
+      const uint16_t* m = (row < 64) ? (shared ? p.sw0 : p.w0) : (shared ? p.sw1 : p.w1);
+      wp = m + ((shared ? 0 : (size_t)g * Nw) + f) * (size_t)K;
     } else if constexpr (MODE == GM_DOWN) {
-      const int n = n0 + row;
-      if (n < Nw) wp = (shared ? p.sw0 : p.w0) + ((shared ? 0 : (size_t)g * Nw) + n) * (size_t)K;
+      const int n = min(n0 + row, Nw - 1);
+      wp = (shared ? p.sw0 : p.w0) + ((shared ? 0 : (size_t)g * Nw) + n) * (size_t)K;
     } else {
-      const int e = n0 + row;
-      if (e < p.E) wp = p.w0 + (size_t)e * K;
-      else if (e < p.ncols) wp = p.sw0;
+      const int e = min(n0 + row, p.ncols - 1);
+      wp = (e < p.E) ? p.w0 + (size_t)e * K : p.sw0;
     }
-    a_src[i] = wp ? wp + ck * 8 : nullptr;
-    // route row
-    const int m = m0 + row;
-    const uint16_t* ap = nullptr;
-    if (m < count) {
-      if constexpr (MODE == GM_DOWN) {
-        ap = shared ? p.sact + (size_t)m * K : p.act + (size_t)(base + m) * K;
-      } else if constexpr (MODE == GM_GATEUP) {
-        const int t = shared ? m : p.row_token[base + m];
-        ap = p.act + (size_t)t * K;
-      } else {
-        ap = p.act + (size_t)m * K;
-      }
+    a_src[i] = wp + ck * 8;
+    // route row, clamped the same way
+    const int m = min(m0 + row, count - 1);
+    const uint16_t* ap;
+    if constexpr (MODE == GM_DOWN) {
+      ap = shared ? p.sact + (size_t)m * K : p.act + (size_t)(base + m) * K;
+    } else if constexpr (MODE == GM_GATEUP) {
+      const int t = shared ? m : p.row_token[base + m];
+      ap = p.act + (size_t)t * K;
+    } else {
+      ap = p.act + (size_t)m * K;
     }
-    b_src[i] = ap ? ap + ck * 8 : nullptr;
+    b_src[i] = ap + ck * 8;
   }
 
   u32x4 ra[4], rb[4];
@@ -135,8 +170,8 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
     const int ko = kt * kTileK;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      ra[i] = a_src[i] ? ld16(a_src[i] + ko) : u32x4{0, 0, 0, 0};
-      rb[i] = b_src[i] ? ld16(b_src[i] + ko) : u32x4{0, 0, 0, 0};
+      ra[i] = ld16(a_src[i] + ko);
+      rb[i] = ld16(b_src[i] + ko);
     }
   };
   auto lstore = [&](int buf) {
@@ -147,68 +182,72 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
     }
   };
 
-  // ---- wave sub-tile: 4 weight blocks x 4 route blocks of 16x16 ------------
+  // ---- wave sub-tile: 2 weight blocks x 2 route blocks of 32x32 ------------
+  // GATEUP: weight block 0 = gate rows [32ww, +32), block 1 = the up rows of
+  // the same features (tile rows 64 + 32ww ...).  Otherwise rows [64ww, +64).
   const int ww = wave & 1, wt = wave >> 1;
-  int arow[4], brow[4];
+  int arow[2], brow[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if constexpr (MODE == GM_GATEUP) arow[i] = (i < 2 ? 0 : 64) + 32 * ww + 16 * (i & 1);
-    else arow[i] = 64 * ww + 16 * i;
-    brow[i] = 64 * wt + 16 * i;
+  for (int i = 0; i < 2; ++i) {
+    if constexpr (MODE == GM_GATEUP) arow[i] = 64 * i + 32 * ww;
+    else arow[i] = 64 * ww + 32 * i;
+    brow[i] = 64 * wt + 32 * i;
   }
-  f32x4 acc[4][4];
+  f32x16 acc[2][2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
   const int nk = K / kTileK;
   gload(0);
   lstore(0);
   __syncthreads();
-  const int fr = lane & 15, fk = lane >> 4;
+  const int fr = lane & 31, fk = lane >> 5;
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & 1;
     if (kt + 1 < nk) gload(kt + 1);
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      bf16x8 af[4], bfr[4];
+    for (int s = 0; s < 4; ++s) {  // 4 k-steps of 16
+      bf16x8 af[2], bfr[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int ra_ = arow[i] + fr;
-        af[i] = *reinterpret_cast<const bf16x8*>(&sA[buf][swz(ra_, 4 * s + fk)]);
-        const int rb_ = brow[i] + fr;
-        bfr[i] = *reinterpret_cast<const bf16x8*>(&sB[buf][swz(rb_, 4 * s + fk)]);
+      for (int i = 0; i < 2; ++i) {
+        af[i] = *reinterpret_cast<const bf16x8*>(&sA[buf][swz(arow[i] + fr, 2 * s + fk)]);
+        bfr[i] = *reinterpret_cast<const bf16x8*>(&sB[buf][swz(brow[i] + fr, 2 * s + fk)]);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
     if (kt + 1 < nk) lstore(buf ^ 1);
     __syncthreads();
   }
 
   // ---- epilogue -------------------------------------------------------------
-  // acc[i][j][v]: weight row arow[i] + 4*(lane>>4) + v, route brow[j] + (lane&15)
-  const int rsub = 4 * (lane >> 4);
+  // acc[i][j][4q + v]: weight row arow[i] + 8q + 4*(lane>>5) + v,
+  //                    route brow[j] + (lane & 31)
+  const int rsub = 4 * (lane >> 5);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int m = m0 + brow[j] + (lane & 15);
+  for (int j = 0; j < 2; ++j) {
+    const int m = m0 + brow[j] + (lane & 31);
     if (m >= count) continue;
     if constexpr (MODE == GM_GATEUP) {
       uint16_t* outp = shared ? reinterpret_cast<uint16_t*>(p.sout) + (size_t)m * Nw
                               : reinterpret_cast<uint16_t*>(p.out) + (size_t)(base + m) * Nw;
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int f = n0 + arow[i] + rsub;   // arow[i] < 64 here: gate rows
+      for (int q = 0; q < 4; ++q) {
+        const int f = n0 + arow[0] + 8 * q + rsub;   // gate rows: tile rows < 64
         if (f < Nw) {
-          const f32x4 gv = acc[i][j], uv = acc[i + 2][j];
           float hv[4];
 #pragma unroll
-          for (int v = 0; v < 4; ++v)   // the shared expert is always SwiGLU
-            hv[v] = (shared ? silu_f(gv[v]) : act_f<ACT>(gv[v])) * uv[v];
+          for (int v = 0; v < 4; ++v) {  // the shared expert is always SwiGLU
+            const float gv = acc[0][j][4 * q + v], uv = acc[1][j][4 * q + v];
+            hv[v] = (shared ? silu_f(gv) : act_f<ACT>(gv)) * uv;
+          }
           u32x2 pk;
           pk[0] = pack_bf16x2(hv[0], hv[1]);
           pk[1] = pack_bf16x2(hv[2], hv[3]);
@@ -219,25 +258,28 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
       uint16_t* outp = shared ? reinterpret_cast<uint16_t*>(p.sout) + (size_t)m * Nw
                               : reinterpret_cast<uint16_t*>(p.out) + (size_t)(base + m) * Nw;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int n = n0 + arow[i] + rsub;
-        if (n < Nw) {
-          const f32x4 v = acc[i][j];
-          u32x2 pk;
-          pk[0] = pack_bf16x2(v[0], v[1]);
-          pk[1] = pack_bf16x2(v[2], v[3]);
-          *reinterpret_cast<u32x2*>(outp + n) = pk;
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int n = n0 + arow[i] + 8 * q + rsub;
+          if (n < Nw) {
+            u32x2 pk;
+            pk[0] = pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
+            pk[1] = pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+            *reinterpret_cast<u32x2*>(outp + n) = pk;
+          }
         }
-      }
     } else {
       float* outp = reinterpret_cast<float*>(p.out) + (size_t)m * p.ncols;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int e = n0 + arow[i] + rsub + v;
-          if (e < p.ncols) outp[e] = acc[i][j][v] + ((e < p.E && p.bias) ? p.bias[e] : 0.f);
-        }
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int e = n0 + arow[i] + 8 * q + rsub + v;
+            if (e < p.ncols) outp[e] = acc[i][j][4 * q + v] + ((e < p.E && p.bias) ? p.bias[e] : 0.f);
+          }
     }
   }
 }
