@@ -14,6 +14,7 @@
 #include "../../include/moe_ffn.h"
 #include "common.h"
 #include "gemm.h"
+#include "gemm_big.h"
 #include "decode.h"
 #include "gemv.h"
 #include "route.h"
@@ -49,6 +50,7 @@ struct Plan {
   int rc = 0;              // decode: routes staged in LDS per pass
   int nblk = 0;            // permutation blocks
   int max_tiles = 0;       // grouped-GEMM route tiles (upper bound)
+  int bt = 128;            // grouped-GEMM route-tile height
   int max_groups = 0;      // active groups (upper bound)
   // workspace offsets
   size_t o_logits, o_ids, o_wts, o_sgate, o_bhist, o_boff, o_counts, o_offsets, o_active,
@@ -114,7 +116,9 @@ Plan make_plan(const moe_desc* d, int64_t T) {
   p.rc = (int)std::max<int64_t>(1, std::min<int64_t>({(int64_t)kRCMax, std::max<int64_t>(T, 1),
                                                       (int64_t)(16384 / p.H)}));
   p.nblk = (int)((p.R + kPermBlock - 1) / kPermBlock);
-  p.max_tiles = (int)((p.R + kTileT - 1) / kTileT) + p.E + (p.shared ? (int)((T + kTileT - 1) / kTileT) : 0);
+  // 256-route tiles when the experts average that many routes, else 128
+  p.bt = 128;
+  p.max_tiles = (int)((p.R + p.bt - 1) / p.bt) + p.E + (p.shared ? (int)((T + p.bt - 1) / p.bt) : 0);
   p.max_groups = (int)std::min<int64_t>(p.E, p.R) + (p.shared ? 1 : 0);
   const size_t es = p.mfma ? 2 : 4;  // h / y element size
   size_t o = 0;
@@ -279,7 +283,7 @@ moe_status run_route_and_group(const moe_desc* d, const Plan& p, void* ws, int32
   so.user_offsets = user_offsets;
   MOE_TRY(launch("perm_scan", s, [&] {
     k_perm_scan<<<1, 256, 0, s>>>(wsp<int32_t>(ws, p.o_bhist), p.nblk, p.E, T, p.shared ? 1 : 0,
-                                  kTileT, p.mfma ? 1 : 0, so);
+                                  p.bt, p.mfma ? 1 : 0, so);
   }));
   return launch("perm_scatter", s, [&] {
     k_perm_scatter<<<p.nblk, 64, 0, s>>>(wsp<int32_t>(ws, p.o_ids), R, p.E, p.k,
@@ -515,10 +519,16 @@ moe_status run_experts_mfma(const moe_desc* d, const Plan& p, const void* x,
   gu.out = wsp<uint16_t>(ws, p.o_h);
   gu.sout = wsp<uint16_t>(ws, p.o_hs);
   const int maxN = std::max(p.I, p.Is);
-  dim3 g1(p.max_tiles, (maxN + kTileW / 2 - 1) / (kTileW / 2));
+  dim3 g1(p.max_tiles, (maxN + kBW / 2 - 1) / (kBW / 2));
   MOE_TRY(launch("gemm_gateup", s, [&] {
-    if (d->activation == MOE_ACT_SILU) k_gemm<GM_GATEUP, ACT_SILU><<<g1, 256, 0, s>>>(gu);
-    else k_gemm<GM_GATEUP, ACT_GELU_TANH><<<g1, 256, 0, s>>>(gu);
+    const bool silu = d->activation == MOE_ACT_SILU;
+    if (p.bt == 256) {
+      if (silu) k_gemm_big<GM_GATEUP, ACT_SILU, 256><<<g1, 256, 0, s>>>(gu);
+      else k_gemm_big<GM_GATEUP, ACT_GELU_TANH, 256><<<g1, 256, 0, s>>>(gu);
+    } else {
+      if (silu) k_gemm_big<GM_GATEUP, ACT_SILU, 128><<<g1, 256, 0, s>>>(gu);
+      else k_gemm_big<GM_GATEUP, ACT_GELU_TANH, 128><<<g1, 256, 0, s>>>(gu);
+    }
   }));
 
   GemmParams gd = g;
@@ -528,8 +538,11 @@ moe_status run_experts_mfma(const moe_desc* d, const Plan& p, const void* x,
   gd.sact = wsp<uint16_t>(ws, p.o_hs);
   gd.out = wsp<uint16_t>(ws, p.o_y);
   gd.sout = wsp<uint16_t>(ws, p.o_ys);
-  dim3 g2(p.max_tiles, (p.H + kTileW - 1) / kTileW);
-  MOE_TRY(launch("gemm_down", s, [&] { k_gemm<GM_DOWN, 0><<<g2, 256, 0, s>>>(gd); }));
+  dim3 g2(p.max_tiles, (p.H + kBW - 1) / kBW);
+  MOE_TRY(launch("gemm_down", s, [&] {
+    if (p.bt == 256) k_gemm_big<GM_DOWN, 0, 256><<<g2, 256, 0, s>>>(gd);
+    else k_gemm_big<GM_DOWN, 0, 128><<<g2, 256, 0, s>>>(gd);
+  }));
 
   const size_t nthr = (size_t)p.T * (p.H / 4);
   return launch("combine", s, [&] {
