@@ -13,8 +13,12 @@ from the 256 MB Infinity Cache (the full expert set is 1.5 GB).
 Prints one JSON line.  Fields beyond the common contract:
   roofline      dominant kernel: algorithmic bytes (decode) or flops
                 (prefill) per launch over its average launch time, measured
-                with hipEvents on the launch stream in a second pass over
-                the same steps
+                with hipEvents recorded on the launch stream around every
+                launch, in a second (eager) pass over the same K steps;
+                traffic = HBM bytes per launch (FETCH_SIZE + WRITE_SIZE,
+                scaled by a plain copy of known size) from the committed
+                counter record, null when the kernel sources have changed
+                since the counters were taken
   cpu_baseline  the float64 CPU oracle timed on a bounded sample of tokens
 """
 from __future__ import annotations
@@ -64,6 +68,7 @@ def main():
     import torch
 
     import mixture_experts_ffn_gemv_amd as M
+    from mixture_experts_ffn_gemv_amd.profiling import recorded_traffic
     from moe_synth import CONFIGS, generate, WF_U4
     from moe_synth.generator import x_rows
     from moe_synth.device import desc_kwargs, weights_kwargs
@@ -151,11 +156,7 @@ def main():
 
     H, I, E, k = cfg.H, cfg.I, cfg.E, cfg.k
     bpw = bytes_per_weight(cfg.weight_format)
-    if decode and "fused_experts" in kernel_ms:
-        # one launch streams every selected expert's gate, up and down rows
-        dom = "fused_experts"
-        alg = touched * 3 * I * H * bpw + (3 * cfg.Is * H * bpw if cfg.shared else 0)
-    elif decode:
+    if decode:
         # selected-expert gate+up weight bytes streamed by one gate/up launch
         dom = "gemv_gateup"
         alg = touched * 2 * I * H * bpw + (2 * cfg.Is * H * bpw if cfg.shared else 0)
@@ -163,7 +164,7 @@ def main():
         achieved = alg / (kernel_ms[dom] * 1e-3) / 1e9
         roof = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": None, "algorithmic_bytes_per_launch": alg,
+                "traffic": recorded_traffic(cfg.name, dom), "algorithmic_bytes_per_launch": alg,
                 "avg_launch_us": round(kernel_ms[dom] * 1e3, 2)}
         step_bytes = touched * 3 * I * H * bpw + (3 * cfg.Is * H * bpw if cfg.shared else 0)
         extra = {"path_weight_bytes": step_bytes,
@@ -175,7 +176,8 @@ def main():
         achieved = fl / (kernel_ms[dom] * 1e-3) / 1e12
         roof = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1),
                 "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                "traffic": recorded_traffic(cfg.name, dom),
                 "algorithmic_flops_per_launch": fl, "avg_launch_us": round(kernel_ms[dom] * 1e3, 2)}
         tot = 2.0 * T * (k * 3 * I * H + (3 * cfg.Is * H if cfg.shared else 0) + (E + 1) * H)
         extra = {"path_flops": tot, "path_tflops": round(tot / (ms_per_step * 1e-3) / 1e12, 1)}

@@ -167,7 +167,9 @@ hipEvent_t ev_get() {
     return e;
   }
   hipEvent_t e = nullptr;
-  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  // timing-only events: without the system-scope fence an event record
+  // costs no cache writeback, so the bracket stays close to the kernel
+  if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
   return e;
 }
 

@@ -1,0 +1,142 @@
+"""Turn rocprofv3 CSV output into the short text summaries kept with the
+sources, and into the per-kernel HBM traffic record bench.py reports.
+
+Traffic comes from two counter passes over the same command: FETCH_SIZE in
+one, WRITE_SIZE in the other (KiB per dispatch).  Each pass first runs one
+plain device copy of known size (bench.py --calib-copy-mb), and the ratio of
+its known bytes to what the counter reports scales the kernels' readings.
+
+Usage:
+  python -m mixture_experts_ffn_gemv_amd.profiling traffic \
+      --fetch DIR --write DIR --workload NAME --copy-mib 1024 \
+      --kernel gemv_gateup=k_dec_gateup3 --kernel gemv_down_combine=k_dec_down3 \
+      --out profiles/traffic.json
+  python -m mixture_experts_ffn_gemv_amd.profiling stats --csv FILE
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_JSON = os.path.join(os.path.dirname(PKG), "profiles", "traffic.json")
+
+
+def kernel_source_sha() -> str:
+    """sha256 over every kernel source file (name and bytes, sorted)."""
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(PKG, "csrc", "*"))):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(workload: str, kernel: str):
+    """HBM bytes (read + write) per launch of `kernel` on `workload`, from the
+    committed counter record, or None when there is none or the kernel
+    sources have changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_JSON) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != kernel_source_sha():
+        return None
+    k = rec.get("kernels", {}).get(workload, {}).get(kernel)
+    if not k:
+        return None
+    return k["fetch_bytes"] + k["write_bytes"]
+
+
+def _counter_csv(d: str) -> str:
+    hits = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if len(hits) != 1:
+        raise SystemExit(f"expected one counter_collection.csv under {d}, found {hits}")
+    return hits[0]
+
+
+def _per_kernel(path: str) -> dict:
+    """kernel name -> list of counter values (one per dispatch)."""
+    out: dict = {}
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return out
+
+
+def _find(agg: dict, key: str) -> list:
+    vals = [v for name, vs in agg.items() if key in name for v in vs]
+    if not vals:
+        raise SystemExit(f"no dispatch of a kernel matching {key!r}")
+    return vals
+
+
+def cmd_traffic(a) -> None:
+    f = _per_kernel(_counter_csv(a.fetch))
+    w = _per_kernel(_counter_csv(a.write))
+    known_kib = a.copy_mib * 1024.0
+    fetch_factor = known_kib / max(_find(f, "copyBuffer"))
+    write_factor = known_kib / max(_find(w, "copyBuffer"))
+    try:
+        with open(a.out) as fh:
+            rec = json.load(fh)
+        if rec.get("source_sha256") != kernel_source_sha():
+            rec = {}
+    except (OSError, ValueError):
+        rec = {}
+    rec["source_sha256"] = kernel_source_sha()
+    rec.setdefault("kernels", {})
+    cal = rec.setdefault("calibration", {})
+    cal[a.workload] = {"copy_mib": a.copy_mib, "fetch_factor": fetch_factor,
+                       "write_factor": write_factor}
+    ks = rec["kernels"].setdefault(a.workload, {})
+    for spec in a.kernel:
+        label, key = spec.split("=", 1)
+        fv, wv = _find(f, key), _find(w, key)
+        ks[label] = {"symbol": key,
+                     "fetch_kib": sum(fv) / len(fv), "write_kib": sum(wv) / len(wv),
+                     "fetch_bytes": sum(fv) / len(fv) * 1024.0 * fetch_factor,
+                     "write_bytes": sum(wv) / len(wv) * 1024.0 * write_factor}
+    os.makedirs(os.path.dirname(os.path.abspath(a.out)), exist_ok=True)
+    with open(a.out, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(json.dumps({a.workload: ks, "calibration": cal[a.workload]}, indent=1))
+
+
+def cmd_stats(a) -> None:
+    """Markdown table of the library's kernels from a --stats kernel CSV."""
+    print("| kernel | calls | avg us | min us | max us | % of traced GPU time |")
+    print("|---|---|---|---|---|---|")
+    with open(a.csv) as fh:
+        for r in csv.DictReader(fh):
+            if "moe::" not in r["Name"]:
+                continue
+            name = r["Name"].replace("moe::", "").split("(")[0]
+            print(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                  f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                  f"{float(r['Percentage']):.2f} |")
+
+
+def main() -> None:
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    t = sub.add_parser("traffic")
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--workload", required=True)
+    t.add_argument("--copy-mib", type=int, required=True)
+    t.add_argument("--kernel", action="append", required=True, help="label=symbol substring")
+    t.add_argument("--out", default=TRAFFIC_JSON)
+    s = sub.add_parser("stats")
+    s.add_argument("--csv", required=True)
+    a = ap.parse_args()
+    {"traffic": cmd_traffic, "stats": cmd_stats}[a.cmd](a)
+
+
+if __name__ == "__main__":
+    main()
