@@ -32,6 +32,12 @@
  * from the caller's workspace, sized by moe_workspace_size (the affine
  * workspace formula of ferrum-kernels' MoeWorkspaceLayout).
  *
+ * Workspace: its first MOE_WORKSPACE_ZERO_BYTES bytes hold completion
+ * counters that every call leaves at zero when its work ends.  Fill them
+ * with zeros once, after allocating the workspace and before its first
+ * use; after that, reuse it as it is.  Calls sharing one workspace must
+ * not overlap in time (same stream, or ordered by events).
+ *
  * Streams: calls enqueue work on `stream` (a hipStream_t; NULL = the
  * default stream) and return without synchronising.  Buffers must stay
  * valid until that work completes.
@@ -52,7 +58,10 @@
 extern "C" {
 #endif
 
-#define MOE_FFN_ABI_VERSION 1
+#define MOE_FFN_ABI_VERSION 2
+
+/* Leading workspace bytes that must be zero before a workspace's first use. */
+#define MOE_WORKSPACE_ZERO_BYTES 256
 
 /* Limits (ferrum-kernels moe.rs route dispatch: at most 256 experts and
  * 32 experts per token). */

@@ -26,6 +26,7 @@ MOE_INVALID_ARGUMENT = 1
 MOE_UNSUPPORTED = 2
 MOE_WORKSPACE_TOO_SMALL = 3
 MOE_HIP_ERROR = 4
+WORKSPACE_ZERO_BYTES = 256   # MOE_WORKSPACE_ZERO_BYTES: leading bytes zeroed before first use
 
 WEIGHTS_F32, WEIGHTS_BF16, WEIGHTS_U4_G32 = 0, 1, 2
 ACT_SILU, ACT_GELU_TANH = 0, 1
@@ -143,7 +144,8 @@ def _stream(stream):
 
 def alloc_workspace(desc: Desc, num_tokens: int, device="cuda"):
     import torch
-    return torch.empty(max(workspace_size(desc, num_tokens), 256), dtype=torch.uint8, device=device)
+    # zero-filled: the leading counter bytes must start at zero (calls keep them so)
+    return torch.zeros(max(workspace_size(desc, num_tokens), WORKSPACE_ZERO_BYTES), dtype=torch.uint8, device=device)
 
 
 @dataclass

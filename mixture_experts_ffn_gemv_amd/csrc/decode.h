@@ -1,10 +1,12 @@
-// Decode path (few tokens, T <= 32): four launches per layer.
+// Decode path (few tokens, T <= 32): three launches per layer.
 //
-//   router GEMV -> k_route_small -> k_dec_gateup3 -> k_dec_down3
+//   k_router_route -> k_dec_gateup3 -> k_dec_down3
 //
-// k_route_small   one workgroup: softmax/top-k/renormalise for every token,
-//                 then the stable expert grouping (counts, offsets, list of
-//                 touched experts, routes grouped by expert).
+// k_router_route  router logits (one workgroup per router row); the last
+//                 workgroup to finish then does softmax/top-k/renormalise
+//                 for every token and the stable expert grouping (counts,
+//                 offsets, list of touched experts, routes grouped by
+//                 expert).
 // k_dec_gateup3   work item = (touched expert, block of 4 features).  Each
 //                 wave owns 1 feature (its gate and up rows); its 64 lanes
 //                 split K into 16-byte chunks and issue every weight load of
@@ -21,119 +23,12 @@
 
 #include "common.h"
 #include "gemv.h"
+#include "route.h"
 
 namespace moe {
 
 constexpr int kSmallMaxTokens = 32;
 constexpr int kSmallRoutes = kSmallMaxTokens * MOE_MAX_TOP_K_DEV;
-
-// ---------------------------------------------------------------------------
-// Top-k of one token's logits by one wave.  Lane j < k returns slot j's
-// expert and weight.  See k_topk for the selection and weight rules.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ void wave_topk(const float* __restrict__ l, int E, int k, int normalize,
-                                          int lane, int& my_id, float& my_w) {
-  float v[4];
-  unsigned taken = 0;  // bit q: candidate q of this lane is used up (or absent)
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int e = lane + 64 * q;
-    v[q] = (e < E) ? l[e] : -INFINITY;
-    if (e >= E) taken |= 1u << q;
-  }
-  my_id = 0;
-  float my_val = -INFINITY;
-  for (int j = 0; j < k; ++j) {
-    float bv = -INFINITY;
-    int bi = 0x7FFFFFFF;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      if (!((taken >> q) & 1u) && (v[q] > bv || bi == 0x7FFFFFFF)) { bv = v[q]; bi = lane + 64 * q; }
-    wave_argmax(bv, bi);
-    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-    if (lane == j) { my_id = bi; my_val = bv; }
-  }
-  const float lmax = __shfl(my_val, 0, 64);
-  const float ex = (lane < k) ? __expf(my_val - lmax) : 0.f;
-  float denom;
-  if (normalize) {
-    denom = wave_sum(ex);
-  } else {
-    float s = 0.f;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      if (lane + 64 * q < E) s += __expf(v[q] - lmax);
-    denom = wave_sum(s);
-  }
-  my_w = ex / denom;
-}
-
-constexpr int kRoutedMaxTokens = 4;
-constexpr int kRoutedMaxRoutes = kRoutedMaxTokens * MOE_MAX_TOP_K_DEV;
-
-struct RoutedLds {
-  int ids[kRoutedMaxRoutes];      // expert of route r = t*k + j
-  float w[kRoutedMaxRoutes];      // routing weight of route r
-  int perm[kRoutedMaxRoutes];     // routes grouped by expert, stable
-  int first[kRoutedMaxRoutes];    // route r is its expert's first route
-  int gexp[MOE_MAX_EXPERTS_DEV];  // expert of touched slot s (ascending)
-  int gstart[MOE_MAX_EXPERTS_DEV + 1];
-  int nrouted;
-  float sg[kRoutedMaxTokens];     // shared-expert gate per token
-};
-
-// Routing of T <= 4 tokens by one workgroup into LDS (wave t handles token t),
-// then the stable grouping of the R = T*k routes by expert with O(R^2)
-// rank counting: few barriers, no scan.
-__device__ __forceinline__ void route_tokens_lds(const float* __restrict__ logits, int T, int E,
-                                                 int k, int ncols, int normalize, int has_shared,
-                                                 RoutedLds& L) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int R = T * k;
-  if (wave < T) {
-    const float* l = logits + (size_t)wave * ncols;
-    int id;
-    float w;
-    wave_topk(l, E, k, normalize, lane, id, w);
-    if (lane < k) {
-      L.ids[wave * k + lane] = id;
-      L.w[wave * k + lane] = w;
-    }
-    if (lane == 0) L.sg[wave] = has_shared ? sigmoid_f(l[E]) : 0.f;
-  }
-  __syncthreads();
-  // stable position of each route in expert order, and first-of-expert flags
-  if (tid < R) {
-    const int e = L.ids[tid];
-    int less = 0, first = 1;
-    for (int r2 = 0; r2 < R; ++r2) {
-      const int e2 = L.ids[r2];
-      less += (e2 < e) || (e2 == e && r2 < tid);
-      first &= !(e2 == e && r2 < tid);
-    }
-    L.perm[less] = tid;
-    L.first[tid] = first;
-  }
-  __syncthreads();
-  if (tid < R && L.first[tid]) {
-    const int e = L.ids[tid];
-    int slot = 0, start = 0;
-    for (int r2 = 0; r2 < R; ++r2) {
-      const int e2 = L.ids[r2];
-      slot += (e2 < e) && L.first[r2];
-      start += (e2 < e);
-    }
-    L.gexp[slot] = e;
-    L.gstart[slot] = start;
-  }
-  if (tid == 0) {
-    int n = 0;
-    for (int r2 = 0; r2 < R; ++r2) n += L.first[r2];
-    L.nrouted = n;
-    L.gstart[n] = R;
-  }
-  __syncthreads();
-}
 
 struct SmallRouteOut {
   int32_t* ids;          // [R]
@@ -152,100 +47,269 @@ struct SmallRouteOut {
   int32_t* user_perm;
 };
 
-__global__ __launch_bounds__(256) void k_route_small(const float* __restrict__ logits, int T, int E,
-                                                     int k, int ncols, int normalize,
-                                                     int has_shared, SmallRouteOut o) {
-  __shared__ int s_ids[kSmallRoutes];
-  __shared__ int s_cnt[256];
-  __shared__ int s_sc[256];
-  __shared__ int s_sa[256];
-  __shared__ RoutedLds L;
+// Exclusive prefix sums of two per-thread values over the 256 threads of a
+// workgroup (thread order), and their totals.
+__device__ __forceinline__ void block_scan2(int a, int b, int& ea, int& eb, int& ta, int& tb) {
+  __shared__ int s_part[2][4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int ia = a, ib = b;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int u = __shfl_up(ia, d, 64);
+    const int v = __shfl_up(ib, d, 64);
+    if (lane >= d) { ia += u; ib += v; }
+  }
+  if (lane == 63) { s_part[0][wave] = ia; s_part[1][wave] = ib; }
+  __syncthreads();
+  ta = 0; tb = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    if (w < wave) { ia += s_part[0][w]; ib += s_part[1][w]; }
+    ta += s_part[0][w];
+    tb += s_part[1][w];
+  }
+  ea = ia - a;
+  eb = ib - b;
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
+// Routing of T <= 32 tokens by one workgroup.  The logits of every token go
+// to LDS, the k experts of each token are selected by one of two methods,
+// the softmax denominators are summed by a 16-lane row per token, the
+// weights formed one thread per route, and the grouping is one thread per
+// expert: its routes, in token order, are its stable block.
+//
+// Rank selection (few pairs): pair (t, e) gets the key (order-preserving
+// bits of l[t,e], ~e).  Keys of one token are distinct and order "larger
+// logit first, lower expert index among equal logits", the tie rule of the
+// stable descending sort.  A pair's rank is the number of larger keys of its
+// token; ranks below k are the slots.  All pairs are ranked at once, E
+// comparisons each, where a wave-wide arg-max needs k dependent rounds.
+//
+// Row selection (more pairs): a 16-lane row per token, four tokens per
+// wave; k rounds of a row maximum over the same keys, built from DPP row
+// operations, which need no cross-row readlane.
+// ---------------------------------------------------------------------------
+constexpr int kRankMaxPairs = 1024;
+
+__device__ __forceinline__ bool rank_route_ok(int T, int E) {
+  const int pairs = T * E;
+  return pairs <= kRankMaxPairs && ((pairs + 255) / 256) * E <= 256;
+}
+
+__device__ __forceinline__ uint64_t route_key(float l, int e) {
+  const uint32_t u = __float_as_uint(l == 0.0f ? 0.0f : l);  // -0 and +0 tie
+  const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)ord << 32) | (uint32_t)~(uint32_t)e;
+}
+
+typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xF, 0xF, true);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xF,
+                                                            0xF, true);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+// k rounds of a 16-lane maximum over the rank keys per token; lane l of a
+// row holds the keys of experts l, l+16, ... (CPL of them, E <= 16*CPL), and
+// the lane holding a round's winner clears it.
+template <int CPL>
+__device__ __forceinline__ void row_select(const float* __restrict__ s_l, int T, int E, int k,
+                                           int8_t* __restrict__ s_sel, int* __restrict__ s_rid) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15;
+  for (int t0 = wave * 4; t0 < T; t0 += 16) {
+    const int t = t0 + (lane >> 4);
+    const bool tok = t < T;
+    uint64_t key[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int e = l16 + 16 * c;
+      key[c] = (tok && e < E) ? route_key(s_l[t * E + e], e) : 0;
+    }
+    for (int j = 0; j < k; ++j) {
+      uint64_t m[CPL];  // pairwise tree: independent compares can overlap
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) m[c] = key[c];
+#pragma unroll
+      for (int w = CPL / 2; w >= 1; w /= 2)
+#pragma unroll
+        for (int c = 0; c < w; ++c) m[c] = max_u64(m[c], m[c + w]);
+      uint64_t b = m[0];
+      b = max_u64(b, dpp_u64<kDppXor1>(b));
+      b = max_u64(b, dpp_u64<kDppXor2>(b));
+      b = max_u64(b, dpp_u64<kDppHalfMirror>(b));
+      b = max_u64(b, dpp_u64<kDppMirror>(b));
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) key[c] = key[c] == b ? 0 : key[c];
+      const int e = (int)~(uint32_t)b;
+      if (tok && (e & 15) == l16) s_sel[t * E + e] = (int8_t)j;
+      if (tok && l16 == 0) s_rid[t * k + j] = e;
+    }
+  }
+}
+
+struct RouteLds {
+  float l[kSmallMaxTokens * MOE_MAX_EXPERTS_DEV];     // logits [T][E]
+  int8_t sel[kSmallMaxTokens * MOE_MAX_EXPERTS_DEV];  // slot of (t, e), or -1
+  int rid[kSmallRoutes];                              // expert of route t*k + j
+  float den[kSmallMaxTokens];                         // softmax denominator per token
+  // rank keys, rows padded to an even length with key 0 (below every real key)
+  __attribute__((aligned(16))) uint64_t key[kRankMaxPairs + kSmallMaxTokens];
+};
+
+// TMAX bounds T: the per-token loops are unrolled to TMAX, so the common
+// few-token case runs a short instruction stream.
+template <int TMAX>
+__device__ __forceinline__ void route_small_impl(const float* __restrict__ logits, int T, int E,
+                                                 int k, int ncols, int normalize, int has_shared,
+                                                 const SmallRouteOut& o, RouteLds& L) {
+  float* s_l = L.l;
+  int8_t* s_sel = L.sel;
+  int* s_rid = L.rid;
+  float* s_den = L.den;
+  uint64_t* s_key = L.key;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int R = T * k;
-  if (T <= kRoutedMaxTokens) {
-    route_tokens_lds(logits, T, E, k, ncols, normalize, has_shared, L);
-    for (int r = tid; r < R; r += 256) {
-      o.ids[r] = L.ids[r];
-      o.wts[r] = L.w[r];
-      o.perm[r] = L.perm[r];
-      o.pos_of_route[L.perm[r]] = r;
-      if (o.user_ids) o.user_ids[r] = L.ids[r];
-      if (o.user_w) o.user_w[r] = L.w[r];
-      if (o.user_perm) o.user_perm[r] = L.perm[r];
-    }
-    // per-expert counts and offsets over all E experts
-    for (int e = tid; e <= E; e += 256) {
-      int less = 0, eq = 0;
-      for (int r = 0; r < R; ++r) {
-        less += L.ids[r] < e;
-        eq += L.ids[r] == e;
-      }
-      o.offsets[e] = less;
-      if (o.user_offsets) o.user_offsets[e] = less;
-      if (e < E) {
-        o.counts[e] = eq;
-        if (o.user_counts) o.user_counts[e] = eq;
+  const bool use_rank = rank_route_ok(T, E);
+  const int Ep = (E + 1) & ~1;
+
+  // 1. logits -> LDS; thread e loads column e of every token, all loads at once
+  {
+    const bool eok = tid < E;
+    float lv[TMAX];
+#pragma unroll
+    for (int t = 0; t < TMAX; ++t)
+      lv[t] = (t < T && eok) ? logits[(size_t)t * ncols + tid] : 0.f;
+#pragma unroll
+    for (int t = 0; t < TMAX; ++t) {
+      if (t < T && eok) {
+        s_l[t * E + tid] = lv[t];
+        s_sel[t * E + tid] = -1;
+        if (use_rank) s_key[t * Ep + tid] = route_key(lv[t], tid);
       }
     }
-    const int nrouted = L.nrouted;
-    for (int sl = tid; sl < nrouted; sl += 256) o.active[sl] = L.gexp[sl];
-    if (tid < T && has_shared) o.sgate[tid] = L.sg[tid];
-    if (tid == 0) {
-      int na = nrouted;
-      if (has_shared) {
-        o.counts[E] = T;
-        o.active[na++] = E;
-      }
-      *o.n_active = na;
-    }
-    return;
+    if (use_rank && (E & 1) && tid < T) s_key[tid * Ep + E] = 0;
   }
-  s_cnt[tid] = 0;
-  for (int t = wave; t < T; t += 4) {
-    const float* l = logits + (size_t)t * ncols;
-    int id;
-    float w;
-    wave_topk(l, E, k, normalize, lane, id, w);
-    if (lane < k) {
-      const int r = t * k + lane;
-      s_ids[r] = id;
+  __syncthreads();
+
+  // 2. selection
+  if (use_rank) {
+    for (int q = tid; q < T * E; q += 256) {
+      const int t = q / E, e = q - t * E;
+      const uint64_t mine = s_key[t * Ep + e];
+      const u64x2* row = reinterpret_cast<const u64x2*>(&s_key[t * Ep]);
+      int rank = 0;
+      for (int i = 0; i < Ep / 2; ++i) {
+        const u64x2 kk = row[i];
+        rank += (kk[0] > mine ? 1 : 0) + (kk[1] > mine ? 1 : 0);
+      }
+      if (rank < k) {
+        s_sel[q] = (int8_t)rank;
+        s_rid[t * k + rank] = e;
+      }
+    }
+  } else if (E <= 64) {
+    row_select<4>(s_l, T, E, k, s_sel, s_rid);
+  } else if (E <= 128) {
+    row_select<8>(s_l, T, E, k, s_sel, s_rid);
+  } else {
+    row_select<16>(s_l, T, E, k, s_sel, s_rid);
+  }
+  __syncthreads();
+
+  if constexpr (TMAX <= 4) {
+    // 3+4. weights: wave t handles token t, lane j slot j
+    if (wave < T) {
+      const int t = wave;
+      const float* lt = s_l + t * E;
+      const int id = lane < k ? s_rid[t * k + lane] : 0;
+      const float lmax = lt[s_rid[t * k]];
+      const float ex = lane < k ? __expf(lt[id] - lmax) : 0.f;
+      float denom;
+      if (normalize) {
+        denom = wave_sum(ex);
+      } else {
+        float sum = 0.f;
+        for (int e = lane; e < E; e += 64) sum += __expf(lt[e] - lmax);
+        denom = wave_sum(sum);
+      }
+      if (lane < k) {
+        const int r = t * k + lane;
+        const float w = ex / denom;
+        o.ids[r] = id;
+        o.wts[r] = w;
+        if (o.user_ids) o.user_ids[r] = id;
+        if (o.user_w) o.user_w[r] = w;
+      }
+    }
+  } else {
+    // 3. softmax denominators, a 16-lane row per token: the selected terms
+    //    (renormalised weights) or all E terms (plain softmax probabilities)
+    const int l16 = lane & 15;
+    for (int t0 = wave * 4; t0 < T; t0 += 16) {
+      const int t = t0 + (lane >> 4);
+      float sum = 0.f;
+      if (t < T) {
+        const float* lt = s_l + t * E;
+        const float lmax = lt[s_rid[t * k]];
+        for (int e = l16; e < E; e += 16)
+          if (!normalize || s_sel[t * E + e] >= 0) sum += __expf(lt[e] - lmax);
+      }
+      sum += dpp_f<kDppXor1>(sum);
+      sum += dpp_f<kDppXor2>(sum);
+      sum += dpp_f<kDppHalfMirror>(sum);
+      sum += dpp_f<kDppMirror>(sum);
+      if (t < T && l16 == 0) s_den[t] = sum;
+    }
+    __syncthreads();
+    // 4. ids and weights, one thread per route
+    for (int r = tid; r < R; r += 256) {
+      const int t = r / k;
+      const float* lt = s_l + t * E;
+      const int id = s_rid[r];
+      const float w = __expf(lt[id] - lt[s_rid[t * k]]) / s_den[t];
       o.ids[r] = id;
       o.wts[r] = w;
       if (o.user_ids) o.user_ids[r] = id;
       if (o.user_w) o.user_w[r] = w;
     }
-    if (has_shared && lane == 0) o.sgate[t] = sigmoid_f(l[E]);
   }
-  __syncthreads();
-  for (int r = tid; r < R; r += 256) atomicAdd(&s_cnt[s_ids[r]], 1);
-  __syncthreads();
-  const int cnt = s_cnt[tid];
-  const int act = (tid < E && cnt > 0) ? 1 : 0;
-  // inclusive scans of counts and active flags: within each wave by
-  // shuffles, then across the four waves
-  int ic = cnt, ia = act;
+  if (has_shared && tid < T) o.sgate[tid] = sigmoid_f(logits[(size_t)tid * ncols + E]);
+
+  // 5. grouping, one thread per expert
+  int sel[TMAX];
+  int cnt = 0;
 #pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int a = __shfl_up(ic, d, 64);
-    const int b = __shfl_up(ia, d, 64);
-    if (lane >= d) { ic += a; ia += b; }
+  for (int t = 0; t < TMAX; ++t) {
+    sel[t] = (t < T && tid < E) ? (int)s_sel[t * E + tid] : -1;
+    cnt += sel[t] >= 0 ? 1 : 0;
   }
-  if (lane == 63) { s_sc[wave] = ic; s_sa[wave] = ia; }
-  __syncthreads();
-  for (int w = 0; w < wave; ++w) { ic += s_sc[w]; ia += s_sa[w]; }
-  __syncthreads();
-  s_sc[tid] = ic;
-  s_sa[tid] = ia;
-  __syncthreads();
-  const int off = s_sc[tid] - cnt;
-  const int aoff = s_sa[tid] - act;
-  const int nact = s_sa[255];
+  const int act = cnt > 0 ? 1 : 0;
+  int off, aoff, total, nact;
+  block_scan2(cnt, act, off, aoff, total, nact);
   if (tid < E) {
     o.counts[tid] = cnt;
     o.offsets[tid] = off;
     if (o.user_counts) o.user_counts[tid] = cnt;
     if (o.user_offsets) o.user_offsets[tid] = off;
     if (act) o.active[aoff] = tid;
+    int pos = off;
+#pragma unroll
+    for (int t = 0; t < TMAX; ++t) {
+      if (sel[t] >= 0) {
+        const int r = t * k + sel[t];
+        o.perm[pos] = r;
+        o.pos_of_route[r] = pos;
+        if (o.user_perm) o.user_perm[pos] = r;
+        ++pos;
+      }
+    }
   }
   if (tid == 0) {
     o.offsets[E] = R;
@@ -257,36 +321,60 @@ __global__ __launch_bounds__(256) void k_route_small(const float* __restrict__ l
     }
     *o.n_active = na;
   }
-  __syncthreads();
-  s_cnt[tid] = off;  // running position per expert
-  __syncthreads();
-  // stable placement, 64 routes per step by wave 0
-  for (int base = 0; base < R; base += 64) {
-    const int r = base + lane;
-    const bool valid = r < R;
-    int pos = 0, e = 0;
-    uint64_t mask = 0;
-    if (wave == 0) {
-      e = valid ? s_ids[r] : 0;
-      mask = __ballot(valid);
-#pragma unroll
-      for (int bit = 0; bit < 8; ++bit) {
-        const bool set = (e >> bit) & 1;
-        const uint64_t b = __ballot(set);
-        mask &= set ? b : ~b;
-      }
-      pos = s_cnt[e] + __popcll(mask & lanemask_lt());
-    }
-    __syncthreads();
-    if (wave == 0 && valid) {
-      if ((mask >> lane) == 1ull) s_cnt[e] += __popcll(mask);
-      o.perm[pos] = r;
-      o.pos_of_route[r] = pos;
-      if (o.user_perm) o.user_perm[pos] = r;
-    }
-    __syncthreads();
-  }
 }
+
+__device__ void route_small_body(const float* __restrict__ logits, int T, int E, int k,
+                                 int ncols, int normalize, int has_shared,
+                                 const SmallRouteOut& o) {
+  __shared__ RouteLds L;
+  if (T <= 4) route_small_impl<4>(logits, T, E, k, ncols, normalize, has_shared, o, L);
+  else route_small_impl<kSmallMaxTokens>(logits, T, E, k, ncols, normalize, has_shared, o, L);
+}
+
+// Router logits fused with the routing: workgroup e computes router row e
+// (logit column e for every token), then takes a ticket.  The workgroup
+// that takes the last ticket sees every column written, routes all tokens
+// and sets the ticket counter back to zero for the next call.
+// Publication: the logits are stored at device scope and the wave waits
+// for those stores to complete before the ticket is taken; the last
+// workgroup invalidates its caches (device-scope acquire) before reading
+// them.  A device-scope release fence per workgroup would instead write
+// back the whole L2 of its XCD, which costs far more than the GEMV.
+template <typename XT, int RDT>
+__global__ __launch_bounds__(256) void k_router_route(const XT* __restrict__ x,
+                                                      const void* __restrict__ router,
+                                                      const float* __restrict__ bias,
+                                                      const void* __restrict__ shared_gate_inp,
+                                                      float* __restrict__ logits, int T, int H,
+                                                      int E, int k, int ncols, int normalize,
+                                                      int has_shared, int* __restrict__ ticket,
+                                                      SmallRouteOut o) {
+  router_row<XT, RDT, true>(x, router, bias, shared_gate_inp, logits, T, H, E, ncols,
+                            blockIdx.x);
+  __shared__ int s_last;
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's logit stores have completed
+  __syncthreads();
+  if (threadIdx.x == 0)
+    s_last = __hip_atomic_fetch_add(ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+             (int)gridDim.x - 1;
+  __syncthreads();
+  if (!s_last) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  if (threadIdx.x == 0) __hip_atomic_store(ticket, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  route_small_body(logits, T, E, k, ncols, normalize, has_shared, o);
+}
+
+// Routing data read back from the workspace, clamped to the layer's ranges,
+// so that the expert kernels stay in bounds whatever the workspace holds
+// (for instance one whose leading counter bytes were never zeroed).
+__device__ __forceinline__ int ws_group(int g, int E, bool has_shared) {
+  return (g >= 0 && (g < E || (has_shared && g == E))) ? g : 0;
+}
+__device__ __forceinline__ void ws_span(int& base, int& count, int R) {
+  base = min(max(base, 0), R);
+  count = min(max(count, 0), R - base);
+}
+__device__ __forceinline__ int ws_route(int r, int R) { return min(max(r, 0), R - 1); }
 
 // ---------------------------------------------------------------------------
 struct Dec2Params {
@@ -393,7 +481,8 @@ __global__ __launch_bounds__(256) void k_dec_gateup3(Dec2Params p) {
   extern __shared__ float xs[];  // [rc][H] (staged path only)
   const int s = blockIdx.x;
   if (s >= *p.n_active) return;
-  const int g = p.active[s];
+  const int R = p.T * p.k;
+  const int g = ws_group(p.active[s], p.E, p.Is > 0);
   const bool shared = (g == p.E);
   const int N = shared ? p.Is : p.I;
   const int fblk = blockIdx.y * kGUWaves;
@@ -406,11 +495,12 @@ __global__ __launch_bounds__(256) void k_dec_gateup3(Dec2Params p) {
   const MatStack& Mu = shared ? p.sup : p.up;
   const size_t row = shared ? (size_t)f : (size_t)g * N + f;
 
-  const int count = shared ? p.T : p.counts[g];
-  const int base = shared ? 0 : p.offsets[g];
+  int count = shared ? p.T : p.counts[g];
+  int base = shared ? 0 : p.offsets[g];
+  if (!shared) ws_span(base, count, R);
 
   if constexpr (DIRECT) {
-    const int r = shared ? 0 : p.perm[base];
+    const int r = shared ? 0 : ws_route(p.perm[base], R);
     const int t = shared ? 0 : r / p.k;
     float ag = 0.f, au = 0.f;
     for (int kb = 0; kb < cpr; kb += 64 * U) {
@@ -465,7 +555,7 @@ __global__ __launch_bounds__(256) void k_dec_gateup3(Dec2Params p) {
           const int q4 = p.H / 4;
           for (int i = tid; i < nr * q4; i += 256) {
             const int r = i / q4, c4 = i - r * q4;
-            const int t = shared ? (r0 + r) : (p.perm[base + r0 + r] / p.k);
+            const int t = shared ? (r0 + r) : (ws_route(p.perm[base + r0 + r], R) / p.k);
             float v4[4];
             load_act<4>(p.x, p.x_bf16, (size_t)t * p.H + 4 * c4, v4);
             *reinterpret_cast<f32x4*>(&xs[r * p.H + 4 * c4]) = f32x4{v4[0], v4[1], v4[2], v4[3]};
@@ -500,7 +590,7 @@ __global__ __launch_bounds__(256) void k_dec_gateup3(Dec2Params p) {
           if (lane == 0 && fok) {
             const float hv = (shared ? silu_f(gs) : act_f<ACT>(gs)) * us;
             if (shared) p.hs[(size_t)(r0 + r) * N + f] = hv;
-            else p.h[(size_t)p.perm[base + r0 + r] * N + f] = hv;
+            else p.h[(size_t)ws_route(p.perm[base + r0 + r], R) * N + f] = hv;
           }
         }
       }
@@ -525,12 +615,13 @@ __global__ __launch_bounds__(256) void k_dec_down3(Dec2Params p) {
   const int n0 = blockIdx.x * RPW;
   for (int i = tid; i < 4 * kSmallMaxTokens * RPW; i += 256) (&part[0][0][0])[i] = 0.f;
   __syncthreads();
-  const int na = *p.n_active;
+  const int na = min(*p.n_active, p.E + (p.Is > 0 ? 1 : 0));
+  const int R = p.T * p.k;
 
   u32x4 wc[RPW][U], wn[RPW][U];
   float sc[RPW][U], mc[RPW][U], sn[RPW][U], mnx[RPW][U];
   auto load_group = [&](int s, u32x4 (&w)[RPW][U], float (&sv)[RPW][U], float (&mv)[RPW][U]) {
-    const int g = p.active[s];
+    const int g = ws_group(p.active[s], p.E, p.Is > 0);
     const bool shared = (g == p.E);
     const int K = shared ? p.Is : p.I;
     const int cpr = K / EPC;
@@ -551,12 +642,13 @@ __global__ __launch_bounds__(256) void k_dec_down3(Dec2Params p) {
   while (s < na) {
     const int sn_ = s + 4;
     if (sn_ < na) load_group(sn_, wn, sn, mnx);
-    const int g = p.active[s];
+    const int g = ws_group(p.active[s], p.E, p.Is > 0);
     const bool shared = (g == p.E);
     const int K = shared ? p.Is : p.I;
     const int cpr = K / EPC;
-    const int count = shared ? p.T : p.counts[g];
-    const int base = shared ? 0 : p.offsets[g];
+    int count = shared ? p.T : p.counts[g];
+    int base = shared ? 0 : p.offsets[g];
+    if (!shared) ws_span(base, count, R);
     for (int i = 0; i < count; ++i) {
       int t;
       float wgt;
@@ -564,7 +656,7 @@ __global__ __launch_bounds__(256) void k_dec_down3(Dec2Params p) {
       if (shared) {
         t = i; wgt = p.sgate_val[t]; hrow = p.hs + (size_t)t * K;
       } else {
-        const int r = p.perm[base + i];
+        const int r = ws_route(p.perm[base + i], R);
         t = r / p.k; wgt = p.wts[r]; hrow = p.h + (size_t)r * K;
       }
       float acc[RPW];

@@ -38,6 +38,7 @@ moe_status fail(moe_status s, const char* fmt, ...) {
 // Largest token count that takes the GEMV (decode) path when the MFMA
 // path is available.
 constexpr int64_t kDecodeMaxTokens = 32;
+constexpr size_t kSyncBytes = MOE_WORKSPACE_ZERO_BYTES;
 
 size_t align_up(size_t v, size_t a = 256) { return (v + a - 1) / a * a; }
 
@@ -53,7 +54,7 @@ struct Plan {
   int bt = 128;            // grouped-GEMM route-tile height
   int max_groups = 0;      // active groups (upper bound)
   // workspace offsets
-  size_t o_logits, o_ids, o_wts, o_sgate, o_bhist, o_boff, o_counts, o_offsets, o_active,
+  size_t o_sync, o_logits, o_ids, o_wts, o_sgate, o_bhist, o_boff, o_counts, o_offsets, o_active,
       o_nactive, o_ntiles, o_perm, o_pos, o_rowtok, o_tgroup, o_tm0, o_h, o_hs, o_y, o_ys;
   size_t total = 0;
 };
@@ -123,6 +124,7 @@ Plan make_plan(const moe_desc* d, int64_t T) {
   const size_t es = p.mfma ? 2 : 4;  // h / y element size
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t r = o; o = align_up(o + bytes); return r; };
+  p.o_sync = take(kSyncBytes);  // ticket counter(s), kept at zero between calls
   p.o_logits = take((size_t)T * p.ncols * 4);
   p.o_ids = take((size_t)p.R * 4);
   p.o_wts = take((size_t)p.R * 4);
@@ -238,31 +240,51 @@ moe_status run_router(const moe_desc* d, const Plan& p, const void* x, const moe
   });
 }
 
+// Decode routing: router logits and the routing in one launch.
+moe_status run_route_small(const moe_desc* d, const Plan& p, const void* x, const moe_weights* w,
+                           void* ws, int32_t* user_ids, float* user_w, int32_t* user_counts,
+                           int32_t* user_offsets, int32_t* user_perm, hipStream_t s) {
+  const int T = (int)p.T;
+  SmallRouteOut o;
+  o.ids = wsp<int32_t>(ws, p.o_ids);
+  o.wts = wsp<float>(ws, p.o_wts);
+  o.sgate = wsp<float>(ws, p.o_sgate);
+  o.counts = wsp<int32_t>(ws, p.o_counts);
+  o.offsets = wsp<int32_t>(ws, p.o_offsets);
+  o.active = wsp<int32_t>(ws, p.o_active);
+  o.n_active = wsp<int32_t>(ws, p.o_nactive);
+  o.perm = wsp<int32_t>(ws, p.o_perm);
+  o.pos_of_route = wsp<int32_t>(ws, p.o_pos);
+  o.user_ids = user_ids;
+  o.user_w = user_w;
+  o.user_counts = user_counts;
+  o.user_offsets = user_offsets;
+  o.user_perm = user_perm;
+  float* logits = wsp<float>(ws, p.o_logits);
+  int* ticket = wsp<int>(ws, p.o_sync);
+  const bool xb = d->act_dtype == MOE_BF16, rb = d->router_dtype == MOE_BF16;
+  const int sh = p.shared ? 1 : 0, nz = d->normalize_topk;
+  dim3 grid(p.ncols);
+  return launch("router_route", s, [&] {
+    if (xb && rb)
+      k_router_route<uint16_t, 1><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(x), w->router,
+          w->router_bias, w->shared_gate_inp, logits, T, p.H, p.E, p.k, p.ncols, nz, sh, ticket, o);
+    else if (xb)
+      k_router_route<uint16_t, 0><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(x), w->router,
+          w->router_bias, w->shared_gate_inp, logits, T, p.H, p.E, p.k, p.ncols, nz, sh, ticket, o);
+    else if (rb)
+      k_router_route<float, 1><<<grid, 256, 0, s>>>(static_cast<const float*>(x), w->router,
+          w->router_bias, w->shared_gate_inp, logits, T, p.H, p.E, p.k, p.ncols, nz, sh, ticket, o);
+    else
+      k_router_route<float, 0><<<grid, 256, 0, s>>>(static_cast<const float*>(x), w->router,
+          w->router_bias, w->shared_gate_inp, logits, T, p.H, p.E, p.k, p.ncols, nz, sh, ticket, o);
+  });
+}
+
 moe_status run_route_and_group(const moe_desc* d, const Plan& p, void* ws, int32_t* user_ids,
                                float* user_w, int32_t* user_counts, int32_t* user_offsets,
                                int32_t* user_perm, hipStream_t s) {
   const int T = (int)p.T, R = (int)p.R;
-  if (p.small) {
-    SmallRouteOut o;
-    o.ids = wsp<int32_t>(ws, p.o_ids);
-    o.wts = wsp<float>(ws, p.o_wts);
-    o.sgate = wsp<float>(ws, p.o_sgate);
-    o.counts = wsp<int32_t>(ws, p.o_counts);
-    o.offsets = wsp<int32_t>(ws, p.o_offsets);
-    o.active = wsp<int32_t>(ws, p.o_active);
-    o.n_active = wsp<int32_t>(ws, p.o_nactive);
-    o.perm = wsp<int32_t>(ws, p.o_perm);
-    o.pos_of_route = wsp<int32_t>(ws, p.o_pos);
-    o.user_ids = user_ids;
-    o.user_w = user_w;
-    o.user_counts = user_counts;
-    o.user_offsets = user_offsets;
-    o.user_perm = user_perm;
-    return launch("route_small", s, [&] {
-      k_route_small<<<1, 256, 0, s>>>(wsp<float>(ws, p.o_logits), T, p.E, p.k, p.ncols,
-                                      d->normalize_topk, p.shared ? 1 : 0, o);
-    });
-  }
   MOE_TRY(launch("topk", s, [&] {
     k_topk<<<(T + 3) / 4, 256, 0, s>>>(wsp<float>(ws, p.o_logits), T, p.E, p.k, p.ncols,
                                        d->normalize_topk, p.shared ? 1 : 0, wsp<int32_t>(ws, p.o_ids),
@@ -629,6 +651,9 @@ moe_status moe_route(const moe_desc* desc, int64_t num_tokens, const void* x,
   if (num_tokens == 0) return MOE_OK;
   if (!topk_ids || !topk_w) return fail(MOE_INVALID_ARGUMENT, "topk_ids/topk_w is NULL");
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p.small)
+    return run_route_small(desc, p, x, weights, ws, topk_ids, topk_w, expert_counts,
+                           expert_offsets, route_perm, s);
   MOE_TRY(run_router(desc, p, x, weights, ws, s));
   return run_route_and_group(desc, p, ws, topk_ids, topk_w, expert_counts, expert_offsets,
                              route_perm, s);
@@ -644,10 +669,14 @@ moe_status moe_ffn_forward(const moe_desc* desc, int64_t num_tokens, const void*
   if (!out) return fail(MOE_INVALID_ARGUMENT, "out is NULL");
   if (!aligned16(out)) return fail(MOE_UNSUPPORTED, "out must be 16-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p.small) {
+    MOE_TRY(run_route_small(desc, p, x, weights, ws, topk_ids_out, topk_w_out, nullptr, nullptr,
+                            nullptr, s));
+    return run_experts_small(desc, p, x, weights, out, ws, s);
+  }
   MOE_TRY(run_router(desc, p, x, weights, ws, s));
   MOE_TRY(run_route_and_group(desc, p, ws, topk_ids_out, topk_w_out, nullptr, nullptr, nullptr, s));
   if (p.mfma) return run_experts_mfma(desc, p, x, weights, out, ws, s);
-  if (p.small) return run_experts_small(desc, p, x, weights, out, ws, s);
   return run_experts_gemv(desc, p, x, weights, out, ws, s);
 }
 

@@ -9,16 +9,20 @@ namespace moe {
 // --------------------------------------------------------------------------
 // Router logits for few tokens: l[t, e] = x[t,:] . Wr[e,:] (+ b[e]).
 // One workgroup per router row; threads split H into 16-byte weight chunks
-// and loop over the tokens four at a time.  Row E (when `has_shared`) is the
-// shared expert's gate vector, whose logit lands in column E.
+// and loop over the tokens four at a time.  Row E (when the layer has a
+// shared expert) is the shared expert's gate vector, whose logit lands in
+// column E.
 // --------------------------------------------------------------------------
-template <typename XT, int RDT>  // RDT: 0 = f32 router, 1 = bf16 router
-__global__ __launch_bounds__(256) void k_router_gemv(
-    const XT* __restrict__ x, const void* __restrict__ router,
-    const float* __restrict__ bias, const void* __restrict__ shared_gate_inp,
-    float* __restrict__ logits, int T, int H, int E, int ncols) {
+// RDT: 0 = f32 router, 1 = bf16 router.  COHERENT: logits are stored at
+// device scope (written through to the point of coherence of all XCDs), so
+// that another workgroup may read them within the same launch.
+template <typename XT, int RDT, bool COHERENT = false>
+__device__ __forceinline__ void router_row(const XT* __restrict__ x, const void* __restrict__ router,
+                                           const float* __restrict__ bias,
+                                           const void* __restrict__ shared_gate_inp,
+                                           float* __restrict__ logits, int T, int H, int E,
+                                           int ncols, int e) {
   constexpr int EPC = RDT ? 8 : 4;  // router elements per 16-byte chunk
-  const int e = blockIdx.x;
   const int tid = threadIdx.x;
   const uint8_t* row = (e < E)
       ? reinterpret_cast<const uint8_t*>(router) + (size_t)e * H * (RDT ? 2 : 4)
@@ -63,10 +67,20 @@ __global__ __launch_bounds__(256) void k_router_gemv(
     if (tid < 4 && t0 + tid < T) {
       float s = red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];
       if (e < E && bias) s += bias[e];
-      logits[(size_t)(t0 + tid) * ncols + e] = s;
+      float* dst = logits + (size_t)(t0 + tid) * ncols + e;
+      if constexpr (COHERENT) __hip_atomic_store(dst, s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else *dst = s;
     }
     __syncthreads();
   }
+}
+
+template <typename XT, int RDT>
+__global__ __launch_bounds__(256) void k_router_gemv(
+    const XT* __restrict__ x, const void* __restrict__ router,
+    const float* __restrict__ bias, const void* __restrict__ shared_gate_inp,
+    float* __restrict__ logits, int T, int H, int E, int ncols) {
+  router_row<XT, RDT>(x, router, bias, shared_gate_inp, logits, T, H, E, ncols, blockIdx.x);
 }
 
 // --------------------------------------------------------------------------

@@ -35,7 +35,7 @@ def test_header_declares_the_bound_functions():
 def test_library_exports_every_declared_symbol(lib):
     for name in _declared_functions():
         assert hasattr(lib, name), name
-    assert lib.moe_abi_version() == 1
+    assert lib.moe_abi_version() == 2
 
 
 def _desc(name="decode_geglu_t1", **over):
@@ -113,3 +113,12 @@ def test_u4_needs_group_32(lib):
     d = _desc("decode_u4_t32", group_size=64)
     n = ctypes.c_size_t(0)
     assert lib.moe_workspace_size(ctypes.byref(d), 1, ctypes.byref(n)) == M.MOE_UNSUPPORTED
+
+
+def test_workspace_zero_bytes_matches_header():
+    import re
+    with open(os.path.join(ROOT, "include", "moe_ffn.h")) as fh:
+        m = re.search(r"#define MOE_WORKSPACE_ZERO_BYTES (\d+)", fh.read())
+    assert m and int(m.group(1)) == M.WORKSPACE_ZERO_BYTES
+    d = M.make_desc(hidden=64, intermediate=32, num_experts=8, top_k=2)
+    assert M.workspace_size(d, 1) >= M.WORKSPACE_ZERO_BYTES

@@ -68,6 +68,10 @@ SMALL = [
     MoeConfig(name="gemv_f32_k32", T=2, H=64, I=32, E=256, k=32, seed_index=21),
     MoeConfig(name="gemv_bf16_f32x_t32", T=32, H=2816, I=704, E=128, k=8, act=ACT_GELU_TANH,
               weight_format=WF_BF16, router_dtype=DT_BF16, seed_index=22),
+    # decode routing: row selection (four tokens per wave) at 64 and 200 experts
+    MoeConfig(name="gemv_route_rows_e64", T=32, H=128, I=64, E=64, k=6, seed_index=28),
+    MoeConfig(name="gemv_route_rows_e200", T=20, H=64, I=32, E=200, k=5, weight_format=WF_BF16,
+              router_dtype=DT_BF16, seed_index=29),
     MoeConfig(name="gemv_bf16_large_t_fallback", T=100, H=96, I=64, E=8, k=2,
               weight_format=WF_BF16, act_dtype=DT_BF16, router_dtype=DT_BF16, seed_index=23),
 ]
@@ -139,3 +143,30 @@ def test_zero_and_identity_weights_on_gpu():
         t.zero_()
     out = M.moe_ffn_forward(case.desc, case.dev.x, case.weights)
     assert (out == 0).all()
+
+
+def test_workspace_reuse_across_calls_and_token_counts():
+    """One workspace serves a sequence of decode calls with changing token
+    counts (routing-only calls in between): every call matches the oracle
+    and the leading counter bytes are back at zero afterwards."""
+    import mixture_experts_ffn_gemv_amd as M
+    cfg = MoeConfig(name="ws_reuse", T=32, H=256, I=128, E=16, k=4, weight_format=WF_BF16,
+                    router_dtype=DT_BF16, seed_index=27)
+    case = Case(cfg)
+    ref_ids, ref_w = case.oracle_routing()
+    ref_out = case.oracle_outputs(list(range(cfg.T)))
+    ws = M.alloc_workspace(case.desc, cfg.T)
+    for it, T in enumerate([1, 32, 5, 1, 17, 32, 2, 1]):
+        x = case.dev.x[:T]
+        log(f"[gpu] ws_reuse call {it}: T={T}")
+        out, ids, w = M.moe_ffn_forward(case.desc, x, case.weights, workspace=ws,
+                                        return_routing=True)
+        if it % 3 == 1:
+            r = M.moe_route(case.desc, x, case.weights, workspace=ws)
+            torch.cuda.synchronize()
+            assert (r.ids.cpu().numpy() == ref_ids[:T]).all()
+        torch.cuda.synchronize()
+        assert (ids.cpu().numpy() == ref_ids[:T]).all(), f"call {it} (T={T}): ids differ"
+        assert float(np.abs(w.cpu().numpy() - ref_w[:T]).max()) <= 1e-5
+        assert rel_err(out.cpu().numpy(), ref_out[:T]) <= 2e-2
+    assert int(ws[:M.WORKSPACE_ZERO_BYTES].count_nonzero()) == 0
