@@ -65,12 +65,19 @@ __device__ __forceinline__ int swz(int row, int chunk) {
   return row * 64 + ((chunk ^ ((row >> 1) & 7)) << 3);
 }
 
-// Hardware deals workgroups round-robin over the 8 XCDs (block b -> XCD b%8).
-// xcd_remap turns the dispatch index into a logical index such that each
-// XCD receives a contiguous range of logical tiles.
-__device__ __forceinline__ int xcd_remap(int b, int total) {
-  const int q = total / 8, r = total % 8, x = b % 8, i = b / 8;
-  return (x < r) ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
+// Hardware deals workgroups round-robin over the 8 XCDs (block b -> XCD b%8),
+// and each XCD has its own L2.
+// The grid of the grouped GEMMs is sized for the largest possible number of
+// route tiles; only the first n_tiles exist.  xcd_valid_remap deals the
+// existing (route tile, weight tile) pairs, nvalid of them, evenly over the
+// XCDs (XCD x takes logical tiles [x*q, x*q + q)) and returns -1 for the
+// surplus workgroups, which exit.  Sizing the split by the grid instead would
+// leave whole XCDs with nothing but empty tiles.
+__device__ __forceinline__ int xcd_valid_remap(int b, int nvalid) {
+  const int x = b & 7, i = b >> 3;
+  const int q = (nvalid + 7) >> 3;
+  const int L = x * q + i;
+  return (i < q && L < nvalid) ? L : -1;
 }
 
 // Grouped order over (route tile, weight tile): groups of kGroupT route tiles
@@ -105,13 +112,14 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
     g = 0; shared = false; m0 = blockIdx.x * kTileT; count = p.T; base = 0;
     if (m0 >= count) return;
   } else {
-    // grid is (max route tiles, weight tiles); see grouped_tile
-    const int ntt = gridDim.x, nnt = gridDim.y;
-    const int L = xcd_remap(blockIdx.y * ntt + blockIdx.x, ntt * nnt);
+    // grid is (max route tiles, weight tiles); see xcd_valid_remap
+    const int nnt = gridDim.y;
+    const int ntiles = *p.n_tiles;
+    const int L = xcd_valid_remap(blockIdx.y * gridDim.x + blockIdx.x, ntiles * nnt);
+    if (L < 0) return;
     int ti, ntile;
-    grouped_tile(L, ntt, nnt, ti, ntile);
+    grouped_tile(L, ntiles, nnt, ti, ntile);
     nt_override = ntile;
-    if (ti >= *p.n_tiles) return;
     g = p.tile_group[ti];
     m0 = p.tile_m0[ti];
     shared = (g == p.E);

@@ -43,11 +43,12 @@ __global__ __launch_bounds__(256, BT == 128 ? 2 : 1) void k_gemm_big(GemmParams 
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int ntt = gridDim.x, nnt = gridDim.y;
-  const int L = xcd_remap(blockIdx.y * ntt + blockIdx.x, ntt * nnt);
+  const int nnt = gridDim.y;
+  const int ntiles = *p.n_tiles;
+  const int L = xcd_valid_remap(blockIdx.y * gridDim.x + blockIdx.x, ntiles * nnt);
+  if (L < 0) return;
   int ti, nt;
-  grouped_tile(L, ntt, nnt, ti, nt);
-  if (ti >= *p.n_tiles) return;
+  grouped_tile(L, ntiles, nnt, ti, nt);
   const int g = p.tile_group[ti];
   const int m0 = p.tile_m0[ti];
   const bool shared = (g == p.E);

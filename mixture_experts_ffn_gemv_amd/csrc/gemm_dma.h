@@ -1,0 +1,315 @@
+// bf16 MFMA grouped GEMM for experts that average many routes (prefill with
+// at least 256 routes per expert): 256 weight rows x 256 routes per
+// workgroup, K in steps of 32.
+//
+// Operands reach LDS by direct global->LDS loads (global_load_lds_dwordx4):
+// no staging registers and no ds_write, so a 4-stage ring (128 KB) keeps three
+// K-steps of loads in flight ahead of the one being multiplied.  The loads are issued
+// from inline assembly and their completion waits are written out: the
+// compiler's own wait insertion cannot tell the ring's stages apart and
+// drains every load in flight at the top of the loop.
+//
+// Each load instruction of a wave fills 1 KB of LDS, lane i writing bytes
+// 16i..16i+15 of it.  The swizzled layout of k_gemm_big (16-byte chunk c of
+// 64-byte row r at slot c ^ ((r >> 2) & 3)) is obtained by the choice of
+// source: lane i of 1-KB block b loads row b*16 + i/4, chunk
+// (i & 3) ^ ((row >> 2) & 3).
+//
+// kDmaWaves waves in a 2 (weight rows) x kDmaWaves/2 (routes) grid, each owning
+// 128 weight rows x 512/kDmaWaves routes of f32 accumulators (tiles of
+// v_mfma_f32_32x32x16_bf16).  Byte offsets of
+// rows are 32-bit (the host checks that every operand fits).
+#pragma once
+
+#include "common.h"
+#include "gemm.h"
+#include "gemm_big.h"
+
+namespace moe {
+
+constexpr int kDmaBT = 256;        // routes per tile
+constexpr int kDmaWaves = 8;       // waves per workgroup
+constexpr int kDmaThreads = 64 * kDmaWaves;
+#ifndef MOE_DMA_BK
+#define MOE_DMA_BK 64
+#endif
+#ifndef MOE_DMA_RING
+#define MOE_DMA_RING 2
+#endif
+constexpr int kDmaBK = MOE_DMA_BK;      // K per stage
+constexpr int kDmaRing = MOE_DMA_RING;  // stages
+
+// One 1-KB direct load per wave: lane i reads 16 bytes at sbase + voff and
+// writes them to LDS byte address lds + 16 i.  M0, which carries the LDS
+// address, is saved and restored around it (the compiler reserves M0).
+__device__ __forceinline__ void lds_dma16(uint32_t voff, const void* sbase, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(sbase), "s"(lds)
+      : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+template <typename T>
+__device__ __forceinline__ const T* uniform_ptr(const T* q) {
+  const uint64_t v = reinterpret_cast<uint64_t>(q);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const T*>(((uint64_t)hi << 32) | lo);
+}
+
+// 16-byte slot of chunk c in LDS row `row` (rows of CH chunks): XOR-ing with
+// row bits spreads the 16 lanes a ds_read_b128 serves per cycle (one chunk
+// of 16 consecutive rows) over 16 distinct bank groups.
+template <int CH>
+__device__ __forceinline__ int dma_slot(int row, int c) {
+  if constexpr (CH == 4) return c ^ ((row >> 2) & 3);
+  else return c ^ ((row >> 1) & 7);
+}
+
+#ifndef MOE_DMA_GROUP
+#define MOE_DMA_GROUP 8
+#endif
+#ifndef MOE_DMA_NFAST
+#define MOE_DMA_NFAST 0
+#endif
+// Logical workgroup L -> (route tile, weight tile): groups of G route tiles x
+// all weight tiles; within a group route tiles vary fastest (or weight tiles,
+// with NFAST).
+__device__ __forceinline__ void dma_tile_order(int L, int ntt, int nnt, int& tt, int& nt) {
+  constexpr int G = MOE_DMA_GROUP;
+  const int gsz = G * nnt;
+  const int grp = L / gsz, r = L - grp * gsz;
+  const int t0 = grp * G;
+  const int gt = min(G, ntt - t0);
+  if (MOE_DMA_NFAST) { tt = t0 + r / nnt; nt = r % nnt; }
+  else { tt = t0 + r % gt; nt = r / gt; }
+}
+
+template <int PER>
+__device__ __forceinline__ void wait_tiles(int ahead) {  // leave `ahead` tiles in flight
+  if (ahead >= 3) wait_vmem<3 * PER>();
+  else if (ahead == 2) wait_vmem<2 * PER>();
+  else if (ahead == 1) wait_vmem<PER>();
+  else wait_vmem<0>();
+}
+
+// BKD: K per stage (32 or 64); STAGES: LDS ring depth.
+template <int MODE, int ACT, int BKD, int STAGES>
+__global__ __launch_bounds__(kDmaThreads, 1) void k_gemm_dma(GemmParams p) {
+  constexpr int NW = kDmaWaves;
+  constexpr int CH = BKD / 8;              // 16-byte chunks per LDS row
+  constexpr int RPB = 64 / CH;             // rows per 1-KB load block
+  constexpr int BLK = 256 / RPB;           // blocks per operand per stage
+  constexpr int NH = BLK / NW;             // blocks per operand per wave
+  constexpr int PER = 2 * NH;              // loads per wave per stage
+  constexpr int S = BKD / 16;              // k-steps of 16 per stage
+  constexpr int WTR = kDmaBT / (NW / 2);   // routes per wave
+  constexpr int NJ = WTR / 32;             // 32-wide route blocks per wave
+  constexpr int REGION = 256 * BKD * 2;    // bytes of A (and of B) per stage
+  constexpr int STAGE = 2 * REGION;
+  static_assert(S % 2 == 0 && BLK % NW == 0 && 3 * PER <= 63, "tile shape");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE];
+  const uint32_t lds0 =
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nnt = gridDim.y;
+  const int ntiles = *p.n_tiles;
+  const int L = xcd_valid_remap(blockIdx.y * gridDim.x + blockIdx.x, ntiles * nnt);
+  if (L < 0) return;
+  int ti, nt;
+  dma_tile_order(L, ntiles, nnt, ti, nt);
+  const int g = p.tile_group[ti];
+  const int m0 = p.tile_m0[ti];
+  const bool shared = (g == p.E);
+  const int count = shared ? p.T : p.counts[g];
+  const int base = shared ? 0 : p.offsets[g];
+  int K, Nw;
+  if constexpr (MODE == GM_GATEUP) { K = p.H; Nw = shared ? p.Is : p.I; }
+  else { K = shared ? p.Is : p.I; Nw = p.H; }
+  const int nstep = (MODE == GM_GATEUP) ? kBW / 2 : kBW;
+  const int n0 = nt * nstep;
+  if (n0 >= Nw) return;
+
+  // ---- load sources: wave w fills blocks w, w+NW, ... of A and of B -----------
+  const uint8_t* a_base[NH];
+  uint32_t a_off[NH], b_off[NH];
+#pragma unroll
+  for (int h = 0; h < NH; ++h) {
+    const int blk = wave + NW * h;
+    const int row = blk * RPB + lane / CH;
+    const int c = dma_slot<CH>(row, lane % CH);  // the XOR is its own inverse
+    const uint16_t* m;
+    int wr;
+    if constexpr (MODE == GM_GATEUP) {  // first half of the blocks: gate rows, then up
+      m = blk < BLK / 2 ? (shared ? p.sw0 : p.w0) : (shared ? p.sw1 : p.w1);
+      wr = min(n0 + (row & 127), Nw - 1);  // clamped rows are never stored
+    } else {
+      m = shared ? p.sw0 : p.w0;
+      wr = min(n0 + row, Nw - 1);
+    }
+    a_base[h] = reinterpret_cast<const uint8_t*>(
+        uniform_ptr(m + (shared ? (size_t)0 : (size_t)g * Nw * K)));
+    a_off[h] = (uint32_t)wr * (uint32_t)K * 2u + (uint32_t)c * 16u;
+    const int rm = min(m0 + row, count - 1);  // clamped routes are never stored
+    uint32_t br;
+    if constexpr (MODE == GM_DOWN) br = (uint32_t)(shared ? rm : base + rm);
+    else br = (uint32_t)(shared ? rm : p.row_token[base + rm]);
+    b_off[h] = br * (uint32_t)K * 2u + (uint32_t)c * 16u;
+  }
+  const uint8_t* b_base = reinterpret_cast<const uint8_t*>(
+      uniform_ptr((MODE == GM_DOWN && shared) ? p.sact : p.act));
+
+  auto issue = [&](int kt, int st) {
+    const uint32_t sb = lds0 + (uint32_t)(st * STAGE);
+    const size_t ko = (size_t)kt * BKD * 2;
+#pragma unroll
+    for (int h = 0; h < NH; ++h) lds_dma16(a_off[h], a_base[h] + ko, sb + (wave + NW * h) * 1024);
+#pragma unroll
+    for (int h = 0; h < NH; ++h)
+      lds_dma16(b_off[h], b_base + ko, sb + REGION + (wave + NW * h) * 1024);
+  };
+
+  // ---- wave sub-tile: 128 weight rows x WTR routes ----------------------------
+  const int ww = wave & 1, wt = wave >> 1;
+  int arow[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (MODE == GM_GATEUP)  // blocks 0,1 gate, 2,3 up of the same features
+      arow[i] = (i >> 1) * 128 + 64 * ww + 32 * (i & 1);
+    else
+      arow[i] = 128 * ww + 32 * i;
+  }
+  const int brow0 = WTR * wt;
+  f32x16 acc[4][NJ];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+  const int fr = lane & 31, fk = lane >> 5;
+
+  // Fragments of k-step s (16 deep) of the tile in stage st.
+  auto frag = [&](int st, int s, bf16x8 (&af)[4], bf16x8 (&bfr)[NJ]) {
+    const uint16_t* sA = reinterpret_cast<const uint16_t*>(smem + st * STAGE);
+    const uint16_t* sB = reinterpret_cast<const uint16_t*>(smem + st * STAGE + REGION);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = arow[i] + fr;
+      af[i] = *reinterpret_cast<const bf16x8*>(&sA[r * BKD + (dma_slot<CH>(r, 2 * s + fk) << 3)]);
+    }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int r = brow0 + 32 * j + fr;
+      bfr[j] = *reinterpret_cast<const bf16x8*>(&sB[r * BKD + (dma_slot<CH>(r, 2 * s + fk) << 3)]);
+    }
+  };
+  auto mma = [&](const bf16x8 (&af)[4], const bf16x8 (&bfr)[NJ]) {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+  };
+
+  // ---- pipeline ---------------------------------------------------------------
+  // Iteration kt: for each k-step of tile kt, read the next k-step's fragments
+  // while multiplying the current ones; before the last k-step, wait for tile
+  // kt+1 and synchronise (after which nobody reads stage kt any more), refill
+  // that stage with tile kt+STAGES, and read the first fragments of tile
+  // kt+1 while the last k-step of tile kt is multiplied.  Fragment reads
+  // always overlap multiplies, and the barrier sits between two runs of
+  // multiplies.  The last tile is peeled off: a branch inside the loop body
+  // would make the wait-count pass merge two paths and wait for the
+  // prefetched reads.
+  const int nk = K / BKD;
+#pragma unroll
+  for (int t = 0; t < STAGES; ++t)
+    if (t < nk) issue(t, t);
+  wait_tiles<PER>(min(nk - 1, STAGES - 1));
+  __syncthreads();
+  bf16x8 fa[2][4], fb[2][NJ];
+  frag(0, 0, fa[0], fb[0]);
+  for (int kt = 0; kt + 1 < nk; ++kt) {
+    const int st = kt % STAGES;
+#pragma unroll
+    for (int s = 1; s < S; ++s) {
+      frag(st, s, fa[s & 1], fb[s & 1]);
+      mma(fa[(s - 1) & 1], fb[(s - 1) & 1]);
+    }
+    wait_tiles<PER>(min(nk - 2 - kt, STAGES - 2));
+    __syncthreads();
+    if (kt + STAGES < nk) issue(kt + STAGES, st);
+    frag((kt + 1) % STAGES, 0, fa[0], fb[0]);
+    mma(fa[1], fb[1]);
+  }
+  {
+    const int st = (nk - 1) % STAGES;
+#pragma unroll
+    for (int s = 1; s < S; ++s) {
+      frag(st, s, fa[s & 1], fb[s & 1]);
+      mma(fa[(s - 1) & 1], fb[(s - 1) & 1]);
+    }
+    mma(fa[1], fb[1]);
+  }
+
+  // ---- epilogue: acc[i][j][4q + v] = weight row arow[i] + 8q + 4*(lane>>5) + v,
+  //      route brow0 + 32 j + (lane & 31) -----------------------------------------
+  const int rsub = 4 * (lane >> 5);
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int m = m0 + brow0 + 32 * j + (lane & 31);
+    if (m >= count) continue;
+    uint16_t* outp = shared ? reinterpret_cast<uint16_t*>(p.sout) + (size_t)m * Nw
+                            : reinterpret_cast<uint16_t*>(p.out) + (size_t)(base + m) * Nw;
+    if constexpr (MODE == GM_GATEUP) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int f = n0 + arow[i] + 8 * q + rsub;  // gate rows: tile rows < 128
+          if (f < Nw) {
+            float hv[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {  // the shared expert is always SwiGLU
+              const float gv = acc[i][j][4 * q + v], uv = acc[i + 2][j][4 * q + v];
+              hv[v] = (shared ? silu_f(gv) : act_f<ACT>(gv)) * uv;
+            }
+            u32x2 pk;
+            pk[0] = pack_bf16x2(hv[0], hv[1]);
+            pk[1] = pack_bf16x2(hv[2], hv[3]);
+            *reinterpret_cast<u32x2*>(outp + f) = pk;
+          }
+        }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int n = n0 + arow[i] + 8 * q + rsub;
+          if (n < Nw) {
+            u32x2 pk;
+            pk[0] = pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
+            pk[1] = pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+            *reinterpret_cast<u32x2*>(outp + n) = pk;
+          }
+        }
+    }
+  }
+}
+
+}  // namespace moe

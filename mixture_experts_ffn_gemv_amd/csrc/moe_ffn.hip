@@ -15,6 +15,7 @@
 #include "common.h"
 #include "gemm.h"
 #include "gemm_big.h"
+#include "gemm_dma.h"
 #include "decode.h"
 #include "gemv.h"
 #include "route.h"
@@ -117,8 +118,16 @@ Plan make_plan(const moe_desc* d, int64_t T) {
   p.rc = (int)std::max<int64_t>(1, std::min<int64_t>({(int64_t)kRCMax, std::max<int64_t>(T, 1),
                                                       (int64_t)(16384 / p.H)}));
   p.nblk = (int)((p.R + kPermBlock - 1) / kPermBlock);
-  // 256-route tiles when the experts average that many routes, else 128
+  // 256-route tiles (direct-to-LDS kernel) when the experts average at least
+  // that many routes and every operand's row offsets fit in 32 bits
   p.bt = 128;
+  if (p.mfma && p.R >= (int64_t)kDmaBT * p.E) {
+    const uint64_t lim = 1ull << 32;
+    const uint64_t maxI = (uint64_t)std::max(p.I, p.Is);
+    const bool fits = (uint64_t)T * p.H * 2 < lim && (uint64_t)p.R * maxI * 2 < lim &&
+                      maxI * p.H * 2 < lim;
+    if (fits) p.bt = kDmaBT;
+  }
   p.max_tiles = (int)((p.R + p.bt - 1) / p.bt) + p.E + (p.shared ? (int)((T + p.bt - 1) / p.bt) : 0);
   p.max_groups = (int)std::min<int64_t>(p.E, p.R) + (p.shared ? 1 : 0);
   const size_t es = p.mfma ? 2 : 4;  // h / y element size
@@ -546,9 +555,9 @@ moe_status run_experts_mfma(const moe_desc* d, const Plan& p, const void* x,
   dim3 g1(p.max_tiles, (maxN + kBW / 2 - 1) / (kBW / 2));
   MOE_TRY(launch("gemm_gateup", s, [&] {
     const bool silu = d->activation == MOE_ACT_SILU;
-    if (p.bt == 256) {
-      if (silu) k_gemm_big<GM_GATEUP, ACT_SILU, 256><<<g1, 256, 0, s>>>(gu);
-      else k_gemm_big<GM_GATEUP, ACT_GELU_TANH, 256><<<g1, 256, 0, s>>>(gu);
+    if (p.bt == kDmaBT) {
+      if (silu) k_gemm_dma<GM_GATEUP, ACT_SILU, kDmaBK, kDmaRing><<<g1, kDmaThreads, 0, s>>>(gu);
+      else k_gemm_dma<GM_GATEUP, ACT_GELU_TANH, kDmaBK, kDmaRing><<<g1, kDmaThreads, 0, s>>>(gu);
     } else {
       if (silu) k_gemm_big<GM_GATEUP, ACT_SILU, 128><<<g1, 256, 0, s>>>(gu);
       else k_gemm_big<GM_GATEUP, ACT_GELU_TANH, 128><<<g1, 256, 0, s>>>(gu);
@@ -564,7 +573,7 @@ moe_status run_experts_mfma(const moe_desc* d, const Plan& p, const void* x,
   gd.sout = wsp<uint16_t>(ws, p.o_ys);
   dim3 g2(p.max_tiles, (p.H + kBW - 1) / kBW);
   MOE_TRY(launch("gemm_down", s, [&] {
-    if (p.bt == 256) k_gemm_big<GM_DOWN, 0, 256><<<g2, 256, 0, s>>>(gd);
+    if (p.bt == kDmaBT) k_gemm_dma<GM_DOWN, 0, kDmaBK, kDmaRing><<<g2, kDmaThreads, 0, s>>>(gd);
     else k_gemm_big<GM_DOWN, 0, 128><<<g2, 256, 0, s>>>(gd);
   }));
 

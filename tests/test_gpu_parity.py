@@ -51,6 +51,12 @@ SMALL = [
     MoeConfig(name="mfma_gelu_bias", T=257, H=128, I=192, E=32, k=8, act=ACT_GELU_TANH,
               weight_format=WF_BF16, act_dtype=DT_BF16, router_dtype=DT_BF16, bias=BIAS_ZIPF,
               shared=True, Is=64, seed_index=13),
+    # 256-route tiles with direct-to-LDS operand loads (>= 256 routes per expert)
+    MoeConfig(name="mfma_dma_shared", T=700, H=256, I=192, E=4, k=2, weight_format=WF_BF16,
+              act_dtype=DT_BF16, router_dtype=DT_BF16, shared=True, Is=128, seed_index=30),
+    MoeConfig(name="mfma_dma_gelu_bias", T=1100, H=128, I=320, E=2, k=1, act=ACT_GELU_TANH,
+              weight_format=WF_BF16, act_dtype=DT_BF16, router_dtype=DT_BF16, bias=BIAS_ZIPF,
+              seed_index=31),
     MoeConfig(name="mfma_t33", T=33, H=128, I=64, E=8, k=2, weight_format=WF_BF16,
               act_dtype=DT_BF16, router_dtype=DT_BF16, seed_index=14),
     MoeConfig(name="mfma_dense_e1", T=40, H=128, I=64, E=1, k=1, weight_format=WF_BF16,
