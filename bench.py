@@ -11,8 +11,10 @@ steps select different experts and the weights stream from HBM rather than
 from the 256 MB Infinity Cache (the full expert set is 1.5 GB).
 
 Prints one JSON line.  Fields beyond the common contract:
-  roofline      dominant kernel: algorithmic bytes (decode) or flops
-                (prefill) per launch over its average launch time, measured
+  roofline      dominant kernel: algorithmic bytes (decode) or flops or
+                bytes (prefill: whichever its arithmetic intensity makes
+                binding against the MI355X ridge point, both fractions
+                reported) per launch over its average launch time, measured
                 with hipEvents recorded on the launch stream around every
                 launch, in a second (eager) pass over the same K steps;
                 traffic = HBM bytes per launch (FETCH_SIZE + WRITE_SIZE,
@@ -170,15 +172,28 @@ def main():
         extra = {"path_weight_bytes": step_bytes,
                  "path_gbs": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1)}
     else:
+        # gate/up grouped GEMM: flops, and the bytes it must move at least
+        # (touched experts' gate+up weights, x, h written; shared expert alike)
         dom = "gemm_gateup"
         R = T * k
-        fl = 2.0 * (R * 2 * I * H + (T * 2 * cfg.Is * H if cfg.shared else 0))
-        achieved = fl / (kernel_ms[dom] * 1e-3) / 1e12
-        roof = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1),
-                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-                "traffic": recorded_traffic(cfg.name, dom),
-                "algorithmic_flops_per_launch": fl, "avg_launch_us": round(kernel_ms[dom] * 1e3, 2)}
+        Is = cfg.Is if cfg.shared else 0
+        fl = 2.0 * (R * 2 * I * H + T * 2 * Is * H)
+        by = (touched * 2 * I * H + 2 * Is * H) * bpw + T * H * 2 + (R * I + T * Is) * 2
+        sec = kernel_ms[dom] * 1e-3
+        tflops, gbs = fl / sec / 1e12, by / sec / 1e9
+        ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+        f_mfma, f_hbm = tflops / MFMA_BF16_PEAK_TFLOPS, gbs / HBM_PEAK_GBS
+        if fl / by >= ridge:   # arithmetic intensity above the ridge: bound by MFMA
+            roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(f_mfma, 4)}
+        else:
+            roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(f_hbm, 4)}
+        roof.update({"kernel": dom, "traffic": recorded_traffic(cfg.name, dom),
+                     "algorithmic_flops_per_launch": fl, "algorithmic_bytes_per_launch": by,
+                     "arithmetic_intensity": round(fl / by, 1), "ridge": round(ridge, 1),
+                     "frac_mfma": round(f_mfma, 4), "frac_hbm": round(f_hbm, 4),
+                     "avg_launch_us": round(kernel_ms[dom] * 1e3, 2)})
         tot = 2.0 * T * (k * 3 * I * H + (3 * cfg.Is * H if cfg.shared else 0) + (E + 1) * H)
         extra = {"path_flops": tot, "path_tflops": round(tot / (ms_per_step * 1e-3) / 1e12, 1)}
 

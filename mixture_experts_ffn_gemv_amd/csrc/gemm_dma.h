@@ -1,19 +1,20 @@
 // bf16 MFMA grouped GEMM for experts that average many routes (prefill with
 // at least 256 routes per expert): 256 weight rows x 256 routes per
-// workgroup, K in steps of 32.
+// workgroup, K in steps of 64.
 //
 // Operands reach LDS by direct global->LDS loads (global_load_lds_dwordx4):
-// no staging registers and no ds_write, so a 4-stage ring (128 KB) keeps three
-// K-steps of loads in flight ahead of the one being multiplied.  The loads are issued
-// from inline assembly and their completion waits are written out: the
-// compiler's own wait insertion cannot tell the ring's stages apart and
-// drains every load in flight at the top of the loop.
+// no staging registers and no ds_write.  The loads are issued from inline
+// assembly and their completion waits are written out: the compiler's own
+// wait insertion cannot tell the ring's stages apart and drains every load
+// in flight at the top of the loop.  K-steps of 64 make every load cover
+// whole 128-byte lines (half as many outstanding requests per byte as steps
+// of 32, whose extra ring depth measured no faster); a 2-stage ring of 64 KB
+// stages keeps one K-step in flight while the other is multiplied.
 //
 // Each load instruction of a wave fills 1 KB of LDS, lane i writing bytes
-// 16i..16i+15 of it.  The swizzled layout of k_gemm_big (16-byte chunk c of
-// 64-byte row r at slot c ^ ((r >> 2) & 3)) is obtained by the choice of
-// source: lane i of 1-KB block b loads row b*16 + i/4, chunk
-// (i & 3) ^ ((row >> 2) & 3).
+// 16i..16i+15 of it.  A swizzled layout (16-byte chunk c of row r at slot
+// c ^ ((r >> 1) & 7) for 128-byte rows) is obtained by the choice of source:
+// lane i of 1-KB block b loads row b*8 + i/8, chunk (i & 7) ^ ((row >> 1) & 7).
 //
 // kDmaWaves waves in a 2 (weight rows) x kDmaWaves/2 (routes) grid, each owning
 // 128 weight rows x 512/kDmaWaves routes of f32 accumulators (tiles of
@@ -27,17 +28,12 @@
 
 namespace moe {
 
-constexpr int kDmaBT = 256;        // routes per tile
-constexpr int kDmaWaves = 8;       // waves per workgroup
+constexpr int kDmaBT = 256;                    // routes per tile
+constexpr int kDmaWaves = 8;                   // waves per workgroup (2 per SIMD)
 constexpr int kDmaThreads = 64 * kDmaWaves;
-#ifndef MOE_DMA_BK
-#define MOE_DMA_BK 64
-#endif
-#ifndef MOE_DMA_RING
-#define MOE_DMA_RING 2
-#endif
-constexpr int kDmaBK = MOE_DMA_BK;      // K per stage
-constexpr int kDmaRing = MOE_DMA_RING;  // stages
+constexpr int kDmaBK = 64;                     // K per stage: full 128-byte rows
+constexpr int kDmaRing = 2;                    // LDS stages (2 x 64 KB)
+constexpr int kDmaGroupT = 8;                  // route tiles per tile-order group
 
 // One 1-KB direct load per wave: lane i reads 16 bytes at sbase + voff and
 // writes them to LDS byte address lds + 16 i.  M0, which carries the LDS
@@ -77,23 +73,17 @@ __device__ __forceinline__ int dma_slot(int row, int c) {
   else return c ^ ((row >> 1) & 7);
 }
 
-#ifndef MOE_DMA_GROUP
-#define MOE_DMA_GROUP 8
-#endif
-#ifndef MOE_DMA_NFAST
-#define MOE_DMA_NFAST 0
-#endif
-// Logical workgroup L -> (route tile, weight tile): groups of G route tiles x
-// all weight tiles; within a group route tiles vary fastest (or weight tiles,
-// with NFAST).
+// Logical workgroup L -> (route tile, weight tile): groups of kDmaGroupT
+// route tiles x all weight tiles, route tiles varying fastest, so the
+// workgroups resident on one XCD at a time share weight tiles (and route
+// tiles) in its L2.
 __device__ __forceinline__ void dma_tile_order(int L, int ntt, int nnt, int& tt, int& nt) {
-  constexpr int G = MOE_DMA_GROUP;
-  const int gsz = G * nnt;
+  const int gsz = kDmaGroupT * nnt;
   const int grp = L / gsz, r = L - grp * gsz;
-  const int t0 = grp * G;
-  const int gt = min(G, ntt - t0);
-  if (MOE_DMA_NFAST) { tt = t0 + r / nnt; nt = r % nnt; }
-  else { tt = t0 + r % gt; nt = r / gt; }
+  const int t0 = grp * kDmaGroupT;
+  const int gt = min(kDmaGroupT, ntt - t0);
+  tt = t0 + r % gt;
+  nt = r / gt;
 }
 
 template <int PER>
