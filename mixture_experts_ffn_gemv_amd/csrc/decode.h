@@ -391,6 +391,7 @@ struct Dec2Params {
   const float* wts;
   const float* sgate_val;
   float* out;    // [T, H]
+  float* y;      // [R, H] per-route down outputs (4-bit path)
   int T, E, k, H, I, Is, rc;
 };
 

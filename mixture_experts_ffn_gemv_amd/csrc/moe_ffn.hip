@@ -17,6 +17,7 @@
 #include "gemm_big.h"
 #include "gemm_dma.h"
 #include "decode.h"
+#include "decode_u4.h"
 #include "gemv.h"
 #include "route.h"
 
@@ -479,6 +480,60 @@ void launch_dn3(int u, dim3 grid, hipStream_t s, const Dec2Params& dp) {
   }
 }
 
+template <int MODE, int ACT>
+moe_status launch_u4(const char* name, int u, dim3 grid, size_t lds, hipStream_t s,
+                     const Dec2Params& dp) {
+  auto go = [&](auto kern) -> moe_status {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess)
+      return fail(MOE_HIP_ERROR, "setting %zu bytes of LDS for %s failed: %s", lds, name,
+                  hipGetErrorString(e));
+    return launch(name, s, [&] { kern<<<grid, 256, lds, s>>>(dp); });
+  };
+  switch (u) {
+    case 1: return go(k_dec_u4<MODE, ACT, 1>);
+    case 2: return go(k_dec_u4<MODE, ACT, 2>);
+    case 3: return go(k_dec_u4<MODE, ACT, 3>);
+    case 4: return go(k_dec_u4<MODE, ACT, 4>);
+    case 6: return go(k_dec_u4<MODE, ACT, 6>);
+    default: return go(k_dec_u4<MODE, ACT, 8>);
+  }
+}
+
+// 4-bit weights, T <= 32: gate/up and down with the routes' activations
+// staged in LDS, then the weighted combine.
+moe_status run_experts_u4(const moe_desc* d, const Plan& p, Dec2Params dp, float* out, void* ws,
+                          hipStream_t s) {
+  dp.y = wsp<float>(ws, p.o_y);
+  auto rc_for = [&](int K) {
+    return (int)std::max<int64_t>(1, std::min<int64_t>({(int64_t)kU4Routes, p.T,
+                                                         (int64_t)(kU4LdsMax / u4_route_bytes(K))}));
+  };
+  {
+    Dec2Params g = dp;
+    g.rc = rc_for(p.H);
+    const size_t lds = (size_t)g.rc * u4_route_bytes(p.H);
+    dim3 grid(p.max_groups, (p.I + kU4Rows - 1) / kU4Rows);
+    const int u = pick_u(p.H / 32);
+    if (d->activation == MOE_ACT_SILU) MOE_TRY((launch_u4<0, ACT_SILU>("gemv_gateup", u, grid, lds, s, g)));
+    else MOE_TRY((launch_u4<0, ACT_GELU_TANH>("gemv_gateup", u, grid, lds, s, g)));
+  }
+  {
+    Dec2Params g = dp;
+    g.rc = rc_for(p.I);
+    const size_t lds = (size_t)g.rc * u4_route_bytes(p.I);
+    dim3 grid(p.max_groups, (p.H + kU4Rows - 1) / kU4Rows);
+    MOE_TRY((launch_u4<1, 0>("gemv_down", pick_u(p.I / 32), grid, lds, s, g)));
+  }
+  const size_t nthr = (size_t)p.T * (p.H / 4);
+  return launch("combine", s, [&] {
+    k_combine<float><<<(unsigned)((nthr + 255) / 256), 256, 0, s>>>(
+        dp.y, nullptr, dp.wts, wsp<int32_t>(ws, p.o_pos), dp.sgate_val, out, (int)p.T, p.H, p.k,
+        0);
+  });
+}
+
 moe_status run_experts_small(const moe_desc* d, const Plan& p, const void* x,
                              const moe_weights* w, float* out, void* ws, hipStream_t s) {
   const int wf = d->weight_format;
@@ -503,6 +558,8 @@ moe_status run_experts_small(const moe_desc* d, const Plan& p, const void* x,
   dp.sgate_val = wsp<float>(ws, p.o_sgate);
   dp.out = out;
   dp.T = (int)p.T; dp.E = p.E; dp.k = p.k; dp.H = p.H; dp.I = p.I; dp.Is = p.Is; dp.rc = p.rc;
+
+  if (wf == MOE_WEIGHTS_U4_G32) return run_experts_u4(d, p, dp, out, ws, s);
 
   const int u1 = pick_u(p.H / epc);
   const bool direct = p.T == 1;

@@ -68,6 +68,13 @@ SMALL = [
               seed_index=17),
     MoeConfig(name="gemv_u4_small", T=5, H=256, I=128, E=16, k=4, weight_format=WF_U4,
               seed_index=18),
+    # 4-bit decode kernels: several staging passes per expert, bf16 x, one token, GELU
+    MoeConfig(name="gemv_u4_passes", T=32, H=256, I=192, E=4, k=2, weight_format=WF_U4,
+              seed_index=32),
+    MoeConfig(name="gemv_u4_bf16x_gelu", T=9, H=512, I=64, E=8, k=3, act=ACT_GELU_TANH,
+              weight_format=WF_U4, act_dtype=DT_BF16, router_dtype=DT_BF16, seed_index=33),
+    MoeConfig(name="gemv_u4_t1", T=1, H=1024, I=320, E=16, k=4, weight_format=WF_U4,
+              seed_index=34),
     MoeConfig(name="gemv_u4_many_routes", T=70, H=128, I=64, E=4, k=2, weight_format=WF_U4,
               seed_index=19),
     MoeConfig(name="gemv_f32_dense_e1", T=3, H=64, I=32, E=1, k=1, seed_index=20),
