@@ -340,7 +340,7 @@ __device__ void route_small_body(const float* __restrict__ logits, int T, int E,
 // workgroup invalidates its caches (device-scope acquire) before reading
 // them.  A device-scope release fence per workgroup would instead write
 // back the whole L2 of its XCD, which costs far more than the GEMV.
-template <typename XT, int RDT>
+template <typename XT, int RDT, int NC>
 __global__ __launch_bounds__(256) void k_router_route(const XT* __restrict__ x,
                                                       const void* __restrict__ router,
                                                       const float* __restrict__ bias,
@@ -349,8 +349,8 @@ __global__ __launch_bounds__(256) void k_router_route(const XT* __restrict__ x,
                                                       int E, int k, int ncols, int normalize,
                                                       int has_shared, int* __restrict__ ticket,
                                                       SmallRouteOut o) {
-  router_row<XT, RDT, true>(x, router, bias, shared_gate_inp, logits, T, H, E, ncols,
-                            blockIdx.x);
+  router_row<XT, RDT, true, NC>(x, router, bias, shared_gate_inp, logits, T, H, E, ncols,
+                                blockIdx.x);
   __shared__ int s_last;
   __builtin_amdgcn_s_waitcnt(0);  // this wave's logit stores have completed
   __syncthreads();

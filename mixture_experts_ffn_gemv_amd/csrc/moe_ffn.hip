@@ -10,6 +10,7 @@
 #include <mutex>
 #include <string>
 #include <vector>
+#include <type_traits>
 
 #include "../../include/moe_ffn.h"
 #include "common.h"
@@ -217,6 +218,20 @@ T* wsp(void* ws, size_t off) {
 }
 
 // ------------------------------------------------------------ launch steps
+// Calls go(XT{}, integral_constant<RDT>, integral_constant<NC>) for the
+// activation type, router dtype and chunks-per-thread of a router launch.
+template <class F>
+void dispatch_router(bool xb, bool rb, int nc, F&& go) {
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  auto by_nc = [&](auto xt, auto rt) {
+    if (nc == 1) go(xt, rt, std::integral_constant<int, 1>{});
+    else if (nc == 2) go(xt, rt, std::integral_constant<int, 2>{});
+    else go(xt, rt, std::integral_constant<int, 4>{});
+  };
+  if (xb) { if (rb) by_nc(uint16_t{}, I1{}); else by_nc(uint16_t{}, I0{}); }
+  else { if (rb) by_nc(float{}, I1{}); else by_nc(float{}, I0{}); }
+}
 moe_status run_router(const moe_desc* d, const Plan& p, const void* x, const moe_weights* w,
                       void* ws, hipStream_t s) {
   float* logits = wsp<float>(ws, p.o_logits);
@@ -234,23 +249,18 @@ moe_status run_router(const moe_desc* d, const Plan& p, const void* x, const moe
   }
   const bool xb = d->act_dtype == MOE_BF16, rb = d->router_dtype == MOE_BF16;
   dim3 grid(p.ncols);
+  const int nc = router_nc(p.H / (rb ? 8 : 4));
   return launch("router_gemv", s, [&] {
-    if (xb && rb)
-      k_router_gemv<uint16_t, 1><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(x), w->router,
+    auto go = [&](auto xtag, auto rtag, auto nctag) {
+      using XT = decltype(xtag);
+      constexpr int RDT = decltype(rtag)::value, NC = decltype(nctag)::value;
+      k_router_gemv<XT, RDT, NC><<<grid, 256, 0, s>>>(static_cast<const XT*>(x), w->router,
           w->router_bias, w->shared_gate_inp, logits, T, p.H, p.E, p.ncols);
-    else if (xb)
-      k_router_gemv<uint16_t, 0><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(x), w->router,
-          w->router_bias, w->shared_gate_inp, logits, T, p.H, p.E, p.ncols);
-    else if (rb)
-      k_router_gemv<float, 1><<<grid, 256, 0, s>>>(static_cast<const float*>(x), w->router,
-          w->router_bias, w->shared_gate_inp, logits, T, p.H, p.E, p.ncols);
-    else
-      k_router_gemv<float, 0><<<grid, 256, 0, s>>>(static_cast<const float*>(x), w->router,
-          w->router_bias, w->shared_gate_inp, logits, T, p.H, p.E, p.ncols);
+    };
+    dispatch_router(xb, rb, nc, go);
   });
 }
 
-// Decode routing: router logits and the routing in one launch.
 moe_status run_route_small(const moe_desc* d, const Plan& p, const void* x, const moe_weights* w,
                            void* ws, int32_t* user_ids, float* user_w, int32_t* user_counts,
                            int32_t* user_offsets, int32_t* user_perm, hipStream_t s) {
@@ -275,19 +285,15 @@ moe_status run_route_small(const moe_desc* d, const Plan& p, const void* x, cons
   const bool xb = d->act_dtype == MOE_BF16, rb = d->router_dtype == MOE_BF16;
   const int sh = p.shared ? 1 : 0, nz = d->normalize_topk;
   dim3 grid(p.ncols);
+  const int nc = router_nc(p.H / (rb ? 8 : 4));
   return launch("router_route", s, [&] {
-    if (xb && rb)
-      k_router_route<uint16_t, 1><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(x), w->router,
+    auto go = [&](auto xtag, auto rtag, auto nctag) {
+      using XT = decltype(xtag);
+      constexpr int RDT = decltype(rtag)::value, NC = decltype(nctag)::value;
+      k_router_route<XT, RDT, NC><<<grid, 256, 0, s>>>(static_cast<const XT*>(x), w->router,
           w->router_bias, w->shared_gate_inp, logits, T, p.H, p.E, p.k, p.ncols, nz, sh, ticket, o);
-    else if (xb)
-      k_router_route<uint16_t, 0><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(x), w->router,
-          w->router_bias, w->shared_gate_inp, logits, T, p.H, p.E, p.k, p.ncols, nz, sh, ticket, o);
-    else if (rb)
-      k_router_route<float, 1><<<grid, 256, 0, s>>>(static_cast<const float*>(x), w->router,
-          w->router_bias, w->shared_gate_inp, logits, T, p.H, p.E, p.k, p.ncols, nz, sh, ticket, o);
-    else
-      k_router_route<float, 0><<<grid, 256, 0, s>>>(static_cast<const float*>(x), w->router,
-          w->router_bias, w->shared_gate_inp, logits, T, p.H, p.E, p.k, p.ncols, nz, sh, ticket, o);
+    };
+    dispatch_router(xb, rb, nc, go);
   });
 }
 

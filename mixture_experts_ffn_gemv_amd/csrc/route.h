@@ -15,8 +15,11 @@ namespace moe {
 // --------------------------------------------------------------------------
 // RDT: 0 = f32 router, 1 = bf16 router.  COHERENT: logits are stored at
 // device scope (written through to the point of coherence of all XCDs), so
-// that another workgroup may read them within the same launch.
-template <typename XT, int RDT, bool COHERENT = false>
+// that another workgroup may read them within the same launch.  NC: chunks
+// per thread per block of the row; all loads of a (4-token, block) step are
+// issued before the first is used, with clamped indices so that none sits
+// behind a branch.
+template <typename XT, int RDT, bool COHERENT = false, int NC = 1>
 __device__ __forceinline__ void router_row(const XT* __restrict__ x, const void* __restrict__ router,
                                            const float* __restrict__ bias,
                                            const void* __restrict__ shared_gate_inp,
@@ -31,56 +34,72 @@ __device__ __forceinline__ void router_row(const XT* __restrict__ x, const void*
   __shared__ float red[4][4];
   for (int t0 = 0; t0 < T; t0 += 4) {
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int c = tid; c < cpr; c += 256) {
-      float w[EPC];
-      u32x4 v = ld16(row + (size_t)c * 16);
-      if constexpr (RDT) {
+    for (int cb = 0; cb < cpr; cb += 256 * NC) {
+      u32x4 wv[NC];
+      float xv[NC][4][EPC];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) { w[2 * q] = bf16lo(v[q]); w[2 * q + 1] = bf16hi(v[q]); }
-      } else {
+      for (int j = 0; j < NC; ++j) {
+        const int c = min(cb + tid + 256 * j, cpr - 1);
+        wv[j] = ld16(row + (size_t)c * 16);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) w[q] = __uint_as_float(v[q]);
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        if (t0 + r < T) {
-          const XT* xr = x + (size_t)(t0 + r) * H + (size_t)c * EPC;
-          float s = 0.f;
+        for (int r = 0; r < 4; ++r) {
+          const XT* xr = x + (size_t)min(t0 + r, T - 1) * H + (size_t)c * EPC;
 #pragma unroll
           for (int q = 0; q < EPC; ++q) {
-            float xv;
-            if constexpr (sizeof(XT) == 4) xv = xr[q];
-            else xv = bf16_to_f32(xr[q]);
-            s = fmaf(w[q], xv, s);
+            if constexpr (sizeof(XT) == 4) xv[j][r][q] = xr[q];
+            else xv[j][r][q] = bf16_to_f32(xr[q]);
           }
-          acc[r] += s;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < NC; ++j) {
+        if (cb + tid + 256 * j < cpr) {
+          float w[EPC];
+          if constexpr (RDT) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) { w[2 * q] = bf16lo(wv[j][q]); w[2 * q + 1] = bf16hi(wv[j][q]); }
+          } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) w[q] = __uint_as_float(wv[j][q]);
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float sdot = 0.f;
+#pragma unroll
+            for (int q = 0; q < EPC; ++q) sdot = fmaf(w[q], xv[j][r][q], sdot);
+            acc[r] += sdot;
+          }
         }
       }
     }
-    const int wv = tid >> 6, ln = tid & 63;
+    const int wv2 = tid >> 6, ln = tid & 63;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      float s = wave_sum(acc[r]);
-      if (ln == 0) red[wv][r] = s;
+      float sm = wave_sum(acc[r]);
+      if (ln == 0) red[wv2][r] = sm;
     }
     __syncthreads();
     if (tid < 4 && t0 + tid < T) {
-      float s = red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];
-      if (e < E && bias) s += bias[e];
+      float sm = red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];
+      if (e < E && bias) sm += bias[e];
       float* dst = logits + (size_t)(t0 + tid) * ncols + e;
-      if constexpr (COHERENT) __hip_atomic_store(dst, s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      else *dst = s;
+      if constexpr (COHERENT) __hip_atomic_store(dst, sm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else *dst = sm;
     }
     __syncthreads();
   }
 }
 
-template <typename XT, int RDT>
+// chunks per thread for a row of `cpr` 16-byte chunks (one block when it fits in 4)
+inline int router_nc(int cpr) { return cpr <= 256 ? 1 : cpr <= 512 ? 2 : 4; }
+
+template <typename XT, int RDT, int NC>
 __global__ __launch_bounds__(256) void k_router_gemv(
     const XT* __restrict__ x, const void* __restrict__ router,
     const float* __restrict__ bias, const void* __restrict__ shared_gate_inp,
     float* __restrict__ logits, int T, int H, int E, int ncols) {
-  router_row<XT, RDT>(x, router, bias, shared_gate_inp, logits, T, H, E, ncols, blockIdx.x);
+  router_row<XT, RDT, false, NC>(x, router, bias, shared_gate_inp, logits, T, H, E, ncols,
+                                 blockIdx.x);
 }
 
 // --------------------------------------------------------------------------
