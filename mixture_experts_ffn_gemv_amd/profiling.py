@@ -26,10 +26,26 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_JSON = os.path.join(os.path.dirname(PKG), "profiles", "traffic.json")
 
 
-def kernel_source_sha() -> str:
-    """sha256 over every kernel source file (name and bytes, sorted)."""
+# Source files each timed kernel is built from (device code and its launch).
+KERNEL_SOURCES = {
+    "gemv_gateup": ["common.h", "gemv.h", "route.h", "decode.h", "decode_u4.h", "moe_ffn.hip"],
+    "gemv_down_combine": ["common.h", "gemv.h", "route.h", "decode.h", "moe_ffn.hip"],
+    "gemv_down": ["common.h", "gemv.h", "route.h", "decode.h", "decode_u4.h", "moe_ffn.hip"],
+    "router_route": ["common.h", "route.h", "decode.h", "moe_ffn.hip"],
+    "gemm_gateup": ["common.h", "gemm.h", "gemm_big.h", "gemm_dma.h", "moe_ffn.hip"],
+    "gemm_down": ["common.h", "gemm.h", "gemm_big.h", "gemm_dma.h", "moe_ffn.hip"],
+}
+
+
+def kernel_source_sha(kernel: str = None) -> str:
+    """sha256 over the named kernel's source files (every kernel source file
+    when `kernel` is None), names and bytes, sorted."""
+    if kernel is None:
+        files = sorted(glob.glob(os.path.join(PKG, "csrc", "*")))
+    else:
+        files = sorted(os.path.join(PKG, "csrc", f) for f in KERNEL_SOURCES[kernel])
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(PKG, "csrc", "*"))):
+    for f in files:
         h.update(os.path.basename(f).encode())
         with open(f, "rb") as fh:
             h.update(fh.read())
@@ -38,17 +54,15 @@ def kernel_source_sha() -> str:
 
 def recorded_traffic(workload: str, kernel: str):
     """HBM bytes (read + write) per launch of `kernel` on `workload`, from the
-    committed counter record, or None when there is none or the kernel
+    committed counter record, or None when there is none or the kernel's
     sources have changed since the counters were taken."""
     try:
         with open(TRAFFIC_JSON) as fh:
             rec = json.load(fh)
     except (OSError, ValueError):
         return None
-    if rec.get("source_sha256") != kernel_source_sha():
-        return None
     k = rec.get("kernels", {}).get(workload, {}).get(kernel)
-    if not k:
+    if not k or kernel not in KERNEL_SOURCES or k.get("source_sha256") != kernel_source_sha(kernel):
         return None
     return k["fetch_bytes"] + k["write_bytes"]
 
@@ -85,11 +99,8 @@ def cmd_traffic(a) -> None:
     try:
         with open(a.out) as fh:
             rec = json.load(fh)
-        if rec.get("source_sha256") != kernel_source_sha():
-            rec = {}
     except (OSError, ValueError):
         rec = {}
-    rec["source_sha256"] = kernel_source_sha()
     rec.setdefault("kernels", {})
     cal = rec.setdefault("calibration", {})
     cal[a.workload] = {"copy_mib": a.copy_mib, "fetch_factor": fetch_factor,
@@ -99,6 +110,7 @@ def cmd_traffic(a) -> None:
         label, key = spec.split("=", 1)
         fv, wv = _find(f, key), _find(w, key)
         ks[label] = {"symbol": key,
+                     "source_sha256": kernel_source_sha(label) if label in KERNEL_SOURCES else None,
                      "fetch_kib": sum(fv) / len(fv), "write_kib": sum(wv) / len(wv),
                      "fetch_bytes": sum(fv) / len(fv) * 1024.0 * fetch_factor,
                      "write_bytes": sum(wv) / len(wv) * 1024.0 * write_factor}
