@@ -274,4 +274,52 @@ __global__ __launch_bounds__(256) void k_combine(const YT* __restrict__ y,
   *reinterpret_cast<f32x4*>(out + (size_t)t * H + c) = o;
 }
 
+// Prefill combine with bf16 y: 8 consecutive outputs per thread, so every
+// y row is read in 16-byte pieces, and the k rows of a token are loaded 8 at a
+// time before they are summed (slot order kept: padded slots add 0 * y).
+__global__ __launch_bounds__(256) void k_combine_bf16x8(const uint16_t* __restrict__ y,
+                                                        const uint16_t* __restrict__ ys,
+                                                        const float* __restrict__ wts,
+                                                        const int32_t* __restrict__ pos_of_route,
+                                                        const float* __restrict__ sgate,
+                                                        float* __restrict__ out, int T, int H,
+                                                        int k, int has_shared) {
+  const int cols8 = H / 8;
+  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (size_t)T * cols8) return;
+  const int t = idx / cols8;
+  const int c = (idx % cols8) * 8;
+  float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int j0 = 0; j0 < k; j0 += 8) {
+    u32x4 v[8];
+    float w[8];
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const int j = min(j0 + jj, k - 1);
+      const size_t pos = pos_of_route[(size_t)t * k + j];
+      v[jj] = *reinterpret_cast<const u32x4*>(y + pos * H + c);
+      w[jj] = (j0 + jj < k) ? wts[(size_t)t * k + j] : 0.f;
+    }
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        a[2 * q] = fmaf(w[jj], bf16lo(v[jj][q]), a[2 * q]);
+        a[2 * q + 1] = fmaf(w[jj], bf16hi(v[jj][q]), a[2 * q + 1]);
+      }
+  }
+  if (has_shared) {
+    const float s = sgate[t];
+    const u32x4 v = *reinterpret_cast<const u32x4*>(ys + (size_t)t * H + c);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      a[2 * q] = fmaf(s, bf16lo(v[q]), a[2 * q]);
+      a[2 * q + 1] = fmaf(s, bf16hi(v[q]), a[2 * q + 1]);
+    }
+  }
+  f32x4* o = reinterpret_cast<f32x4*>(out + (size_t)t * H + c);
+  o[0] = f32x4{a[0], a[1], a[2], a[3]};
+  o[1] = f32x4{a[4], a[5], a[6], a[7]};
+}
+
 }  // namespace moe

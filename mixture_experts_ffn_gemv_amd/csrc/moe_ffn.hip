@@ -640,9 +640,9 @@ moe_status run_experts_mfma(const moe_desc* d, const Plan& p, const void* x,
     else k_gemm_big<GM_DOWN, 0, 128><<<g2, 256, 0, s>>>(gd);
   }));
 
-  const size_t nthr = (size_t)p.T * (p.H / 4);
+  const size_t nthr = (size_t)p.T * (p.H / 8);
   return launch("combine", s, [&] {
-    k_combine<uint16_t><<<(unsigned)((nthr + 255) / 256), 256, 0, s>>>(
+    k_combine_bf16x8<<<(unsigned)((nthr + 255) / 256), 256, 0, s>>>(
         wsp<uint16_t>(ws, p.o_y), wsp<uint16_t>(ws, p.o_ys), wsp<float>(ws, p.o_wts),
         wsp<int32_t>(ws, p.o_pos), wsp<float>(ws, p.o_sgate), out, (int)p.T, p.H, p.k,
         p.shared ? 1 : 0);
