@@ -22,6 +22,8 @@
 // rows are 32-bit (the host checks that every operand fits).
 #pragma once
 
+#include <type_traits>
+
 #include "common.h"
 #include "gemm.h"
 #include "gemm_big.h"
@@ -34,6 +36,10 @@ constexpr int kDmaThreads = 64 * kDmaWaves;
 constexpr int kDmaBK = 64;                     // K per stage: full 128-byte rows
 constexpr int kDmaRing = 2;                    // LDS stages (2 x 64 KB)
 constexpr int kDmaGroupT = 8;                  // route tiles per tile-order group
+#ifndef MOE_DMA_MIN_AVG_ROUTES
+#define MOE_DMA_MIN_AVG_ROUTES 96
+#endif
+constexpr int kDmaMinAvgRoutes = MOE_DMA_MIN_AVG_ROUTES;  // mean routes per expert
 
 // One 1-KB direct load per wave: lane i reads 16 bytes at sbase + voff and
 // writes them to LDS byte address lds + 16 i.  M0, which carries the LDS
@@ -184,6 +190,12 @@ __global__ __launch_bounds__(kDmaThreads, 1) void k_gemm_dma(GemmParams p) {
       arow[i] = 128 * ww + 32 * i;
   }
   const int brow0 = WTR * wt;
+  // 32-route blocks of this wave that hold routes of the tile: a tile with
+  // fewer than kDmaBT routes (an expert's last tile) skips the fragment reads
+  // and multiplies of the empty blocks.  Waves whose blocks are all empty
+  // still load their share of the operands and join every barrier.
+  const int tile_rows = min(kDmaBT, count - m0);
+  const int nja = min(NJ, max(0, (tile_rows - brow0 + 31) >> 5));
   f32x16 acc[4][NJ];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -192,29 +204,6 @@ __global__ __launch_bounds__(kDmaThreads, 1) void k_gemm_dma(GemmParams p) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
   const int fr = lane & 31, fk = lane >> 5;
-
-  // Fragments of k-step s (16 deep) of the tile in stage st.
-  auto frag = [&](int st, int s, bf16x8 (&af)[4], bf16x8 (&bfr)[NJ]) {
-    const uint16_t* sA = reinterpret_cast<const uint16_t*>(smem + st * STAGE);
-    const uint16_t* sB = reinterpret_cast<const uint16_t*>(smem + st * STAGE + REGION);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = arow[i] + fr;
-      af[i] = *reinterpret_cast<const bf16x8*>(&sA[r * BKD + (dma_slot<CH>(r, 2 * s + fk) << 3)]);
-    }
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int r = brow0 + 32 * j + fr;
-      bfr[j] = *reinterpret_cast<const bf16x8*>(&sB[r * BKD + (dma_slot<CH>(r, 2 * s + fk) << 3)]);
-    }
-  };
-  auto mma = [&](const bf16x8 (&af)[4], const bf16x8 (&bfr)[NJ]) {
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-  };
 
   // ---- pipeline ---------------------------------------------------------------
   // Iteration kt: for each k-step of tile kt, read the next k-step's fragments
@@ -225,37 +214,71 @@ __global__ __launch_bounds__(kDmaThreads, 1) void k_gemm_dma(GemmParams p) {
   // always overlap multiplies, and the barrier sits between two runs of
   // multiplies.  The last tile is peeled off: a branch inside the loop body
   // would make the wait-count pass merge two paths and wait for the
-  // prefetched reads.
+  // prefetched reads.  NA (the wave's non-empty route blocks) is a template
+  // constant so that no branch sits between the reads and the multiplies.
   const int nk = K / BKD;
+  auto pipeline = [&](auto na_c) {
+    constexpr int NA = decltype(na_c)::value;
+    // Fragments of k-step s (16 deep) of the tile in stage st.
+    auto frag = [&](int st, int s, bf16x8 (&af)[4], bf16x8 (&bfr)[NJ]) {
+      if constexpr (NA > 0) {
+        const uint16_t* sA = reinterpret_cast<const uint16_t*>(smem + st * STAGE);
+        const uint16_t* sB = reinterpret_cast<const uint16_t*>(smem + st * STAGE + REGION);
 #pragma unroll
-  for (int t = 0; t < STAGES; ++t)
-    if (t < nk) issue(t, t);
-  wait_tiles<PER>(min(nk - 1, STAGES - 1));
-  __syncthreads();
-  bf16x8 fa[2][4], fb[2][NJ];
-  frag(0, 0, fa[0], fb[0]);
-  for (int kt = 0; kt + 1 < nk; ++kt) {
-    const int st = kt % STAGES;
+        for (int i = 0; i < 4; ++i) {
+          const int r = arow[i] + fr;
+          af[i] = *reinterpret_cast<const bf16x8*>(
+              &sA[r * BKD + (dma_slot<CH>(r, 2 * s + fk) << 3)]);
+        }
 #pragma unroll
-    for (int s = 1; s < S; ++s) {
-      frag(st, s, fa[s & 1], fb[s & 1]);
-      mma(fa[(s - 1) & 1], fb[(s - 1) & 1]);
-    }
-    wait_tiles<PER>(min(nk - 2 - kt, STAGES - 2));
+        for (int j = 0; j < NA; ++j) {
+          const int r = brow0 + 32 * j + fr;
+          bfr[j] = *reinterpret_cast<const bf16x8*>(
+              &sB[r * BKD + (dma_slot<CH>(r, 2 * s + fk) << 3)]);
+        }
+      }
+    };
+    auto mma = [&](const bf16x8 (&af)[4], const bf16x8 (&bfr)[NJ]) {
+#pragma unroll
+      for (int j = 0; j < NA; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    };
+#pragma unroll
+    for (int t = 0; t < STAGES; ++t)
+      if (t < nk) issue(t, t);
+    wait_tiles<PER>(min(nk - 1, STAGES - 1));
     __syncthreads();
-    if (kt + STAGES < nk) issue(kt + STAGES, st);
-    frag((kt + 1) % STAGES, 0, fa[0], fb[0]);
-    mma(fa[1], fb[1]);
-  }
-  {
-    const int st = (nk - 1) % STAGES;
+    bf16x8 fa[2][4], fb[2][NJ];
+    frag(0, 0, fa[0], fb[0]);
+    for (int kt = 0; kt + 1 < nk; ++kt) {
+      const int st = kt % STAGES;
 #pragma unroll
-    for (int s = 1; s < S; ++s) {
-      frag(st, s, fa[s & 1], fb[s & 1]);
-      mma(fa[(s - 1) & 1], fb[(s - 1) & 1]);
+      for (int s = 1; s < S; ++s) {
+        frag(st, s, fa[s & 1], fb[s & 1]);
+        mma(fa[(s - 1) & 1], fb[(s - 1) & 1]);
+      }
+      wait_tiles<PER>(min(nk - 2 - kt, STAGES - 2));
+      __syncthreads();
+      if (kt + STAGES < nk) issue(kt + STAGES, st);
+      frag((kt + 1) % STAGES, 0, fa[0], fb[0]);
+      mma(fa[1], fb[1]);
     }
-    mma(fa[1], fb[1]);
-  }
+    {
+      const int st = (nk - 1) % STAGES;
+#pragma unroll
+      for (int s = 1; s < S; ++s) {
+        frag(st, s, fa[s & 1], fb[s & 1]);
+        mma(fa[(s - 1) & 1], fb[(s - 1) & 1]);
+      }
+      mma(fa[1], fb[1]);
+    }
+  };
+  static_assert(NJ == 2, "one pipeline instance per count of non-empty blocks");
+  if (nja == 2) pipeline(std::integral_constant<int, 2>{});
+  else if (nja == 1) pipeline(std::integral_constant<int, 1>{});
+  else pipeline(std::integral_constant<int, 0>{});
 
   // ---- epilogue: acc[i][j][4q + v] = weight row arow[i] + 8q + 4*(lane>>5) + v,
   //      route brow0 + 32 j + (lane & 31) -----------------------------------------

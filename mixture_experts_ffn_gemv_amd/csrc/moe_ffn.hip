@@ -121,9 +121,11 @@ Plan make_plan(const moe_desc* d, int64_t T) {
                                                       (int64_t)(16384 / p.H)}));
   p.nblk = (int)((p.R + kPermBlock - 1) / kPermBlock);
   // 256-route tiles (direct-to-LDS kernel) when the experts average at least
-  // that many routes and every operand's row offsets fit in 32 bits
+  // kDmaMinAvgRoutes routes, so that most experts fit in one route tile and
+  // their weights are streamed once, and every operand's row offsets fit in
+  // 32 bits
   p.bt = 128;
-  if (p.mfma && p.R >= (int64_t)kDmaBT * p.E) {
+  if (p.mfma && p.R >= (int64_t)kDmaMinAvgRoutes * p.E) {
     const uint64_t lim = 1ull << 32;
     const uint64_t maxI = (uint64_t)std::max(p.I, p.Is);
     const bool fits = (uint64_t)T * p.H * 2 < lim && (uint64_t)p.R * maxI * 2 < lim &&
