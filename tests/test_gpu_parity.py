@@ -77,6 +77,11 @@ SMALL = [
               seed_index=34),
     MoeConfig(name="gemv_u4_many_routes", T=70, H=128, I=64, E=4, k=2, weight_format=WF_U4,
               seed_index=19),
+    # one token, bf16 weights (gate/up activations straight from x), shared expert
+    MoeConfig(name="gemv_bf16_shared_t1", T=1, H=1024, I=320, E=16, k=4, weight_format=WF_BF16,
+              router_dtype=DT_BF16, shared=True, Is=192, seed_index=35),
+    MoeConfig(name="gemv_bf16x_gelu_t1", T=1, H=512, I=256, E=64, k=8, act=ACT_GELU_TANH,
+              weight_format=WF_BF16, act_dtype=DT_BF16, router_dtype=DT_BF16, seed_index=36),
     MoeConfig(name="gemv_f32_dense_e1", T=3, H=64, I=32, E=1, k=1, seed_index=20),
     MoeConfig(name="gemv_f32_k32", T=2, H=64, I=32, E=256, k=32, seed_index=21),
     MoeConfig(name="gemv_bf16_f32x_t32", T=32, H=2816, I=704, E=128, k=8, act=ACT_GELU_TANH,
@@ -183,3 +188,4 @@ def test_workspace_reuse_across_calls_and_token_counts():
         assert float(np.abs(w.cpu().numpy() - ref_w[:T]).max()) <= 1e-5
         assert rel_err(out.cpu().numpy(), ref_out[:T]) <= 2e-2
     assert int(ws[:M.WORKSPACE_ZERO_BYTES].count_nonzero()) == 0
+
