@@ -50,6 +50,9 @@ def parse():
     ap.add_argument("--eager", action="store_true", help="no HIP graph replay")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--gating", choices=["softmax", "sigmoid"], default="softmax",
+                    help="routing scores (the workloads are quoted with softmax)")
+    ap.add_argument("--routed-scale", type=float, default=1.0)
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="first run one plain device copy of this many MiB (a kernel of known "
                          "traffic, to scale hardware byte counters)")
@@ -87,7 +90,8 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     inp = generate(cfg, backend="torch", device=dev)
-    desc = M.make_desc(**desc_kwargs(cfg))
+    gating = {"softmax": M.GATING_SOFTMAX, "sigmoid": M.GATING_SIGMOID}[args.gating]
+    desc = M.make_desc(**desc_kwargs(cfg, gating=gating, routed_scale=args.routed_scale))
     w = M.make_weights(**weights_kwargs(inp))
     T = cfg.T
     decode = T <= 32
@@ -199,7 +203,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(cfg, inp, xs, args.cpu_seconds)
+        cpu = cpu_baseline(cfg, inp, xs, args.cpu_seconds, gating, args.routed_scale)
 
     line = {
         "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -212,6 +216,7 @@ def main():
                    "weights": ["f32", "bf16", "u4_g32"][cfg.weight_format],
                    "activations": ["f32", "bf16"][cfg.act_dtype],
                    "shared_expert": cfg.Is if cfg.shared else 0,
+                   "gating": args.gating, "routed_scale": args.routed_scale,
                    "touched_experts": touched, "token_pool": P,
                    "launch": "eager" if graph is None else f"hipgraph x{P} steps",
                    "parallelism": "single-gpu"},
@@ -240,7 +245,7 @@ def _host_copy(inp):
     return hv
 
 
-def cpu_baseline(cfg, inp, xs, seconds):
+def cpu_baseline(cfg, inp, xs, seconds, gating=0, scale=1.0):
     """The float64 CPU oracle, as it stands, on a bounded sample of tokens."""
     from threadpoolctl import threadpool_info
     from moe_synth.device import HostView
@@ -258,7 +263,7 @@ def cpu_baseline(cfg, inp, xs, seconds):
         for tok in range(cfg.T):
             src = WeightSource(host, cache=False)
             t0 = time.perf_counter()
-            moe_ffn(host, tokens=[tok], src=src)
+            moe_ffn(host, tokens=[tok], src=src, gating=gating, scale=scale)
             t_total += time.perf_counter() - t0
             n_done += 1
             if t_total >= seconds:

@@ -6,10 +6,12 @@
  * ("MoE FFN op order"):
  *
  *   1. router logits      l[t,e] = x[t,:] . router[e,:] (+ router_bias[e])
- *   2. routing            softmax over the E logits, the top_k experts by
- *                         probability (ties: lower expert index first),
- *                         weights renormalised over the selected experts
- *                         (hf2q softmax_topk_renorm_cpu)
+ *   2. routing            softmax over the E logits (or a sigmoid per
+ *                         logit, moe_gating), the top_k experts by score
+ *                         (ties: lower expert index first), weights
+ *                         renormalised over the selected experts
+ *                         (hf2q softmax_topk_renorm_cpu), times
+ *                         routed_scale
  *   3. routed experts     for each selected expert e of token t:
  *                         h = act(gate[e] x) * (up[e] x),  y = down[e] h
  *                         (act = SiLU, or the tanh form of GELU used by
@@ -58,7 +60,7 @@
 extern "C" {
 #endif
 
-#define MOE_FFN_ABI_VERSION 2
+#define MOE_FFN_ABI_VERSION 3
 
 /* Leading workspace bytes that must be zero before a workspace's first use. */
 #define MOE_WORKSPACE_ZERO_BYTES 256
@@ -94,6 +96,17 @@ typedef enum moe_activation {
 
 typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
+/* Routing scores from the router logits l (ferrox-models decoder.rs: the
+ * gating function of the MoE config; its dense-layer note states that
+ * sigmoid gating with renormalisation divides a selected score by the sum
+ * of the selected scores).  Either way the k experts with the largest
+ * scores are selected, the lower expert index first among equal scores;
+ * both scores are increasing in l, so this is the order of the logits. */
+typedef enum moe_gating {
+  MOE_GATING_SOFTMAX = 0,  /* p = softmax(l) over all E experts           */
+  MOE_GATING_SIGMOID = 1   /* p_e = 1 / (1 + exp(-l_e)), each on its own   */
+} moe_gating;
+
 /* Shape and format attributes (ferrum-kernels MoeAttributes). */
 typedef struct moe_desc {
   int32_t hidden;              /* H                                          */
@@ -104,10 +117,14 @@ typedef struct moe_desc {
   int32_t weight_format;       /* moe_weight_format (routed and shared)      */
   int32_t act_dtype;           /* moe_dtype of x                             */
   int32_t router_dtype;        /* moe_dtype of router and shared_gate_inp    */
-  int32_t normalize_topk;      /* 1: renormalise the k weights; 0: raw probs */
+  int32_t normalize_topk;      /* 1: renormalise the k weights; 0: raw scores */
   int32_t has_shared_expert;   /* 0 or 1                                     */
   int32_t shared_intermediate; /* Is (ignored without a shared expert)       */
   int32_t group_size;          /* 32 for MOE_WEIGHTS_U4_G32, else ignored    */
+  int32_t gating;              /* moe_gating                                 */
+  float routed_scale;          /* every routing weight is multiplied by it
+                                  (llama.cpp's w_scale, which ferrox-models
+                                  names in gpt_oss_ffn); finite, 1 for none */
 } moe_desc;
 
 typedef struct moe_u4_matrix {
@@ -154,8 +171,8 @@ moe_status moe_workspace_size(const moe_desc* desc, int64_t num_tokens,
  *   x              [T, H] act_dtype
  *   topk_ids       [T, k] int32 out: slot j holds the j-th most probable
  *                  expert (lower index first among equal probabilities)
- *   topk_w         [T, k] f32 out: routing weights (sum to 1 per token when
- *                  normalize_topk)
+ *   topk_w         [T, k] f32 out: routing weights (sum to routed_scale per
+ *                  token when normalize_topk)
  *   expert_counts  [E] int32 out or NULL: routes that chose each expert
  *   expert_offsets [E+1] int32 out or NULL: exclusive prefix sum of counts
  *   route_perm     [T*k] int32 out or NULL: the flat routes r = t*k + j

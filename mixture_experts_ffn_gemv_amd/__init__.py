@@ -30,6 +30,7 @@ WORKSPACE_ZERO_BYTES = 256   # MOE_WORKSPACE_ZERO_BYTES: leading bytes zeroed be
 
 WEIGHTS_F32, WEIGHTS_BF16, WEIGHTS_U4_G32 = 0, 1, 2
 ACT_SILU, ACT_GELU_TANH = 0, 1
+GATING_SOFTMAX, GATING_SIGMOID = 0, 1
 DT_F32, DT_BF16 = 0, 1
 
 EXPORTED_SYMBOLS = ("moe_abi_version", "moe_last_error", "moe_workspace_size", "moe_route",
@@ -47,7 +48,7 @@ class Desc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "hidden", "intermediate", "num_experts", "top_k", "activation", "weight_format",
         "act_dtype", "router_dtype", "normalize_topk", "has_shared_expert",
-        "shared_intermediate", "group_size")]
+        "shared_intermediate", "group_size", "gating")] + [("routed_scale", ctypes.c_float)]
 
 
 class U4Matrix(ctypes.Structure):
@@ -104,10 +105,11 @@ def _check(status: int):
 
 def make_desc(hidden, intermediate, num_experts, top_k, activation=ACT_SILU,
               weight_format=WEIGHTS_BF16, act_dtype=DT_F32, router_dtype=DT_F32,
-              normalize_topk=True, shared_intermediate=0, group_size=32) -> Desc:
+              normalize_topk=True, shared_intermediate=0, group_size=32,
+              gating=GATING_SOFTMAX, routed_scale=1.0) -> Desc:
     return Desc(hidden, intermediate, num_experts, top_k, activation, weight_format, act_dtype,
                 router_dtype, int(bool(normalize_topk)), int(shared_intermediate > 0),
-                shared_intermediate, group_size)
+                shared_intermediate, group_size, gating, routed_scale)
 
 
 def _ptr(t) -> Optional[int]:

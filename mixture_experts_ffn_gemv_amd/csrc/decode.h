@@ -167,7 +167,7 @@ struct RouteLds {
 // few-token case runs a short instruction stream.
 template <int TMAX>
 __device__ __forceinline__ void route_small_impl(const float* __restrict__ logits, int T, int E,
-                                                 int k, int ncols, int normalize, int has_shared,
+                                                 int k, int ncols, RouteMode rm, int has_shared,
                                                  const SmallRouteOut& o, RouteLds& L) {
   float* s_l = L.l;
   int8_t* s_sel = L.sel;
@@ -230,10 +230,12 @@ __device__ __forceinline__ void route_small_impl(const float* __restrict__ logit
       const float* lt = s_l + t * E;
       const int id = lane < k ? s_rid[t * k + lane] : 0;
       const float lmax = lt[s_rid[t * k]];
-      const float ex = lane < k ? __expf(lt[id] - lmax) : 0.f;
+      const float ex = lane < k ? (rm.sigmoid ? sigmoid_f(lt[id]) : __expf(lt[id] - lmax)) : 0.f;
       float denom;
-      if (normalize) {
+      if (rm.normalize) {
         denom = wave_sum(ex);
+      } else if (rm.sigmoid) {
+        denom = 1.f;
       } else {
         float sum = 0.f;
         for (int e = lane; e < E; e += 64) sum += __expf(lt[e] - lmax);
@@ -241,7 +243,7 @@ __device__ __forceinline__ void route_small_impl(const float* __restrict__ logit
       }
       if (lane < k) {
         const int r = t * k + lane;
-        const float w = ex / denom;
+        const float w = ex / denom * rm.scale;
         o.ids[r] = id;
         o.wts[r] = w;
         if (o.user_ids) o.user_ids[r] = id;
@@ -249,8 +251,9 @@ __device__ __forceinline__ void route_small_impl(const float* __restrict__ logit
       }
     }
   } else {
-    // 3. softmax denominators, a 16-lane row per token: the selected terms
-    //    (renormalised weights) or all E terms (plain softmax probabilities)
+    // 3. denominators, a 16-lane row per token: the selected terms
+    //    (renormalised weights), all E terms (plain softmax probabilities),
+    //    or none (plain sigmoid scores)
     const int l16 = lane & 15;
     for (int t0 = wave * 4; t0 < T; t0 += 16) {
       const int t = t0 + (lane >> 4);
@@ -258,14 +261,20 @@ __device__ __forceinline__ void route_small_impl(const float* __restrict__ logit
       if (t < T) {
         const float* lt = s_l + t * E;
         const float lmax = lt[s_rid[t * k]];
-        for (int e = l16; e < E; e += 16)
-          if (!normalize || s_sel[t * E + e] >= 0) sum += __expf(lt[e] - lmax);
+        for (int e = l16; e < E; e += 16) {
+          const bool sel = s_sel[t * E + e] >= 0;
+          if (rm.sigmoid) {
+            if (sel) sum += sigmoid_f(lt[e]);
+          } else if (!rm.normalize || sel) {
+            sum += __expf(lt[e] - lmax);
+          }
+        }
       }
       sum += dpp_f<kDppXor1>(sum);
       sum += dpp_f<kDppXor2>(sum);
       sum += dpp_f<kDppHalfMirror>(sum);
       sum += dpp_f<kDppMirror>(sum);
-      if (t < T && l16 == 0) s_den[t] = sum;
+      if (t < T && l16 == 0) s_den[t] = (rm.sigmoid && !rm.normalize) ? 1.f : sum;
     }
     __syncthreads();
     // 4. ids and weights, one thread per route
@@ -273,7 +282,8 @@ __device__ __forceinline__ void route_small_impl(const float* __restrict__ logit
       const int t = r / k;
       const float* lt = s_l + t * E;
       const int id = s_rid[r];
-      const float w = __expf(lt[id] - lt[s_rid[t * k]]) / s_den[t];
+      const float sc = rm.sigmoid ? sigmoid_f(lt[id]) : __expf(lt[id] - lt[s_rid[t * k]]);
+      const float w = sc / s_den[t] * rm.scale;
       o.ids[r] = id;
       o.wts[r] = w;
       if (o.user_ids) o.user_ids[r] = id;
@@ -324,11 +334,11 @@ __device__ __forceinline__ void route_small_impl(const float* __restrict__ logit
 }
 
 __device__ void route_small_body(const float* __restrict__ logits, int T, int E, int k,
-                                 int ncols, int normalize, int has_shared,
+                                 int ncols, RouteMode rm, int has_shared,
                                  const SmallRouteOut& o) {
   __shared__ RouteLds L;
-  if (T <= 4) route_small_impl<4>(logits, T, E, k, ncols, normalize, has_shared, o, L);
-  else route_small_impl<kSmallMaxTokens>(logits, T, E, k, ncols, normalize, has_shared, o, L);
+  if (T <= 4) route_small_impl<4>(logits, T, E, k, ncols, rm, has_shared, o, L);
+  else route_small_impl<kSmallMaxTokens>(logits, T, E, k, ncols, rm, has_shared, o, L);
 }
 
 // Router logits fused with the routing: workgroup e computes router row e
@@ -346,7 +356,7 @@ __global__ __launch_bounds__(256) void k_router_route(const XT* __restrict__ x,
                                                       const float* __restrict__ bias,
                                                       const void* __restrict__ shared_gate_inp,
                                                       float* __restrict__ logits, int T, int H,
-                                                      int E, int k, int ncols, int normalize,
+                                                      int E, int k, int ncols, RouteMode rm,
                                                       int has_shared, int* __restrict__ ticket,
                                                       SmallRouteOut o) {
   router_row<XT, RDT, true, NC>(x, router, bias, shared_gate_inp, logits, T, H, E, ncols,
@@ -361,7 +371,7 @@ __global__ __launch_bounds__(256) void k_router_route(const XT* __restrict__ x,
   if (!s_last) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   if (threadIdx.x == 0) __hip_atomic_store(ticket, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  route_small_body(logits, T, E, k, ncols, normalize, has_shared, o);
+  route_small_body(logits, T, E, k, ncols, rm, has_shared, o);
 }
 
 // Routing data read back from the workspace, clamped to the layer's ranges,

@@ -3,6 +3,7 @@
 // caller's stream.  The library allocates no device memory.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -62,6 +63,10 @@ struct Plan {
   size_t total = 0;
 };
 
+RouteMode route_mode(const moe_desc* d) {
+  return RouteMode{d->normalize_topk, d->gating == MOE_GATING_SIGMOID ? 1 : 0, d->routed_scale};
+}
+
 int epc_of(int wf) { return wf == MOE_WEIGHTS_F32 ? 4 : (wf == MOE_WEIGHTS_BF16 ? 8 : 32); }
 
 moe_status check_desc(const moe_desc* d) {
@@ -84,6 +89,10 @@ moe_status check_desc(const moe_desc* d) {
     return fail(MOE_INVALID_ARGUMENT, "act_dtype/router_dtype must be MOE_F32 or MOE_BF16");
   if (d->normalize_topk != 0 && d->normalize_topk != 1)
     return fail(MOE_INVALID_ARGUMENT, "normalize_topk must be 0 or 1");
+  if (d->gating != MOE_GATING_SOFTMAX && d->gating != MOE_GATING_SIGMOID)
+    return fail(MOE_INVALID_ARGUMENT, "unknown gating %d", d->gating);
+  if (!std::isfinite(d->routed_scale))
+    return fail(MOE_INVALID_ARGUMENT, "routed_scale must be finite");
   if (d->has_shared_expert != 0 && d->has_shared_expert != 1)
     return fail(MOE_INVALID_ARGUMENT, "has_shared_expert must be 0 or 1");
   if (d->has_shared_expert && d->shared_intermediate <= 0)
@@ -285,7 +294,8 @@ moe_status run_route_small(const moe_desc* d, const Plan& p, const void* x, cons
   float* logits = wsp<float>(ws, p.o_logits);
   int* ticket = wsp<int>(ws, p.o_sync);
   const bool xb = d->act_dtype == MOE_BF16, rb = d->router_dtype == MOE_BF16;
-  const int sh = p.shared ? 1 : 0, nz = d->normalize_topk;
+  const int sh = p.shared ? 1 : 0;
+  const RouteMode rm = route_mode(d);
   dim3 grid(p.ncols);
   const int nc = router_nc(p.H / (rb ? 8 : 4));
   return launch("router_route", s, [&] {
@@ -293,7 +303,7 @@ moe_status run_route_small(const moe_desc* d, const Plan& p, const void* x, cons
       using XT = decltype(xtag);
       constexpr int RDT = decltype(rtag)::value, NC = decltype(nctag)::value;
       k_router_route<XT, RDT, NC><<<grid, 256, 0, s>>>(static_cast<const XT*>(x), w->router,
-          w->router_bias, w->shared_gate_inp, logits, T, p.H, p.E, p.k, p.ncols, nz, sh, ticket, o);
+          w->router_bias, w->shared_gate_inp, logits, T, p.H, p.E, p.k, p.ncols, rm, sh, ticket, o);
     };
     dispatch_router(xb, rb, nc, go);
   });
@@ -305,7 +315,7 @@ moe_status run_route_and_group(const moe_desc* d, const Plan& p, void* ws, int32
   const int T = (int)p.T, R = (int)p.R;
   MOE_TRY(launch("topk", s, [&] {
     k_topk<<<(T + 3) / 4, 256, 0, s>>>(wsp<float>(ws, p.o_logits), T, p.E, p.k, p.ncols,
-                                       d->normalize_topk, p.shared ? 1 : 0, wsp<int32_t>(ws, p.o_ids),
+                                       route_mode(d), p.shared ? 1 : 0, wsp<int32_t>(ws, p.o_ids),
                                        wsp<float>(ws, p.o_wts), user_ids, user_w,
                                        wsp<float>(ws, p.o_sgate));
   }));

@@ -102,17 +102,30 @@ __global__ __launch_bounds__(256) void k_router_gemv(
                                  blockIdx.x);
 }
 
+// How the selected experts' weights follow from their logits:
+//   softmax gating: p = softmax(l) over all E experts;
+//   sigmoid gating: p_e = sigmoid(l_e), each expert on its own;
+//   normalize:      w_j = p_j / (sum of the k selected p), else w_j = p_j;
+//   scale:          every w_j is multiplied by it.
+struct RouteMode {
+  int normalize;
+  int sigmoid;
+  float scale;
+};
+
 // --------------------------------------------------------------------------
-// Softmax -> top-k -> renormalise, one wave per token.
+// Softmax (or sigmoid) -> top-k -> renormalise, one wave per token.
 // Selection is on the logits: softmax is monotone, so the k most probable
 // experts are the k largest logits, with the lower index first on a tie.
 // The renormalised weights are exp(l_j - l_max) / sum over the selected
 // exp(l - l_max), which equals p_j / sum(p_selected).  Without
-// renormalisation the denominator runs over all E experts.
+// renormalisation the denominator runs over all E experts.  Sigmoid scores
+// are increasing in the logit too, so selection is the same; their weights
+// are sigmoid(l_j) over the selected sum, or sigmoid(l_j) alone.
 // --------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_topk(
     const float* __restrict__ logits, int T, int E, int k, int ncols,
-    int normalize, int has_shared, int32_t* __restrict__ ids,
+    RouteMode rm, int has_shared, int32_t* __restrict__ ids,
     float* __restrict__ wts, int32_t* __restrict__ user_ids,
     float* __restrict__ user_w, float* __restrict__ sgate) {
   const int lane = threadIdx.x & 63;
@@ -141,10 +154,12 @@ __global__ __launch_bounds__(256) void k_topk(
     if (lane == j) { my_id = bi; my_val = bv; }
   }
   const float lmax = __shfl(my_val, 0, 64);
-  float ex = (lane < k) ? __expf(my_val - lmax) : 0.f;
+  const float ex = (lane < k) ? (rm.sigmoid ? sigmoid_f(my_val) : __expf(my_val - lmax)) : 0.f;
   float denom;
-  if (normalize) {
+  if (rm.normalize) {
     denom = wave_sum(ex);
+  } else if (rm.sigmoid) {
+    denom = 1.f;
   } else {
     float s = 0.f;
 #pragma unroll
@@ -153,7 +168,7 @@ __global__ __launch_bounds__(256) void k_topk(
     denom = wave_sum(s);
   }
   if (lane < k) {
-    const float w = ex / denom;
+    const float w = ex / denom * rm.scale;
     ids[(size_t)t * k + lane] = my_id;
     wts[(size_t)t * k + lane] = w;
     if (user_ids) user_ids[(size_t)t * k + lane] = my_id;

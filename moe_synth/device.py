@@ -48,11 +48,12 @@ def to_device(inp: MoeInputs, device) -> MoeInputs:
     return out
 
 
-def desc_kwargs(cfg, normalize_topk=True):
+def desc_kwargs(cfg, normalize_topk=True, gating=0, routed_scale=1.0):
     return dict(hidden=cfg.H, intermediate=cfg.I, num_experts=cfg.E, top_k=cfg.k,
                 activation=cfg.act, weight_format=cfg.weight_format, act_dtype=cfg.act_dtype,
                 router_dtype=cfg.router_dtype, normalize_topk=normalize_topk,
-                shared_intermediate=cfg.Is if cfg.shared else 0, group_size=cfg.group_size)
+                shared_intermediate=cfg.Is if cfg.shared else 0, group_size=cfg.group_size,
+                gating=gating, routed_scale=routed_scale)
 
 
 def weights_kwargs(dev: MoeInputs):

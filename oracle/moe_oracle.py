@@ -11,9 +11,10 @@ order"):
 
 1. router logits  l = x . Wr^T  (+ per-expert bias, as ferrox-models
    decoder.rs adds in gpt_oss_ffn before selection)
-2. softmax over all experts, top-k by probability (stable sort, so the
-   lower expert index wins a tie), renormalise the k selected
-   probabilities to sum to one (hf2q softmax_topk_renorm_cpu)
+2. softmax over all experts (or a sigmoid per expert), top-k by score
+   (stable sort, so the lower expert index wins a tie), renormalise the k
+   selected scores to sum to one (hf2q softmax_topk_renorm_cpu), times a
+   weight scale
 3. for each selected expert e: g = Wg[e] x, u = Wu[e] x,
    h = act(g) * u, y = Wd[e] h; out += w * y, in slot order
 4. shared expert (when present): s = sigmoid(x . w_sg),
@@ -142,23 +143,46 @@ def topk_stable_desc(p, k: int) -> np.ndarray:
     return np.array(order[:k], dtype=np.int64)
 
 
-def route(logits, k: int, normalize: bool = True):
-    """Softmax -> top-k -> renormalise, per token.
+GATING_SOFTMAX = 0
+GATING_SIGMOID = 1
+
+
+def gating_scores(l, gating: int = GATING_SOFTMAX) -> np.ndarray:
+    """Routing scores of one token's logits.
+
+    Softmax over all experts (hf2q softmax_topk_renorm_cpu), or one sigmoid
+    per expert, the other gating function ferrox-models decoder.rs routes
+    with (its dense-layer note: sigmoid scores, then renormalisation
+    divides the selected score by the selected sum).
+    """
+    if gating == GATING_SOFTMAX:
+        return softmax_row(l)
+    if gating == GATING_SIGMOID:
+        return sigmoid(l)
+    raise ValueError(f"unknown gating {gating}")
+
+
+def route(logits, k: int, normalize: bool = True, gating: int = GATING_SOFTMAX,
+          scale: float = 1.0):
+    """Scores -> top-k -> renormalise -> scale, per token.
 
     Returns (ids [T, k] int64, weights [T, k] float64); slot j holds the
-    j-th largest probability.  Without ``normalize`` the raw softmax
-    probabilities of the winners are returned.
+    j-th largest score.  Without ``normalize`` the raw scores of the winners
+    are returned.  Every weight is then multiplied by ``scale`` (llama.cpp's
+    w_scale, which ferrox-models names in gpt_oss_ffn; the pages give only
+    the name and the value 1, so a plain factor on the weights is the
+    reading taken).
     """
     logits = np.atleast_2d(np.asarray(logits, dtype=np.float64))
     T = logits.shape[0]
     ids = np.zeros((T, k), dtype=np.int64)
     w = np.zeros((T, k), dtype=np.float64)
     for t in range(T):
-        p = softmax_row(logits[t])
+        p = gating_scores(logits[t], gating)
         sel = topk_stable_desc(p, k)
         ids[t] = sel
         ps = p[sel]
-        w[t] = ps / ps.sum() if normalize else ps
+        w[t] = (ps / ps.sum() if normalize else ps) * scale
     return ids, w
 
 
@@ -263,7 +287,8 @@ def shared_expert(xt, w_sg, Wsg, Wsu, Wsd):
     return s * (Wsd @ (silu(Wsg @ xt) * (Wsu @ xt))), s
 
 
-def moe_ffn(inputs, tokens=None, normalize: bool = True, src: WeightSource = None):
+def moe_ffn(inputs, tokens=None, normalize: bool = True, src: WeightSource = None,
+            gating: int = GATING_SOFTMAX, scale: float = 1.0):
     """The whole layer for the given token ids (all tokens by default).
 
     Returns dict with out [n, H] float64, ids [n, k], w [n, k] float64,
@@ -274,7 +299,7 @@ def moe_ffn(inputs, tokens=None, normalize: bool = True, src: WeightSource = Non
     toks = list(range(cfg.T)) if tokens is None else list(tokens)
     X = np.stack([src.x_row(t) for t in toks]) if toks else np.zeros((0, cfg.H))
     logits = router_logits(X, src.router(), src.router_bias())
-    ids, w = route(logits, cfg.k, normalize)
+    ids, w = route(logits, cfg.k, normalize, gating, scale)
     out = np.zeros((len(toks), cfg.H), dtype=np.float64)
     sgate = np.zeros(len(toks), dtype=np.float64)
     for n in range(len(toks)):

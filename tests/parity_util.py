@@ -29,15 +29,18 @@ def rel_err(gpu, ref):
 class Case:
     """Device inputs + descriptor + weights for one configuration."""
 
-    def __init__(self, cfg, device="cuda", normalize=True):
+    def __init__(self, cfg, device="cuda", normalize=True, gating=0, scale=1.0):
         import torch
         self.cfg = cfg
         self.normalize = normalize
+        self.gating = gating
+        self.scale = scale
         log(f"[case] generate {cfg.name} T={cfg.T} H={cfg.H} I={cfg.I} E={cfg.E} k={cfg.k}")
         self.dev = generate(cfg, backend="torch", device=device)
         self.redraws = enforce_margin(self.dev)
         torch.cuda.synchronize()
-        self.desc = M.make_desc(**desc_kwargs(cfg, normalize_topk=normalize))
+        self.desc = M.make_desc(**desc_kwargs(cfg, normalize_topk=normalize, gating=gating,
+                                              routed_scale=scale))
         self.weights = M.make_weights(**weights_kwargs(self.dev))
         self.host = host_views(self.dev)
 
@@ -62,12 +65,13 @@ class Case:
         cfg = self.cfg
         X = O.decode_matrix(self.host.x[:], cfg.act_dtype == DT_BF16)
         L = O.router_logits(X, src.router(), src.router_bias())
-        ids, w = O.route(L, cfg.k, self.normalize)
+        ids, w = O.route(L, cfg.k, self.normalize, self.gating, self.scale)
         return ids, w
 
     def oracle_outputs(self, tokens, cache=True):
         src = O.WeightSource(self.host, cache=cache)
-        r = O.moe_ffn(self.host, tokens=tokens, normalize=self.normalize, src=src)
+        r = O.moe_ffn(self.host, tokens=tokens, normalize=self.normalize, src=src,
+                      gating=self.gating, scale=self.scale)
         return r["out"]
 
 

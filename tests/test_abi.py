@@ -35,7 +35,7 @@ def test_header_declares_the_bound_functions():
 def test_library_exports_every_declared_symbol(lib):
     for name in _declared_functions():
         assert hasattr(lib, name), name
-    assert lib.moe_abi_version() == 2
+    assert lib.moe_abi_version() == 3
 
 
 def _desc(name="decode_geglu_t1", **over):
@@ -58,7 +58,8 @@ def test_workspace_size_grows_affinely(lib):
 @pytest.mark.parametrize("field,value", [
     ("hidden", 0), ("intermediate", -32), ("num_experts", 0), ("num_experts", 257),
     ("top_k", 0), ("top_k", 129), ("activation", 5), ("weight_format", 7), ("act_dtype", 3),
-    ("normalize_topk", 2)])
+    ("normalize_topk", 2), ("gating", 2), ("gating", -1), ("routed_scale", float("inf")),
+    ("routed_scale", float("nan"))])
 def test_bad_descriptor_is_invalid_argument(lib, field, value):
     d = _desc()
     setattr(d, field, value)          # raw field: bypass make_desc's coercions

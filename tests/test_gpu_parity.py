@@ -108,6 +108,36 @@ def test_unnormalised_routing_parity():
     check_case(Case(cfg2, normalize=False))
 
 
+# sigmoid gating and a routing-weight scale on every routing kernel: the
+# decode router (wave per token at T <= 4, rows or ranks above), the prefill
+# top-k kernel, and the 4-bit decode path; both with and without
+# renormalisation
+ROUTING_VARIANTS = [
+    (MoeConfig(name="sig_decode_t3", T=3, H=128, I=64, E=16, k=4, seed_index=38),
+     dict(gating=1, normalize=True, scale=2.5)),
+    (MoeConfig(name="sig_decode_t20_raw", T=20, H=128, I=64, E=64, k=6, weight_format=WF_BF16,
+               router_dtype=DT_BF16, seed_index=39), dict(gating=1, normalize=False, scale=0.5)),
+    (MoeConfig(name="sig_decode_t1_bf16", T=1, H=1024, I=320, E=32, k=8, weight_format=WF_BF16,
+               router_dtype=DT_BF16, shared=True, Is=128, seed_index=40),
+     dict(gating=1, normalize=True, scale=1.0)),
+    (MoeConfig(name="sig_prefill_shared", T=200, H=128, I=64, E=16, k=4, weight_format=WF_BF16,
+               act_dtype=DT_BF16, router_dtype=DT_BF16, shared=True, Is=64, seed_index=41),
+     dict(gating=1, normalize=True, scale=1.75)),
+    (MoeConfig(name="sig_prefill_raw", T=150, H=128, I=96, E=8, k=3, weight_format=WF_BF16,
+               act_dtype=DT_BF16, router_dtype=DT_BF16, seed_index=42),
+     dict(gating=1, normalize=False, scale=1.0)),
+    (MoeConfig(name="softmax_scaled_u4", T=6, H=256, I=128, E=16, k=4, weight_format=WF_U4,
+               seed_index=43), dict(gating=0, normalize=True, scale=2.0)),
+    (MoeConfig(name="sig_u4_raw", T=2, H=256, I=64, E=8, k=2, weight_format=WF_U4,
+               seed_index=44), dict(gating=1, normalize=False, scale=3.0)),
+]
+
+
+@pytest.mark.parametrize("cfg,opts", ROUTING_VARIANTS, ids=[c.name for c, _ in ROUTING_VARIANTS])
+def test_routing_variant_parity(cfg, opts):
+    check_case(Case(cfg, **opts))
+
+
 def test_repeat_runs_bit_identical():
     case = Case(SMALL[0])
     a = case.forward()

@@ -128,6 +128,64 @@ def test_route_shift_invariance():
     np.testing.assert_allclose(w0, w1, rtol=1e-13)
 
 
+# ----------------------------------------------- sigmoid gating, weight scale
+def test_sigmoid_gating_selects_like_softmax():
+    # both scores increase with the logit: same experts, same slot order,
+    # ties (equal logits) still to the lower index
+    rng = np.random.default_rng(41)
+    for _ in range(200):
+        E = int(rng.integers(2, 12))
+        k = int(rng.integers(1, E + 1))
+        l = rng.integers(-3, 4, size=E).astype(np.float64) * 0.5
+        a, _ = O.route(l[None, :], k)
+        b, _ = O.route(l[None, :], k, gating=O.GATING_SIGMOID)
+        assert (a == b).all()
+
+
+def test_one_expert_weight_is_one_under_either_gating():
+    # the dense-layer note: softmax of one logit is 1, and sigmoid followed
+    # by renormalisation divides the selected score by itself
+    for g in (O.GATING_SOFTMAX, O.GATING_SIGMOID):
+        for l in (-40.0, -1.5, 0.0, 2.25, 30.0):
+            ids, w = O.route(np.array([[l]]), 1, gating=g)
+            assert ids[0, 0] == 0 and w[0, 0] == 1.0
+
+
+def test_sigmoid_gating_worked_values():
+    # logits (ln 3, 0, -ln 3): sigmoid scores 3/4, 1/2, 1/4
+    l = np.array([[math.log(3.0), 0.0, -math.log(3.0)]])
+    ids, w = O.route(l, 2, gating=O.GATING_SIGMOID)
+    assert ids[0].tolist() == [0, 1]
+    np.testing.assert_allclose(w[0], [0.6, 0.4], rtol=1e-15)          # 0.75/1.25, 0.5/1.25
+    ids, w = O.route(l, 2, normalize=False, gating=O.GATING_SIGMOID)
+    np.testing.assert_allclose(w[0], [0.75, 0.5], rtol=1e-15)
+    ids, w = O.route(l, 2)                                             # softmax: 3:1 of e^l
+    np.testing.assert_allclose(w[0], [0.75, 0.25], rtol=1e-15)
+
+
+def test_sigmoid_unnormalised_is_library_expit():
+    rng = np.random.default_rng(42)
+    L = rng.normal(size=(16, 40)) * 2
+    ids, w = O.route(L, 6, normalize=False, gating=O.GATING_SIGMOID)
+    for t in range(16):
+        np.testing.assert_allclose(w[t], scipy.special.expit(L[t, ids[t]]), rtol=1e-14)
+    ids, w = O.route(L, 6, gating=O.GATING_SIGMOID)
+    np.testing.assert_allclose(w.sum(axis=1), 1.0, rtol=0, atol=1e-14)
+    # unlike softmax, sigmoid weights move when every logit shifts by a constant
+    _, w2 = O.route(L + 1.0, 6, gating=O.GATING_SIGMOID)
+    assert np.abs(w2 - w).max() > 1e-3
+
+
+def test_weight_scale_multiplies_the_routed_sum_only():
+    for g in (O.GATING_SOFTMAX, O.GATING_SIGMOID):
+        base = O.moe_ffn(_tiny_inputs(seed=43, shared=True, T=4), gating=g)
+        sc = O.moe_ffn(_tiny_inputs(seed=43, shared=True, T=4), gating=g, scale=2.5)
+        np.testing.assert_allclose(sc["w"], 2.5 * base["w"], rtol=1e-15)
+        routed = O.moe_ffn(_tiny_inputs(seed=43, shared=False, T=4), gating=g)["out"]
+        # the shared expert's contribution is untouched by the scale
+        np.testing.assert_allclose(sc["out"] - base["out"], 1.5 * routed, rtol=1e-10, atol=1e-13)
+
+
 def test_router_logits_transpose_and_bias():
     # l[t, e] = x_t . Wr[e]: a rectangular check that catches a transposed Wr
     x = np.array([[1.0, 2.0, 3.0]])
