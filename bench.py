@@ -53,6 +53,9 @@ def parse():
     ap.add_argument("--gating", choices=["softmax", "sigmoid"], default="softmax",
                     help="routing scores (the workloads are quoted with softmax)")
     ap.add_argument("--routed-scale", type=float, default=1.0)
+    ap.add_argument("--pre-norm", type=float, default=None, metavar="EPS",
+                    help="run the layer on RMSNorm(x) with this epsilon")
+    ap.add_argument("--residual", action="store_true", help="add a residual to out")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="first run one plain device copy of this many MiB (a kernel of known "
                          "traffic, to scale hardware byte counters)")
@@ -91,8 +94,17 @@ def main():
         del src, dst
     inp = generate(cfg, backend="torch", device=dev)
     gating = {"softmax": M.GATING_SOFTMAX, "sigmoid": M.GATING_SIGMOID}[args.gating]
-    desc = M.make_desc(**desc_kwargs(cfg, gating=gating, routed_scale=args.routed_scale))
-    w = M.make_weights(**weights_kwargs(inp))
+    desc = M.make_desc(**desc_kwargs(cfg, gating=gating, routed_scale=args.routed_scale),
+                       norm_eps=args.pre_norm)
+    wkw = weights_kwargs(inp)
+    if args.pre_norm is not None:
+        from moe_synth import norm_weight_values
+        wkw["norm_weight"] = torch.from_numpy(norm_weight_values(cfg)).to(dev)
+    w = M.make_weights(**wkw)
+    res = None
+    if args.residual:
+        from moe_synth import residual_values
+        res = torch.from_numpy(residual_values(cfg)).to(dev)
     T = cfg.T
     decode = T <= 32
     P = args.pool if decode else 1
@@ -105,7 +117,7 @@ def main():
     stream = torch.cuda.current_stream()
 
     def step(i):
-        M.moe_ffn_forward(desc, xs[i % P], w, out=out, workspace=ws)
+        M.moe_ffn_forward(desc, xs[i % P], w, out=out, workspace=ws, residual=res)
 
     # realized expert load of pool[0] (for the algorithmic byte / flop counts)
     r = M.moe_route(desc, xs[0], w, workspace=ws)
@@ -203,7 +215,12 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(cfg, inp, xs, args.cpu_seconds, gating, args.routed_scale)
+        pn = None
+        if args.pre_norm is not None:
+            from moe_synth import norm_weight_values
+            pn = (norm_weight_values(cfg), args.pre_norm)
+        cpu = cpu_baseline(cfg, inp, xs, args.cpu_seconds, gating, args.routed_scale, pn,
+                           None if res is None else res.cpu().numpy())
 
     line = {
         "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -217,6 +234,7 @@ def main():
                    "activations": ["f32", "bf16"][cfg.act_dtype],
                    "shared_expert": cfg.Is if cfg.shared else 0,
                    "gating": args.gating, "routed_scale": args.routed_scale,
+                   "pre_norm_eps": args.pre_norm, "residual": args.residual,
                    "touched_experts": touched, "token_pool": P,
                    "launch": "eager" if graph is None else f"hipgraph x{P} steps",
                    "parallelism": "single-gpu"},
@@ -245,7 +263,7 @@ def _host_copy(inp):
     return hv
 
 
-def cpu_baseline(cfg, inp, xs, seconds, gating=0, scale=1.0):
+def cpu_baseline(cfg, inp, xs, seconds, gating=0, scale=1.0, pre_norm=None, residual=None):
     """The float64 CPU oracle, as it stands, on a bounded sample of tokens."""
     from threadpoolctl import threadpool_info
     from moe_synth.device import HostView
@@ -263,7 +281,8 @@ def cpu_baseline(cfg, inp, xs, seconds, gating=0, scale=1.0):
         for tok in range(cfg.T):
             src = WeightSource(host, cache=False)
             t0 = time.perf_counter()
-            moe_ffn(host, tokens=[tok], src=src, gating=gating, scale=scale)
+            moe_ffn(host, tokens=[tok], src=src, gating=gating, scale=scale, pre_norm=pre_norm,
+                    residual=residual)
             t_total += time.perf_counter() - t0
             n_done += 1
             if t_total >= seconds:

@@ -21,6 +21,10 @@
  *                                   * shared_down(silu(shared_gate x) *
  *                                                 (shared_up x))
  *
+ * Two optional ends (moe_desc.pre_norm, the residual of moe_ffn_forward):
+ * x may first be replaced by RMSNorm(x) * norm_weight, and a residual may
+ * be added to out.
+ *
  * Layouts are row-major with the last index contiguous; weight matrices are
  * [out, in] (y = W x), the stacked-expert layout of hf2q's
  * MoeFfnWeightsGpu and of ferrum-kernels' validate_participant bindings.
@@ -60,7 +64,7 @@
 extern "C" {
 #endif
 
-#define MOE_FFN_ABI_VERSION 3
+#define MOE_FFN_ABI_VERSION 4
 
 /* Leading workspace bytes that must be zero before a workspace's first use. */
 #define MOE_WORKSPACE_ZERO_BYTES 256
@@ -125,6 +129,12 @@ typedef struct moe_desc {
   float routed_scale;          /* every routing weight is multiplied by it
                                   (llama.cpp's w_scale, which ferrox-models
                                   names in gpt_oss_ffn); finite, 1 for none */
+  int32_t pre_norm;            /* 1: the layer runs on RMSNorm(x) (the
+                                  pre-FFN norm of ferrox-models' decoder
+                                  step), x[t] / sqrt(mean(x[t]^2) + norm_eps)
+                                  * norm_weight, rounded to act_dtype;
+                                  0: on x as given                          */
+  float norm_eps;              /* > 0 when pre_norm, else ignored            */
 } moe_desc;
 
 typedef struct moe_u4_matrix {
@@ -147,6 +157,7 @@ typedef struct moe_weights {
   const void* shared_gate;     /* [Is, H], f32/bf16                          */
   const void* shared_up;       /* [Is, H]                                    */
   const void* shared_down;     /* [H, Is]                                    */
+  const float* norm_weight;    /* [H] f32 (pre_norm only)                    */
 } moe_weights;
 
 /* ABI version (MOE_FFN_ABI_VERSION of the built library). */
@@ -197,6 +208,10 @@ moe_status moe_route(const moe_desc* desc, int64_t num_tokens, const void* x,
  *   x            [T, H] act_dtype
  *   out          [T, H] f32 out (the f32 accumulator/output convention of
  *                mlx-native's moe_weighted_sum_seq)
+ *   residual     [T, H] f32 or NULL: when given, out = layer(x) + residual,
+ *                added in the kernel that writes out (hf2q folds the
+ *                residual into its final weighted reduce the same way).
+ *                It may be `out` itself (out += layer(x)).
  *   topk_ids_out [T, k] int32 out or NULL (as in moe_route)
  *   topk_w_out   [T, k] f32 out or NULL
  *   ws, ws_bytes workspace, at least moe_workspace_size(desc, T) bytes
@@ -205,9 +220,9 @@ moe_status moe_route(const moe_desc* desc, int64_t num_tokens, const void* x,
  */
 moe_status moe_ffn_forward(const moe_desc* desc, int64_t num_tokens,
                            const void* x, const moe_weights* weights,
-                           float* out, int32_t* topk_ids_out,
-                           float* topk_w_out, void* ws, size_t ws_bytes,
-                           void* stream);
+                           float* out, const float* residual,
+                           int32_t* topk_ids_out, float* topk_w_out,
+                           void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Kernel timing, for measurement.  While enabled, every kernel the library

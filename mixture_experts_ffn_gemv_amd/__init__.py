@@ -48,7 +48,9 @@ class Desc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "hidden", "intermediate", "num_experts", "top_k", "activation", "weight_format",
         "act_dtype", "router_dtype", "normalize_topk", "has_shared_expert",
-        "shared_intermediate", "group_size", "gating")] + [("routed_scale", ctypes.c_float)]
+        "shared_intermediate", "group_size", "gating")] + [
+        ("routed_scale", ctypes.c_float), ("pre_norm", ctypes.c_int32),
+        ("norm_eps", ctypes.c_float)]
 
 
 class U4Matrix(ctypes.Structure):
@@ -60,7 +62,8 @@ class Weights(ctypes.Structure):
                 ("gate", ctypes.c_void_p), ("up", ctypes.c_void_p), ("down", ctypes.c_void_p),
                 ("gate_u4", U4Matrix), ("up_u4", U4Matrix), ("down_u4", U4Matrix),
                 ("shared_gate_inp", ctypes.c_void_p), ("shared_gate", ctypes.c_void_p),
-                ("shared_up", ctypes.c_void_p), ("shared_down", ctypes.c_void_p)]
+                ("shared_up", ctypes.c_void_p), ("shared_down", ctypes.c_void_p),
+                ("norm_weight", ctypes.c_void_p)]
 
 
 _lib = None
@@ -85,7 +88,7 @@ def load(path: Optional[str] = None):
                               vp, vp, vp, ctypes.c_size_t, vp]
     lib.moe_route.restype = i32
     lib.moe_ffn_forward.argtypes = [ctypes.POINTER(Desc), i64, vp, ctypes.POINTER(Weights), vp, vp,
-                                    vp, vp, ctypes.c_size_t, vp]
+                                    vp, vp, vp, ctypes.c_size_t, vp]
     lib.moe_ffn_forward.restype = i32
     lib.moe_timing_enable.argtypes = [i32]
     lib.moe_timing_enable.restype = i32
@@ -106,10 +109,12 @@ def _check(status: int):
 def make_desc(hidden, intermediate, num_experts, top_k, activation=ACT_SILU,
               weight_format=WEIGHTS_BF16, act_dtype=DT_F32, router_dtype=DT_F32,
               normalize_topk=True, shared_intermediate=0, group_size=32,
-              gating=GATING_SOFTMAX, routed_scale=1.0) -> Desc:
+              gating=GATING_SOFTMAX, routed_scale=1.0, norm_eps=None) -> Desc:
+    """``norm_eps`` (a float) turns on the pre-FFN RMSNorm (weights need norm_weight)."""
     return Desc(hidden, intermediate, num_experts, top_k, activation, weight_format, act_dtype,
                 router_dtype, int(bool(normalize_topk)), int(shared_intermediate > 0),
-                shared_intermediate, group_size, gating, routed_scale)
+                shared_intermediate, group_size, gating, routed_scale,
+                int(norm_eps is not None), 0.0 if norm_eps is None else norm_eps)
 
 
 def _ptr(t) -> Optional[int]:
@@ -117,7 +122,8 @@ def _ptr(t) -> Optional[int]:
 
 
 def make_weights(router, gate=None, up=None, down=None, router_bias=None, shared_gate_inp=None,
-                 shared_gate=None, shared_up=None, shared_down=None, u4=None) -> Weights:
+                 shared_gate=None, shared_up=None, shared_down=None, u4=None,
+                 norm_weight=None) -> Weights:
     """Device tensors -> moe_weights.  ``u4`` = dict(gate=(codes, scales, mins), up=..., down=...)."""
     w = Weights()
     w.router, w.router_bias = _ptr(router), _ptr(router_bias)
@@ -128,6 +134,7 @@ def make_weights(router, gate=None, up=None, down=None, router_bias=None, shared
             setattr(w, name + "_u4", U4Matrix(_ptr(c), _ptr(s), _ptr(m)))
     w.shared_gate_inp, w.shared_gate = _ptr(shared_gate_inp), _ptr(shared_gate)
     w.shared_up, w.shared_down = _ptr(shared_up), _ptr(shared_down)
+    w.norm_weight = _ptr(norm_weight)
     return w
 
 
@@ -177,7 +184,8 @@ def moe_route(desc: Desc, x, weights: Weights, workspace=None, stream=None) -> R
 
 
 def moe_ffn_forward(desc: Desc, x, weights: Weights, out=None, workspace=None, stream=None,
-                    return_routing: bool = False):
+                    return_routing: bool = False, residual=None):
+    """out = layer(x) (+ residual, a float32 [T, H] tensor, which may be ``out``)."""
     import torch
     T = x.shape[0]
     dev = x.device
@@ -189,8 +197,8 @@ def moe_ffn_forward(desc: Desc, x, weights: Weights, out=None, workspace=None, s
         w = torch.empty((T, desc.top_k), dtype=torch.float32, device=dev)
     ws = workspace if workspace is not None else alloc_workspace(desc, T, dev)
     _check(load().moe_ffn_forward(ctypes.byref(desc), T, x.data_ptr(), ctypes.byref(weights),
-                                  out.data_ptr(), _ptr(ids), _ptr(w), ws.data_ptr(), ws.numel(),
-                                  _stream(stream)))
+                                  out.data_ptr(), _ptr(residual), _ptr(ids), _ptr(w),
+                                  ws.data_ptr(), ws.numel(), _stream(stream)))
     return (out, ids, w) if return_routing else out
 
 

@@ -401,6 +401,7 @@ struct Dec2Params {
   const float* wts;
   const float* sgate_val;
   float* out;    // [T, H]
+  const float* residual;  // [T, H] or null, added to out (may be out)
   float* y;      // [R, H] per-route down outputs (4-bit path)
   int T, E, k, H, I, Is, rc;
 };
@@ -699,7 +700,11 @@ __global__ __launch_bounds__(256) void k_dec_down3(Dec2Params p) {
   for (int i = tid; i < p.T * RPW; i += 256) {
     const int t = i / RPW, q = i - t * RPW;
     const int n = n0 + q;
-    if (n < p.H) p.out[(size_t)t * p.H + n] = part[0][t][q] + part[1][t][q] + part[2][t][q] + part[3][t][q];
+    if (n < p.H) {
+      float o = part[0][t][q] + part[1][t][q] + part[2][t][q] + part[3][t][q];
+      if (p.residual) o += p.residual[(size_t)t * p.H + n];
+      p.out[(size_t)t * p.H + n] = o;
+    }
   }
 }
 

@@ -239,8 +239,8 @@ __global__ __launch_bounds__(256) void k_combine(const YT* __restrict__ y,
                                                  const float* __restrict__ wts,
                                                  const int32_t* __restrict__ pos_of_route,
                                                  const float* __restrict__ sgate,
-                                                 float* __restrict__ out, int T, int H, int k,
-                                                 int has_shared) {
+                                                 float* out, const float* residual, int T,
+                                                 int H, int k, int has_shared) {
   const int cols4 = H / 4;
   const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= (size_t)T * cols4) return;
@@ -270,6 +270,10 @@ __global__ __launch_bounds__(256) void k_combine(const YT* __restrict__ y,
       a2 = fmaf(s, bf16lo(v[1]), a2); a3 = fmaf(s, bf16hi(v[1]), a3);
     }
   }
+  if (residual) {  // may be out itself: read before the store, same thread
+    const f32x4 r = *reinterpret_cast<const f32x4*>(residual + (size_t)t * H + c);
+    a0 += r[0]; a1 += r[1]; a2 += r[2]; a3 += r[3];
+  }
   f32x4 o = {a0, a1, a2, a3};
   *reinterpret_cast<f32x4*>(out + (size_t)t * H + c) = o;
 }
@@ -282,8 +286,8 @@ __global__ __launch_bounds__(256) void k_combine_bf16x8(const uint16_t* __restri
                                                         const float* __restrict__ wts,
                                                         const int32_t* __restrict__ pos_of_route,
                                                         const float* __restrict__ sgate,
-                                                        float* __restrict__ out, int T, int H,
-                                                        int k, int has_shared) {
+                                                        float* out, const float* residual,
+                                                        int T, int H, int k, int has_shared) {
   const int cols8 = H / 8;
   const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= (size_t)T * cols8) return;
@@ -316,6 +320,12 @@ __global__ __launch_bounds__(256) void k_combine_bf16x8(const uint16_t* __restri
       a[2 * q] = fmaf(s, bf16lo(v[q]), a[2 * q]);
       a[2 * q + 1] = fmaf(s, bf16hi(v[q]), a[2 * q + 1]);
     }
+  }
+  if (residual) {  // may be out itself: read before the store, same thread
+    const f32x4* r = reinterpret_cast<const f32x4*>(residual + (size_t)t * H + c);
+    const f32x4 r0 = r[0], r1 = r[1];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) { a[q] += r0[q]; a[4 + q] += r1[q]; }
   }
   f32x4* o = reinterpret_cast<f32x4*>(out + (size_t)t * H + c);
   o[0] = f32x4{a[0], a[1], a[2], a[3]};

@@ -21,6 +21,7 @@
 #include "decode.h"
 #include "decode_u4.h"
 #include "gemv.h"
+#include "norm.h"
 #include "route.h"
 
 namespace {
@@ -58,7 +59,7 @@ struct Plan {
   int bt = 128;            // grouped-GEMM route-tile height
   int max_groups = 0;      // active groups (upper bound)
   // workspace offsets
-  size_t o_sync, o_logits, o_ids, o_wts, o_sgate, o_bhist, o_boff, o_counts, o_offsets, o_active,
+  size_t o_sync, o_xn, o_logits, o_ids, o_wts, o_sgate, o_bhist, o_boff, o_counts, o_offsets, o_active,
       o_nactive, o_ntiles, o_perm, o_pos, o_rowtok, o_tgroup, o_tm0, o_h, o_hs, o_y, o_ys;
   size_t total = 0;
 };
@@ -93,6 +94,10 @@ moe_status check_desc(const moe_desc* d) {
     return fail(MOE_INVALID_ARGUMENT, "unknown gating %d", d->gating);
   if (!std::isfinite(d->routed_scale))
     return fail(MOE_INVALID_ARGUMENT, "routed_scale must be finite");
+  if (d->pre_norm != 0 && d->pre_norm != 1)
+    return fail(MOE_INVALID_ARGUMENT, "pre_norm must be 0 or 1");
+  if (d->pre_norm && !(std::isfinite(d->norm_eps) && d->norm_eps > 0.f))
+    return fail(MOE_INVALID_ARGUMENT, "norm_eps must be finite and positive");
   if (d->has_shared_expert != 0 && d->has_shared_expert != 1)
     return fail(MOE_INVALID_ARGUMENT, "has_shared_expert must be 0 or 1");
   if (d->has_shared_expert && d->shared_intermediate <= 0)
@@ -147,6 +152,7 @@ Plan make_plan(const moe_desc* d, int64_t T) {
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t r = o; o = align_up(o + bytes); return r; };
   p.o_sync = take(kSyncBytes);  // ticket counter(s), kept at zero between calls
+  p.o_xn = take(d->pre_norm ? (size_t)T * p.H * (d->act_dtype == MOE_BF16 ? 2 : 4) : 0);
   p.o_logits = take((size_t)T * p.ncols * 4);
   p.o_ids = take((size_t)p.R * 4);
   p.o_wts = take((size_t)p.R * 4);
@@ -398,7 +404,8 @@ void launch_down_rw(int rw, dim3 grid, hipStream_t s, const GemvDownParams& dp) 
 }
 
 moe_status run_experts_gemv(const moe_desc* d, const Plan& p, const void* x,
-                            const moe_weights* w, float* out, void* ws, hipStream_t s) {
+                            const moe_weights* w, float* out, const float* residual, void* ws,
+                            hipStream_t s) {
   const int wf = d->weight_format;
   const int epc = epc_of(wf);
   GroupInfo gi;
@@ -456,7 +463,7 @@ moe_status run_experts_gemv(const moe_desc* d, const Plan& p, const void* x,
   return launch("combine", s, [&] {
     k_combine<float><<<(unsigned)((nthr + 255) / 256), 256, 0, s>>>(
         dp.y, dp.ys, wsp<float>(ws, p.o_wts), wsp<int32_t>(ws, p.o_pos), wsp<float>(ws, p.o_sgate),
-        out, (int)p.T, p.H, p.k, p.shared ? 1 : 0);
+        out, residual, (int)p.T, p.H, p.k, p.shared ? 1 : 0);
   });
 }
 
@@ -521,7 +528,8 @@ moe_status launch_u4(const char* name, int u, dim3 grid, size_t lds, hipStream_t
 
 // 4-bit weights, T <= 32: gate/up and down with the routes' activations
 // staged in LDS, then the weighted combine.
-moe_status run_experts_u4(const moe_desc* d, const Plan& p, Dec2Params dp, float* out, void* ws,
+moe_status run_experts_u4(const moe_desc* d, const Plan& p, Dec2Params dp, float* out,
+                          const float* residual, void* ws,
                           hipStream_t s) {
   dp.y = wsp<float>(ws, p.o_y);
   auto rc_for = [&](int K) {
@@ -547,13 +555,14 @@ moe_status run_experts_u4(const moe_desc* d, const Plan& p, Dec2Params dp, float
   const size_t nthr = (size_t)p.T * (p.H / 4);
   return launch("combine", s, [&] {
     k_combine<float><<<(unsigned)((nthr + 255) / 256), 256, 0, s>>>(
-        dp.y, nullptr, dp.wts, wsp<int32_t>(ws, p.o_pos), dp.sgate_val, out, (int)p.T, p.H, p.k,
-        0);
+        dp.y, nullptr, dp.wts, wsp<int32_t>(ws, p.o_pos), dp.sgate_val, out, residual, (int)p.T,
+        p.H, p.k, 0);
   });
 }
 
 moe_status run_experts_small(const moe_desc* d, const Plan& p, const void* x,
-                             const moe_weights* w, float* out, void* ws, hipStream_t s) {
+                             const moe_weights* w, float* out, const float* residual, void* ws,
+                             hipStream_t s) {
   const int wf = d->weight_format;
   const int epc = epc_of(wf);
   Dec2Params dp;
@@ -575,9 +584,10 @@ moe_status run_experts_small(const moe_desc* d, const Plan& p, const void* x,
   dp.wts = wsp<float>(ws, p.o_wts);
   dp.sgate_val = wsp<float>(ws, p.o_sgate);
   dp.out = out;
+  dp.residual = residual;
   dp.T = (int)p.T; dp.E = p.E; dp.k = p.k; dp.H = p.H; dp.I = p.I; dp.Is = p.Is; dp.rc = p.rc;
 
-  if (wf == MOE_WEIGHTS_U4_G32) return run_experts_u4(d, p, dp, out, ws, s);
+  if (wf == MOE_WEIGHTS_U4_G32) return run_experts_u4(d, p, dp, out, residual, ws, s);
 
   const int u1 = pick_u(p.H / epc);
   const bool direct = p.T == 1;
@@ -608,7 +618,8 @@ moe_status run_experts_small(const moe_desc* d, const Plan& p, const void* x,
 }
 
 moe_status run_experts_mfma(const moe_desc* d, const Plan& p, const void* x,
-                            const moe_weights* w, float* out, void* ws, hipStream_t s) {
+                            const moe_weights* w, float* out, const float* residual, void* ws,
+                            hipStream_t s) {
   GemmParams g{};
   g.counts = wsp<int32_t>(ws, p.o_counts);
   g.offsets = wsp<int32_t>(ws, p.o_offsets);
@@ -656,8 +667,25 @@ moe_status run_experts_mfma(const moe_desc* d, const Plan& p, const void* x,
   return launch("combine", s, [&] {
     k_combine_bf16x8<<<(unsigned)((nthr + 255) / 256), 256, 0, s>>>(
         wsp<uint16_t>(ws, p.o_y), wsp<uint16_t>(ws, p.o_ys), wsp<float>(ws, p.o_wts),
-        wsp<int32_t>(ws, p.o_pos), wsp<float>(ws, p.o_sgate), out, (int)p.T, p.H, p.k,
+        wsp<int32_t>(ws, p.o_pos), wsp<float>(ws, p.o_sgate), out, residual, (int)p.T, p.H, p.k,
         p.shared ? 1 : 0);
+  });
+}
+
+// The layer's input: x, or its RMSNorm rows written to the workspace first.
+moe_status layer_input(const moe_desc* d, const Plan& p, const void* x, const moe_weights* w,
+                       void* ws, hipStream_t s, const void** xin) {
+  *xin = x;
+  if (!d->pre_norm) return MOE_OK;
+  void* xn = static_cast<uint8_t*>(ws) + p.o_xn;
+  *xin = xn;
+  return launch("rmsnorm", s, [&] {
+    if (d->act_dtype == MOE_BF16)
+      k_rmsnorm<uint16_t><<<(unsigned)p.T, 256, 0, s>>>(static_cast<const uint16_t*>(x),
+          w->norm_weight, d->norm_eps, p.H, static_cast<uint16_t*>(xn));
+    else
+      k_rmsnorm<float><<<(unsigned)p.T, 256, 0, s>>>(static_cast<const float*>(x),
+          w->norm_weight, d->norm_eps, p.H, static_cast<float*>(xn));
   });
 }
 
@@ -695,6 +723,9 @@ moe_status check_common(const moe_desc* d, int64_t T, const void* x, const moe_w
         return fail(MOE_UNSUPPORTED, "shared expert weights must be 16-byte aligned");
     }
   }
+  if (d->pre_norm && (!w->norm_weight || !aligned16(w->norm_weight)))
+    return fail(w->norm_weight ? MOE_UNSUPPORTED : MOE_INVALID_ARGUMENT,
+                "pre_norm needs weights->norm_weight, 16-byte aligned");
   if (!aligned16(x) || !aligned16(w->router) ||
       (d->has_shared_expert && !aligned16(w->shared_gate_inp)))
     return fail(MOE_UNSUPPORTED, "x, router and shared_gate_inp must be 16-byte aligned");
@@ -735,6 +766,7 @@ moe_status moe_route(const moe_desc* desc, int64_t num_tokens, const void* x,
   if (num_tokens == 0) return MOE_OK;
   if (!topk_ids || !topk_w) return fail(MOE_INVALID_ARGUMENT, "topk_ids/topk_w is NULL");
   hipStream_t s = static_cast<hipStream_t>(stream);
+  MOE_TRY(layer_input(desc, p, x, weights, ws, s, &x));
   if (p.small)
     return run_route_small(desc, p, x, weights, ws, topk_ids, topk_w, expert_counts,
                            expert_offsets, route_perm, s);
@@ -744,24 +776,27 @@ moe_status moe_route(const moe_desc* desc, int64_t num_tokens, const void* x,
 }
 
 moe_status moe_ffn_forward(const moe_desc* desc, int64_t num_tokens, const void* x,
-                           const moe_weights* weights, float* out, int32_t* topk_ids_out,
-                           float* topk_w_out, void* ws, size_t ws_bytes, void* stream) {
+                           const moe_weights* weights, float* out, const float* residual,
+                           int32_t* topk_ids_out, float* topk_w_out, void* ws, size_t ws_bytes,
+                           void* stream) {
   g_err.clear();
   Plan p;
   MOE_TRY(check_common(desc, num_tokens, x, weights, ws, ws_bytes, true, &p));
   if (num_tokens == 0) return MOE_OK;
   if (!out) return fail(MOE_INVALID_ARGUMENT, "out is NULL");
-  if (!aligned16(out)) return fail(MOE_UNSUPPORTED, "out must be 16-byte aligned");
+  if (!aligned16(out) || !aligned16(residual))
+    return fail(MOE_UNSUPPORTED, "out and residual must be 16-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
+  MOE_TRY(layer_input(desc, p, x, weights, ws, s, &x));
   if (p.small) {
     MOE_TRY(run_route_small(desc, p, x, weights, ws, topk_ids_out, topk_w_out, nullptr, nullptr,
                             nullptr, s));
-    return run_experts_small(desc, p, x, weights, out, ws, s);
+    return run_experts_small(desc, p, x, weights, out, residual, ws, s);
   }
   MOE_TRY(run_router(desc, p, x, weights, ws, s));
   MOE_TRY(run_route_and_group(desc, p, ws, topk_ids_out, topk_w_out, nullptr, nullptr, nullptr, s));
-  if (p.mfma) return run_experts_mfma(desc, p, x, weights, out, ws, s);
-  return run_experts_gemv(desc, p, x, weights, out, ws, s);
+  if (p.mfma) return run_experts_mfma(desc, p, x, weights, out, residual, ws, s);
+  return run_experts_gemv(desc, p, x, weights, out, residual, ws, s);
 }
 
 moe_status moe_timing_enable(int32_t enable) {

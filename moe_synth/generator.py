@@ -53,6 +53,8 @@ TID_SH_GATE_INP = 6
 TID_SH_GATE = 7
 TID_SH_UP = 8
 TID_SH_DOWN = 9
+TID_NORM = 10          # pre-FFN RMSNorm weight [H]
+TID_RESIDUAL = 11      # residual rows [T, H]
 TID_U4_CODES = 16      # + matrix index (0 gate, 1 up, 2 down)
 TID_U4_SCALES = 32     # + matrix index
 ATTEMPT_SHIFT = 20     # resampled x rows use TID_X + (attempt << 20)
@@ -270,6 +272,19 @@ class MoeInputs:
     shared_up: object = None         # [Is, H]
     shared_down: object = None       # [H, Is]
     backend: str = "numpy"
+
+
+def norm_weight_values(cfg: MoeConfig) -> np.ndarray:
+    """Pre-FFN RMSNorm weight [H] (float32), uniform in [0.5, 1.5)."""
+    key = stream_key(cfg.seed, TID_NORM)
+    u = uniform_np(key, np.arange(cfg.H, dtype=np.uint64))
+    return (0.5 + u).astype(np.float32)
+
+
+def residual_values(cfg: MoeConfig) -> np.ndarray:
+    """Residual rows [T, H] (float32), N(0, 1)."""
+    key = stream_key(cfg.seed, TID_RESIDUAL)
+    return normal_np(key, 0, cfg.T * cfg.H).astype(np.float32).reshape(cfg.T, cfg.H)
 
 
 def generate(cfg: MoeConfig, backend: str = "numpy", device=None) -> MoeInputs:

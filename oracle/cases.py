@@ -51,8 +51,12 @@ def margin_violations(logits: np.ndarray, k: int, margin: float = MARGIN):
     return bad
 
 
-def enforce_margin(inp, margin: float = MARGIN, max_attempts: int = 64):
-    """Redraw offending x rows in place; returns the number of redraws."""
+def enforce_margin(inp, margin: float = MARGIN, max_attempts: int = 64, xform=None):
+    """Redraw offending x rows in place; returns the number of redraws.
+
+    ``xform`` maps decoded x rows to the router's input when the layer
+    transforms x first (the pre-FFN RMSNorm)."""
+    xform = xform or (lambda X: X)
     cfg = inp.cfg
     xbf = cfg.act_dtype == DT_BF16
     rbf = cfg.router_dtype == DT_BF16
@@ -61,7 +65,7 @@ def enforce_margin(inp, margin: float = MARGIN, max_attempts: int = 64):
     if b is not None and inp.backend != "numpy":
         b = b.cpu().numpy()
     X = O.decode_matrix(_x_host(inp), xbf)
-    bad = margin_violations(O.router_logits(X, Wr, b), cfg.k, margin)
+    bad = margin_violations(O.router_logits(xform(X), Wr, b), cfg.k, margin)
     redraws = 0
     attempt = 1
     while bad:
@@ -81,7 +85,7 @@ def enforce_margin(inp, margin: float = MARGIN, max_attempts: int = 64):
             else:
                 Xb = O.decode_matrix(rows.cpu().numpy(), False)
         redraws += len(bad)
-        still = margin_violations(O.router_logits(Xb, Wr, b), cfg.k, margin)
+        still = margin_violations(O.router_logits(xform(Xb), Wr, b), cfg.k, margin)
         bad = [bad[i] for i in still]
         attempt += 1
     return redraws

@@ -19,7 +19,8 @@ order"):
    h = act(g) * u, y = Wd[e] h; out += w * y, in slot order
 4. shared expert (when present): s = sigmoid(x . w_sg),
    y_s = Wsd (silu(Wsg x) * Wsu x), out += s * y_s
-5. out is returned as float64 (the library writes float32)
+5. out is returned as float64 (the library writes float32), plus an
+   optional residual; the input may first go through the pre-FFN RMSNorm
 
 plus the expert-grouping permutation (a stable counting sort of the flat
 route ids by expert, as DS4Server qwen_mtplx.rs gather_sort obtains with an
@@ -122,6 +123,30 @@ def router_logits(x, Wr, bias=None) -> np.ndarray:
     if bias is not None:
         l = l + np.asarray(bias, dtype=np.float64)[None, :]
     return l
+
+
+def rms_norm(X, w, eps: float) -> np.ndarray:
+    """Pre-FFN RMSNorm of token rows: x / sqrt(mean(x^2) + eps) * w.
+
+    ferrox-models decoder.rs runs the MoE block on rms_norm(hidden,
+    norm_weight, rms_norm_eps); the pages call it without printing its
+    arithmetic, so this is the usual definition (mean over the hidden
+    dimension, eps inside the square root, weight applied last).
+    """
+    X = np.atleast_2d(np.asarray(X, dtype=np.float64))
+    ms = (X * X).mean(axis=1, keepdims=True)
+    return X / np.sqrt(ms + float(eps)) * np.asarray(w, dtype=np.float64)[None, :]
+
+
+def round_to_act(X, bf16: bool) -> np.ndarray:
+    """Values as the layer stores its normalised input: float32, then (for
+    bf16 activations) bfloat16, each by round-to-nearest-even."""
+    f = np.asarray(X, dtype=np.float64).astype(np.float32)
+    if not bf16:
+        return f.astype(np.float64)
+    u = f.view(np.uint32).astype(np.uint64)
+    r = ((u + np.uint64(0x7FFF) + ((u >> np.uint64(16)) & np.uint64(1))) >> np.uint64(16))
+    return bf16_to_f64(r.astype(np.uint16))
 
 
 def softmax_row(l) -> np.ndarray:
@@ -288,16 +313,22 @@ def shared_expert(xt, w_sg, Wsg, Wsu, Wsd):
 
 
 def moe_ffn(inputs, tokens=None, normalize: bool = True, src: WeightSource = None,
-            gating: int = GATING_SOFTMAX, scale: float = 1.0):
+            gating: int = GATING_SOFTMAX, scale: float = 1.0, pre_norm=None, residual=None):
     """The whole layer for the given token ids (all tokens by default).
 
     Returns dict with out [n, H] float64, ids [n, k], w [n, k] float64,
     logits [n, E] float64 and (when present) shared gate values [n].
+    ``pre_norm`` = (norm_weight [H], eps) runs the layer on the RMSNorm of
+    x, stored in the activation type; ``residual`` [T, H] is added to out
+    (hf2q's residual folded into the final reduce).
     """
     cfg = inputs.cfg
     src = src or WeightSource(inputs)
     toks = list(range(cfg.T)) if tokens is None else list(tokens)
     X = np.stack([src.x_row(t) for t in toks]) if toks else np.zeros((0, cfg.H))
+    if pre_norm is not None and toks:
+        nw, eps = pre_norm
+        X = round_to_act(rms_norm(X, nw, eps), cfg.act_dtype == 1)
     logits = router_logits(X, src.router(), src.router_bias())
     ids, w = route(logits, cfg.k, normalize, gating, scale)
     out = np.zeros((len(toks), cfg.H), dtype=np.float64)
@@ -311,5 +342,7 @@ def moe_ffn(inputs, tokens=None, normalize: bool = True, src: WeightSource = Non
             ys, s = shared_expert(X[n], w_sg, Wsg, Wsu, Wsd)
             out[n] += ys
             sgate[n] = s
+        if residual is not None:
+            out[n] += np.asarray(residual[toks[n]], dtype=np.float64)
     return {"out": out, "ids": ids, "w": w, "logits": logits, "shared_gate": sgate,
             "tokens": toks}

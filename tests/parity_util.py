@@ -7,7 +7,7 @@ import sys
 import numpy as np
 
 import mixture_experts_ffn_gemv_amd as M
-from moe_synth import generate, WF_F32, WF_BF16, WF_U4, DT_BF16
+from moe_synth import generate, norm_weight_values, WF_F32, WF_BF16, WF_U4, DT_BF16
 from moe_synth.device import desc_kwargs, weights_kwargs, host_views
 from oracle import moe_oracle as O
 from oracle.cases import enforce_margin
@@ -29,7 +29,7 @@ def rel_err(gpu, ref):
 class Case:
     """Device inputs + descriptor + weights for one configuration."""
 
-    def __init__(self, cfg, device="cuda", normalize=True, gating=0, scale=1.0):
+    def __init__(self, cfg, device="cuda", normalize=True, gating=0, scale=1.0, norm_eps=None):
         import torch
         self.cfg = cfg
         self.normalize = normalize
@@ -37,11 +37,20 @@ class Case:
         self.scale = scale
         log(f"[case] generate {cfg.name} T={cfg.T} H={cfg.H} I={cfg.I} E={cfg.E} k={cfg.k}")
         self.dev = generate(cfg, backend="torch", device=device)
-        self.redraws = enforce_margin(self.dev)
+        self.pre_norm = None
+        xform = None
+        wkw = weights_kwargs(self.dev)
+        if norm_eps is not None:
+            nw = norm_weight_values(cfg)
+            self.pre_norm = (nw, norm_eps)
+            self.norm_weight = torch.from_numpy(nw).to(device)
+            wkw["norm_weight"] = self.norm_weight
+            xform = lambda X: O.round_to_act(O.rms_norm(X, nw, norm_eps), cfg.act_dtype == DT_BF16)
+        self.redraws = enforce_margin(self.dev, xform=xform)
         torch.cuda.synchronize()
         self.desc = M.make_desc(**desc_kwargs(cfg, normalize_topk=normalize, gating=gating,
-                                              routed_scale=scale))
-        self.weights = M.make_weights(**weights_kwargs(self.dev))
+                                              routed_scale=scale), norm_eps=norm_eps)
+        self.weights = M.make_weights(**wkw)
         self.host = host_views(self.dev)
 
     def forward(self):
@@ -64,14 +73,17 @@ class Case:
         src = O.WeightSource(self.host, cache=False)
         cfg = self.cfg
         X = O.decode_matrix(self.host.x[:], cfg.act_dtype == DT_BF16)
+        if self.pre_norm is not None:
+            X = O.round_to_act(O.rms_norm(X, *self.pre_norm), cfg.act_dtype == DT_BF16)
         L = O.router_logits(X, src.router(), src.router_bias())
         ids, w = O.route(L, cfg.k, self.normalize, self.gating, self.scale)
         return ids, w
 
-    def oracle_outputs(self, tokens, cache=True):
+    def oracle_outputs(self, tokens, cache=True, residual=None):
         src = O.WeightSource(self.host, cache=cache)
         r = O.moe_ffn(self.host, tokens=tokens, normalize=self.normalize, src=src,
-                      gating=self.gating, scale=self.scale)
+                      gating=self.gating, scale=self.scale, pre_norm=self.pre_norm,
+                      residual=residual)
         return r["out"]
 
 

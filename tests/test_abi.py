@@ -35,7 +35,7 @@ def test_header_declares_the_bound_functions():
 def test_library_exports_every_declared_symbol(lib):
     for name in _declared_functions():
         assert hasattr(lib, name), name
-    assert lib.moe_abi_version() == 3
+    assert lib.moe_abi_version() == 4
 
 
 def _desc(name="decode_geglu_t1", **over):
@@ -59,7 +59,7 @@ def test_workspace_size_grows_affinely(lib):
     ("hidden", 0), ("intermediate", -32), ("num_experts", 0), ("num_experts", 257),
     ("top_k", 0), ("top_k", 129), ("activation", 5), ("weight_format", 7), ("act_dtype", 3),
     ("normalize_topk", 2), ("gating", 2), ("gating", -1), ("routed_scale", float("inf")),
-    ("routed_scale", float("nan"))])
+    ("routed_scale", float("nan")), ("pre_norm", 2)])
 def test_bad_descriptor_is_invalid_argument(lib, field, value):
     d = _desc()
     setattr(d, field, value)          # raw field: bypass make_desc's coercions
@@ -84,22 +84,22 @@ def test_unaligned_sizes_unsupported(lib):
 def test_forward_rejects_null_and_small_workspace_on_host(lib):
     d = _desc()
     w = M.Weights()
-    st = lib.moe_ffn_forward(ctypes.byref(d), 1, None, ctypes.byref(w), None, None, None, None, 0,
-                             None)
+    st = lib.moe_ffn_forward(ctypes.byref(d), 1, None, ctypes.byref(w), None, None, None, None, None,
+                             0, None)
     assert st == M.MOE_INVALID_ARGUMENT
     # fake, aligned "device" addresses: validation fails before anything is enqueued
     fake = 1 << 20
     w = M.make_weights(router=None)
     w.router, w.gate, w.up, w.down = fake, fake, fake, fake
-    st = lib.moe_ffn_forward(ctypes.byref(d), 1, fake, ctypes.byref(w), fake, None, None, fake, 16,
-                             None)
+    st = lib.moe_ffn_forward(ctypes.byref(d), 1, fake, ctypes.byref(w), fake, None, None, None, fake,
+                             16, None)
     assert st == M.MOE_WORKSPACE_TOO_SMALL
     assert "workspace" in lib.moe_last_error().decode()
-    st = lib.moe_ffn_forward(ctypes.byref(d), -1, fake, ctypes.byref(w), fake, None, None, fake,
-                             1 << 30, None)
+    st = lib.moe_ffn_forward(ctypes.byref(d), -1, fake, ctypes.byref(w), fake, None, None, None,
+                             fake, 1 << 30, None)
     assert st == M.MOE_INVALID_ARGUMENT
-    st = lib.moe_ffn_forward(ctypes.byref(d), 1, fake + 4, ctypes.byref(w), fake, None, None, fake,
-                             1 << 30, None)
+    st = lib.moe_ffn_forward(ctypes.byref(d), 1, fake + 4, ctypes.byref(w), fake, None, None, None,
+                             fake, 1 << 30, None)
     assert st == M.MOE_UNSUPPORTED            # misaligned x
 
 
@@ -107,7 +107,7 @@ def test_zero_tokens_is_a_noop(lib):
     d = _desc()
     w = M.Weights()
     assert lib.moe_ffn_forward(ctypes.byref(d), 0, None, ctypes.byref(w), None, None, None, None,
-                               0, None) == M.MOE_OK
+                               None, 0, None) == M.MOE_OK
 
 
 def test_u4_needs_group_32(lib):
@@ -123,3 +123,18 @@ def test_workspace_zero_bytes_matches_header():
     assert m and int(m.group(1)) == M.WORKSPACE_ZERO_BYTES
     d = M.make_desc(hidden=64, intermediate=32, num_experts=8, top_k=2)
     assert M.workspace_size(d, 1) >= M.WORKSPACE_ZERO_BYTES
+
+
+def test_pre_norm_needs_positive_eps_and_weight(lib):
+    n = ctypes.c_size_t(0)
+    for eps in (0.0, -1e-5, float("inf")):
+        d = _desc(norm_eps=eps)
+        assert lib.moe_workspace_size(ctypes.byref(d), 1, ctypes.byref(n)) == M.MOE_INVALID_ARGUMENT
+    d = _desc(norm_eps=1e-5)
+    assert lib.moe_workspace_size(ctypes.byref(d), 1, ctypes.byref(n)) == M.MOE_OK
+    fake = 1 << 20
+    w = M.make_weights(router=None)
+    w.router, w.gate, w.up, w.down = fake, fake, fake, fake     # no norm_weight
+    st = lib.moe_ffn_forward(ctypes.byref(d), 1, fake, ctypes.byref(w), fake, None, None, None,
+                             fake, 1 << 30, None)
+    assert st == M.MOE_INVALID_ARGUMENT and "norm_weight" in lib.moe_last_error().decode()

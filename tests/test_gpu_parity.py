@@ -23,7 +23,7 @@ def _gpu():
     M.load()
 
 
-from parity_util import Case, check_case, log, rel_err  # noqa: E402
+from parity_util import Case, check_case, log, rel_err, TOL as TOL_BY_WF  # noqa: E402
 
 # ----------------------------------------------------------- full workloads
 FULL_SAMPLES = {
@@ -138,6 +138,61 @@ def test_routing_variant_parity(cfg, opts):
     check_case(Case(cfg, **opts))
 
 
+# pre-FFN RMSNorm on every path: decode (wave-per-token and one-token
+# kernels), 4-bit decode, the MFMA prefill path and the GEMV fallback
+PRE_NORM = [
+    (MoeConfig(name="norm_decode_t3", T=3, H=128, I=64, E=16, k=4, seed_index=45), 1e-5),
+    (MoeConfig(name="norm_decode_t1_bf16", T=1, H=1024, I=320, E=32, k=8, weight_format=WF_BF16,
+               router_dtype=DT_BF16, shared=True, Is=128, seed_index=46), 1e-6),
+    (MoeConfig(name="norm_prefill_shared", T=300, H=256, I=128, E=16, k=4, weight_format=WF_BF16,
+               act_dtype=DT_BF16, router_dtype=DT_BF16, shared=True, Is=192, seed_index=47), 1e-5),
+    (MoeConfig(name="norm_u4_bf16x", T=9, H=512, I=64, E=8, k=3, weight_format=WF_U4,
+               act_dtype=DT_BF16, router_dtype=DT_BF16, seed_index=48), 1e-5),
+    (MoeConfig(name="norm_gemv_fallback", T=100, H=96, I=64, E=8, k=2, weight_format=WF_BF16,
+               act_dtype=DT_BF16, router_dtype=DT_BF16, seed_index=49), 1e-5),
+]
+
+
+@pytest.mark.parametrize("cfg,eps", PRE_NORM, ids=[c.name for c, _ in PRE_NORM])
+def test_pre_norm_parity(cfg, eps):
+    check_case(Case(cfg, norm_eps=eps))
+
+
+# residual folded into the kernel that writes out, on every path; also in
+# place (residual == out)
+RESIDUAL = [
+    MoeConfig(name="res_decode_t4", T=4, H=128, I=64, E=8, k=2, seed_index=50),
+    MoeConfig(name="res_decode_t1_bf16", T=1, H=1024, I=320, E=16, k=4, weight_format=WF_BF16,
+              router_dtype=DT_BF16, seed_index=51),
+    MoeConfig(name="res_u4", T=5, H=256, I=128, E=16, k=4, weight_format=WF_U4, seed_index=52),
+    MoeConfig(name="res_prefill_shared", T=300, H=256, I=128, E=16, k=4, weight_format=WF_BF16,
+              act_dtype=DT_BF16, router_dtype=DT_BF16, shared=True, Is=64, seed_index=53),
+    MoeConfig(name="res_gemv_fallback", T=100, H=96, I=64, E=8, k=2, weight_format=WF_BF16,
+              act_dtype=DT_BF16, router_dtype=DT_BF16, seed_index=54),
+]
+
+
+@pytest.mark.parametrize("cfg", RESIDUAL, ids=[c.name for c in RESIDUAL])
+def test_residual_parity(cfg):
+    import mixture_experts_ffn_gemv_amd as M
+    from moe_synth import residual_values
+    case = Case(cfg)
+    r_host = residual_values(cfg)
+    r = torch.from_numpy(r_host).cuda()
+    log(f"[gpu] residual forward {cfg.name}")
+    out = M.moe_ffn_forward(case.desc, case.dev.x, case.weights, residual=r)
+    buf = r.clone()
+    M.moe_ffn_forward(case.desc, case.dev.x, case.weights, out=buf, residual=buf)
+    torch.cuda.synchronize()
+    assert torch.equal(buf, out), "in-place residual differs"
+    toks = list(range(cfg.T))
+    ffn = case.oracle_outputs(toks)
+    got = out.cpu().numpy()
+    # the layer's part, against the layer alone, and the sum against the oracle's sum
+    assert rel_err(got - r_host, ffn) <= TOL_BY_WF[cfg.weight_format]
+    assert rel_err(got, case.oracle_outputs(toks, residual=r_host)) <= TOL_BY_WF[cfg.weight_format]
+
+
 def test_repeat_runs_bit_identical():
     case = Case(SMALL[0])
     a = case.forward()
@@ -156,18 +211,18 @@ def test_error_path_enqueues_nothing():
     bad = M.make_desc(hidden=64, intermediate=32, num_experts=8, top_k=9)
     lib = M.load()
     st = lib.moe_ffn_forward(ctypes.byref(bad), 4, case.dev.x.data_ptr(), ctypes.byref(case.weights),
-                             out.data_ptr(), None, None, ws.data_ptr(), ws.numel(),
+                             out.data_ptr(), None, None, None, ws.data_ptr(), ws.numel(),
                              torch.cuda.current_stream().cuda_stream)
     assert st == M.MOE_INVALID_ARGUMENT
     st = lib.moe_ffn_forward(ctypes.byref(case.desc), 4, case.dev.x.data_ptr(),
-                             ctypes.byref(case.weights), out.data_ptr(), None, None,
+                             ctypes.byref(case.weights), out.data_ptr(), None, None, None,
                              ws.data_ptr(), 64, torch.cuda.current_stream().cuda_stream)
     assert st == M.MOE_WORKSPACE_TOO_SMALL
     torch.cuda.synchronize()
     assert (out == 7.0).all()
     # zero tokens: nothing written either
     st = lib.moe_ffn_forward(ctypes.byref(case.desc), 0, case.dev.x.data_ptr(),
-                             ctypes.byref(case.weights), out.data_ptr(), None, None,
+                             ctypes.byref(case.weights), out.data_ptr(), None, None, None,
                              ws.data_ptr(), ws.numel(), torch.cuda.current_stream().cuda_stream)
     assert st == M.MOE_OK
     torch.cuda.synchronize()

@@ -186,6 +186,54 @@ def test_weight_scale_multiplies_the_routed_sum_only():
         np.testing.assert_allclose(sc["out"] - base["out"], 1.5 * routed, rtol=1e-10, atol=1e-13)
 
 
+# ------------------------------------------------- pre-FFN RMSNorm, residual
+def test_rms_norm_worked_value_and_library():
+    # [3, 4]: mean square 12.5, so x / sqrt(12.5) = x * sqrt(2) / 5
+    np.testing.assert_allclose(O.rms_norm([[3.0, 4.0]], [1.0, 1.0], 0.0),
+                               [[3 * math.sqrt(2) / 5, 4 * math.sqrt(2) / 5]], rtol=1e-15)
+    rng = np.random.default_rng(51)
+    X = rng.normal(size=(7, 96)) * 3
+    w = rng.uniform(0.5, 1.5, size=96)
+    ref = F.rms_norm(torch.from_numpy(X), (96,), torch.from_numpy(w), eps=1e-5).numpy()
+    np.testing.assert_allclose(O.rms_norm(X, w, 1e-5), ref, rtol=1e-13, atol=1e-15)
+    # invariant under a positive scale of the row when eps is 0
+    np.testing.assert_allclose(O.rms_norm(X * 7.5, w, 0.0), O.rms_norm(X, w, 0.0), rtol=1e-13)
+
+
+def test_round_to_act_matches_library_casts():
+    rng = np.random.default_rng(52)
+    X = rng.normal(size=(5, 64)) * 10
+    t = torch.from_numpy(X)
+    np.testing.assert_array_equal(O.round_to_act(X, False), t.float().double().numpy())
+    np.testing.assert_array_equal(O.round_to_act(X, True),
+                                  t.float().bfloat16().double().numpy())
+
+
+def test_pre_norm_layer_runs_on_normalised_rows():
+    inp = _tiny_inputs(seed=53, T=4, H=32)
+    nw = np.linspace(0.6, 1.4, 32)
+    normed = O.round_to_act(O.rms_norm(inp.x, nw, 1e-6), False)
+    direct = _tiny_inputs(seed=53, T=4, H=32)
+    direct.x = normed.astype(np.float32)      # exact: normed already holds float32 values
+    np.testing.assert_allclose(O.moe_ffn(inp, pre_norm=(nw, 1e-6))["out"],
+                               O.moe_ffn(direct)["out"], rtol=1e-13, atol=1e-15)
+    # a positive rescale of x leaves the normalised layer unchanged (up to f32 rounding)
+    big = _tiny_inputs(seed=53, T=4, H=32)
+    big.x = big.x * np.float32(16.0)          # exact power of two
+    np.testing.assert_allclose(O.moe_ffn(big, pre_norm=(nw, 0.0))["out"],
+                               O.moe_ffn(inp, pre_norm=(nw, 0.0))["out"], rtol=1e-12, atol=1e-14)
+
+
+def test_residual_is_added_to_out():
+    inp = _tiny_inputs(seed=54, T=3, shared=True)
+    r = np.random.default_rng(55).normal(size=(3, 16))
+    a = O.moe_ffn(inp)["out"]
+    b = O.moe_ffn(inp, residual=r)["out"]
+    np.testing.assert_allclose(b - a, r, rtol=0, atol=1e-14)
+    c = O.moe_ffn(inp, residual=-a)["out"]    # the residual cancels the layer
+    np.testing.assert_allclose(c, 0.0, atol=1e-14)
+
+
 def test_router_logits_transpose_and_bias():
     # l[t, e] = x_t . Wr[e]: a rectangular check that catches a transposed Wr
     x = np.array([[1.0, 2.0, 3.0]])
