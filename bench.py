@@ -56,6 +56,9 @@ def parse():
     ap.add_argument("--pre-norm", type=float, default=None, metavar="EPS",
                     help="run the layer on RMSNorm(x) with this epsilon")
     ap.add_argument("--residual", action="store_true", help="add a residual to out")
+    ap.add_argument("--op", choices=["forward", "backward"], default="forward",
+                    help="backward: the weighted-combine and gated-activation backward kernels "
+                         "at the workload's shape")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="first run one plain device copy of this many MiB (a kernel of known "
                          "traffic, to scale hardware byte counters)")
@@ -72,6 +75,8 @@ def main():
         print(f"bench.py measures one GPU only (this build has no multi-GPU path); "
               f"--gpus {args.gpus} is not supported", file=sys.stderr)
         sys.exit(2)
+    if args.op == "backward":
+        return bench_backward(args)
     import numpy as np
     import torch
 
@@ -261,6 +266,94 @@ def _host_copy(inp):
         else:
             setattr(hv, name, v[:])
     return hv
+
+
+def bench_backward(args):
+    """Both backward kernels at the workload's shape (f32 inputs resident in
+    HBM), timed together as one step; roofline of the combine backward."""
+    import torch
+    import mixture_experts_ffn_gemv_amd as M
+    from mixture_experts_ffn_gemv_amd.profiling import recorded_traffic
+    from moe_synth import CONFIGS, grad_inputs
+    cfg = CONFIGS[args.workload]
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    if args.calib_copy_mb:
+        src = torch.ones(args.calib_copy_mb << 18, device=dev)
+        torch.empty_like(src).copy_(src)
+        torch.cuda.synchronize()
+        del src
+    g = grad_inputs(cfg)
+    d = {k: torch.from_numpy(v).to(dev) for k, v in g.items()}
+    T, k, H, I = cfg.T, cfg.k, cfg.H, cfg.I
+    R = T * k
+    dy = torch.empty((T, k, H), dtype=torch.float32, device=dev)
+    dw = torch.empty((T, k), dtype=torch.float32, device=dev)
+    dgu = torch.empty((R, 2 * I), dtype=torch.float32, device=dev)
+    lib = M.load()
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def step(_=0):
+        M._check(lib.moe_weighted_sum_backward(T, k, H, d["w"].data_ptr(), d["y"].data_ptr(),
+                                               d["dout"].data_ptr(), dy.data_ptr(),
+                                               dw.data_ptr(), stream))
+        M._check(lib.moe_glu_backward(R, I, cfg.act, d["gate_up"].data_ptr(), d["dh"].data_ptr(),
+                                      dgu.data_ptr(), stream))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    M.timing_reset()
+    M.timing_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    kt = M.timing_read()
+    M.timing_enable(False)
+    kernel_ms = {n: v[1] / v[0] for n, v in kt.items()}
+    wsum_bytes = 4 * (2 * R * H + T * H + 2 * R)        # y, dy, dout, w, dw
+    glu_bytes = 4 * (2 * R * 2 * I + R * I)             # gate_up, d_gate_up, dh
+    dom = "wsum_backward"
+    achieved = wsum_bytes / (kernel_ms[dom] * 1e-3) / 1e9
+    roof = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": recorded_traffic(cfg.name, dom), "algorithmic_bytes_per_launch": wsum_bytes,
+            "avg_launch_us": round(kernel_ms[dom] * 1e3, 2),
+            "glu_backward": {"algorithmic_bytes_per_launch": glu_bytes,
+                             "avg_launch_us": round(kernel_ms["glu_backward"] * 1e3, 2),
+                             "achieved_gbs": round(glu_bytes / (kernel_ms["glu_backward"] * 1e-3)
+                                                   / 1e9, 1)}}
+    cpu = None
+    if not args.no_cpu_baseline:
+        from threadpoolctl import threadpool_info
+        from oracle import weighted_sum_backward, glu_backward
+        n, tcpu, t = 0, 0.0, 0
+        while tcpu < args.cpu_seconds:
+            t0c = time.perf_counter()
+            weighted_sum_backward(g["w"][t:t + 1], g["y"][t:t + 1], g["dout"][t:t + 1])
+            glu_backward(g["gate_up"][t * k:(t + 1) * k], g["dh"][t * k:(t + 1) * k], cfg.act)
+            tcpu += time.perf_counter() - t0c
+            n += 1
+            t = (t + 1) % T
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        cpu = {"value": round(n / tcpu, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+               "sample": f"{n} tokens of {cfg.name}: both float64 backward steps per token"}
+    ms = elapsed * 1e3 / args.steps
+    print(json.dumps({
+        "metric": "MoE FFN backward tokens/s (routing-weighted combine + gated activation)",
+        "value": round(T * args.steps / elapsed, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "op": "backward", "T": T, "H": H, "I": I, "top_k": k,
+                   "activation": ["silu", "gelu_tanh"][cfg.act], "parallelism": "single-gpu"},
+        "roofline": roof, "kernels_us": {n: round(v * 1e3, 2) for n, v in kernel_ms.items()},
+        "cpu_baseline": cpu}), flush=True)
 
 
 def cpu_baseline(cfg, inp, xs, seconds, gating=0, scale=1.0, pre_norm=None, residual=None):

@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define MOE_FFN_ABI_VERSION 4
+#define MOE_FFN_ABI_VERSION 5
 
 /* Leading workspace bytes that must be zero before a workspace's first use. */
 #define MOE_WORKSPACE_ZERO_BYTES 256
@@ -223,6 +223,43 @@ moe_status moe_ffn_forward(const moe_desc* desc, int64_t num_tokens,
                            float* out, const float* residual,
                            int32_t* topk_ids_out, float* topk_w_out,
                            void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Backward of the routing-weighted combine (mlx-native moe_dispatch.rs,
+ * moe_weighted_sum_seq and its two backward kernels).  Forward:
+ * out[t,d] = sum_j w[t,j] * y[t,j,d].  Gradients, given dout = dL/dout:
+ *
+ *   dy[t,j,d] = w[t,j] * dout[t,d]
+ *   dw[t,j]   = sum_d y[t,j,d] * dout[t,d]
+ *
+ *   w    [T, k] f32;   y [T, k, H] f32;   dout [T, H] f32
+ *   dy   [T, k, H] f32 out, or NULL to skip it
+ *   dw   [T, k] f32 out, or NULL to skip it
+ *
+ * All f32 device memory, 16-byte aligned; H a multiple of 4; k in 1..32.
+ * Outputs must not alias inputs.  T = 0 is a no-op.
+ */
+moe_status moe_weighted_sum_backward(int64_t num_tokens, int32_t top_k, int32_t hidden,
+                                     const float* w, const float* y, const float* dout,
+                                     float* dy, float* dw, void* stream);
+
+/*
+ * Backward of the gated activation h = act(g) * u (mlx-native
+ * moe_dispatch.rs, moe_swiglu_seq backward; act = SiLU or the tanh GELU of
+ * moe_activation), one fused pass:
+ *
+ *   dg = dh * u * act'(g)
+ *   du = dh * act(g)
+ *
+ *   gate_up  [R, 2I] f32: row r holds g (columns 0..I-1) then u (I..2I-1)
+ *   dh       [R, I] f32
+ *   d_gate_up[R, 2I] f32 out, the same layout (dg, then du)
+ *
+ * R = rows (routes); 16-byte aligned; I a multiple of 4.  R = 0 is a no-op.
+ */
+moe_status moe_glu_backward(int64_t rows, int32_t intermediate, int32_t activation,
+                            const float* gate_up, const float* dh, float* d_gate_up,
+                            void* stream);
 
 /*
  * Kernel timing, for measurement.  While enabled, every kernel the library

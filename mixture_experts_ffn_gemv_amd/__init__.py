@@ -34,8 +34,8 @@ GATING_SOFTMAX, GATING_SIGMOID = 0, 1
 DT_F32, DT_BF16 = 0, 1
 
 EXPORTED_SYMBOLS = ("moe_abi_version", "moe_last_error", "moe_workspace_size", "moe_route",
-                    "moe_ffn_forward", "moe_timing_enable", "moe_timing_read",
-                    "moe_timing_reset")
+                    "moe_ffn_forward", "moe_weighted_sum_backward", "moe_glu_backward",
+                    "moe_timing_enable", "moe_timing_read", "moe_timing_reset")
 
 
 class MoeError(RuntimeError):
@@ -90,6 +90,10 @@ def load(path: Optional[str] = None):
     lib.moe_ffn_forward.argtypes = [ctypes.POINTER(Desc), i64, vp, ctypes.POINTER(Weights), vp, vp,
                                     vp, vp, vp, ctypes.c_size_t, vp]
     lib.moe_ffn_forward.restype = i32
+    lib.moe_weighted_sum_backward.argtypes = [i64, i32, i32, vp, vp, vp, vp, vp, vp]
+    lib.moe_weighted_sum_backward.restype = i32
+    lib.moe_glu_backward.argtypes = [i64, i32, i32, vp, vp, vp, vp]
+    lib.moe_glu_backward.restype = i32
     lib.moe_timing_enable.argtypes = [i32]
     lib.moe_timing_enable.restype = i32
     lib.moe_timing_read.argtypes = [ctypes.c_char_p, i32, ctypes.POINTER(ctypes.c_int64),
@@ -200,6 +204,31 @@ def moe_ffn_forward(desc: Desc, x, weights: Weights, out=None, workspace=None, s
                                   out.data_ptr(), _ptr(residual), _ptr(ids), _ptr(w),
                                   ws.data_ptr(), ws.numel(), _stream(stream)))
     return (out, ids, w) if return_routing else out
+
+
+def weighted_sum_backward(w, y, dout, need_dy: bool = True, need_dw: bool = True, stream=None):
+    """Gradients of out[t] = sum_j w[t,j] y[t,j] (float32 tensors w [T,k],
+    y [T,k,H], dout [T,H]): returns (dy [T,k,H] or None, dw [T,k] or None)."""
+    import torch
+    T, k = w.shape
+    H = dout.shape[1]
+    dy = torch.empty((T, k, H), dtype=torch.float32, device=w.device) if need_dy else None
+    dw = torch.empty((T, k), dtype=torch.float32, device=w.device) if need_dw else None
+    _check(load().moe_weighted_sum_backward(T, k, H, w.data_ptr(), _ptr(y), dout.data_ptr(),
+                                            _ptr(dy), _ptr(dw), _stream(stream)))
+    return dy, dw
+
+
+def glu_backward(gate_up, dh, activation=ACT_SILU, out=None, stream=None):
+    """Gradients of h = act(g) * u for gate_up [R, 2I] (g | u) and dh [R, I]:
+    returns d_gate_up [R, 2I] (dg | du), float32."""
+    import torch
+    R, I2 = gate_up.shape
+    if out is None:
+        out = torch.empty((R, I2), dtype=torch.float32, device=gate_up.device)
+    _check(load().moe_glu_backward(R, I2 // 2, activation, gate_up.data_ptr(), dh.data_ptr(),
+                                   out.data_ptr(), _stream(stream)))
+    return out
 
 
 def timing_enable(on: bool = True):

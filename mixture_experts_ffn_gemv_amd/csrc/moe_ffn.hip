@@ -22,6 +22,7 @@
 #include "decode_u4.h"
 #include "gemv.h"
 #include "norm.h"
+#include "backward.h"
 #include "route.h"
 
 namespace {
@@ -797,6 +798,55 @@ moe_status moe_ffn_forward(const moe_desc* desc, int64_t num_tokens, const void*
   MOE_TRY(run_route_and_group(desc, p, ws, topk_ids_out, topk_w_out, nullptr, nullptr, nullptr, s));
   if (p.mfma) return run_experts_mfma(desc, p, x, weights, out, residual, ws, s);
   return run_experts_gemv(desc, p, x, weights, out, residual, ws, s);
+}
+
+moe_status moe_weighted_sum_backward(int64_t num_tokens, int32_t top_k, int32_t hidden,
+                                     const float* w, const float* y, const float* dout,
+                                     float* dy, float* dw, void* stream) {
+  g_err.clear();
+  if (num_tokens < 0) return fail(MOE_INVALID_ARGUMENT, "num_tokens is negative");
+  if (top_k < 1 || top_k > MOE_MAX_TOP_K)
+    return fail(MOE_INVALID_ARGUMENT, "top_k %d outside 1..%d", top_k, MOE_MAX_TOP_K);
+  if (hidden <= 0) return fail(MOE_INVALID_ARGUMENT, "hidden must be positive");
+  if (hidden % 4) return fail(MOE_UNSUPPORTED, "hidden must be a multiple of 4");
+  if (num_tokens * top_k > INT32_MAX)
+    return fail(MOE_UNSUPPORTED, "num_tokens * top_k too large");
+  if (num_tokens == 0 || (!dy && !dw)) return MOE_OK;
+  if (!w || !dout || (dw && !y)) return fail(MOE_INVALID_ARGUMENT, "w, y or dout is NULL");
+  if (!aligned16(y) || !aligned16(dout) || !aligned16(dy))
+    return fail(MOE_UNSUPPORTED, "y, dout and dy must be 16-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const unsigned grid = (unsigned)(num_tokens * top_k);
+  return launch("wsum_backward", s, [&] {
+    if (dy && dw) k_wsum_backward<true, true><<<grid, 256, 0, s>>>(w, y, dout, dy, dw, top_k, hidden);
+    else if (dy) k_wsum_backward<true, false><<<grid, 256, 0, s>>>(w, y, dout, dy, dw, top_k, hidden);
+    else k_wsum_backward<false, true><<<grid, 256, 0, s>>>(w, y, dout, dy, dw, top_k, hidden);
+  });
+}
+
+moe_status moe_glu_backward(int64_t rows, int32_t intermediate, int32_t activation,
+                            const float* gate_up, const float* dh, float* d_gate_up,
+                            void* stream) {
+  g_err.clear();
+  if (rows < 0) return fail(MOE_INVALID_ARGUMENT, "rows is negative");
+  if (intermediate <= 0) return fail(MOE_INVALID_ARGUMENT, "intermediate must be positive");
+  if (intermediate % 4) return fail(MOE_UNSUPPORTED, "intermediate must be a multiple of 4");
+  if (activation != MOE_ACT_SILU && activation != MOE_ACT_GELU_TANH)
+    return fail(MOE_INVALID_ARGUMENT, "unknown activation %d", activation);
+  if (rows == 0) return MOE_OK;
+  if (!gate_up || !dh || !d_gate_up) return fail(MOE_INVALID_ARGUMENT, "a pointer is NULL");
+  if (!aligned16(gate_up) || !aligned16(dh) || !aligned16(d_gate_up))
+    return fail(MOE_UNSUPPORTED, "gate_up, dh and d_gate_up must be 16-byte aligned");
+  const uint64_t n = (uint64_t)rows * (uint64_t)(intermediate / 4);
+  if ((n + 255) / 256 > 0x7FFFFFFFull) return fail(MOE_UNSUPPORTED, "rows too large");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const unsigned grid = (unsigned)((n + 255) / 256);
+  return launch("glu_backward", s, [&] {
+    if (activation == MOE_ACT_SILU)
+      k_glu_backward<ACT_SILU><<<grid, 256, 0, s>>>(gate_up, dh, d_gate_up, rows, intermediate);
+    else
+      k_glu_backward<ACT_GELU_TANH><<<grid, 256, 0, s>>>(gate_up, dh, d_gate_up, rows, intermediate);
+  });
 }
 
 moe_status moe_timing_enable(int32_t enable) {

@@ -34,6 +34,8 @@ KERNEL_SOURCES = {
     "router_route": ["common.h", "route.h", "decode.h", "moe_ffn.hip"],
     "gemm_gateup": ["common.h", "gemm.h", "gemm_big.h", "gemm_dma.h", "moe_ffn.hip"],
     "gemm_down": ["common.h", "gemm.h", "gemm_big.h", "gemm_dma.h", "moe_ffn.hip"],
+    "wsum_backward": ["common.h", "backward.h", "moe_ffn.hip"],
+    "glu_backward": ["common.h", "backward.h", "moe_ffn.hip"],
 }
 
 

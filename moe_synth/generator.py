@@ -55,7 +55,12 @@ TID_SH_UP = 8
 TID_SH_DOWN = 9
 TID_NORM = 10          # pre-FFN RMSNorm weight [H]
 TID_RESIDUAL = 11      # residual rows [T, H]
+TID_GRAD_W = 12        # backward inputs: routing weights, y, dout, gate_up, dh
+TID_GRAD_Y = 13
+TID_GRAD_DOUT = 14
+TID_GRAD_GU = 15
 TID_U4_CODES = 16      # + matrix index (0 gate, 1 up, 2 down)
+TID_GRAD_DH = 24
 TID_U4_SCALES = 32     # + matrix index
 ATTEMPT_SHIFT = 20     # resampled x rows use TID_X + (attempt << 20)
 
@@ -285,6 +290,21 @@ def residual_values(cfg: MoeConfig) -> np.ndarray:
     """Residual rows [T, H] (float32), N(0, 1)."""
     key = stream_key(cfg.seed, TID_RESIDUAL)
     return normal_np(key, 0, cfg.T * cfg.H).astype(np.float32).reshape(cfg.T, cfg.H)
+
+
+def grad_inputs(cfg: MoeConfig) -> dict:
+    """Inputs of the two backward steps at the workload's shape (float32):
+    w [T, k] uniform (0, 1); y [T, k, H], dout [T, H], dh [T*k, I] N(0, 1);
+    gate_up [T*k, 2I] N(0, 2^2), wide enough to reach both activation tails."""
+    T, k, H, I, s = cfg.T, cfg.k, cfg.H, cfg.I, cfg.seed
+    def nrm(tid, shape, std):
+        n = int(np.prod(shape))
+        return (normal_np(stream_key(s, tid), 0, n) * std).astype(np.float32).reshape(shape)
+    w = uniform_np(stream_key(s, TID_GRAD_W), np.arange(T * k, dtype=np.uint64))
+    return {"w": w.astype(np.float32).reshape(T, k), "y": nrm(TID_GRAD_Y, (T, k, H), 1.0),
+            "dout": nrm(TID_GRAD_DOUT, (T, H), 1.0),
+            "gate_up": nrm(TID_GRAD_GU, (T * k, 2 * I), 2.0),
+            "dh": nrm(TID_GRAD_DH, (T * k, I), 1.0)}
 
 
 def generate(cfg: MoeConfig, backend: str = "numpy", device=None) -> MoeInputs:

@@ -8,4 +8,5 @@ from . import moe_oracle
 from .moe_oracle import (router_logits, softmax_row, topk_stable_desc, route,
                          permutation, expert_ffn, shared_expert, moe_ffn,
                          silu, gelu_tanh, sigmoid, bf16_to_f64, f16_to_f64,
-                         u4_dequant, WeightSource)
+                         u4_dequant, WeightSource, weighted_sum_backward, glu_backward,
+                         rms_norm)

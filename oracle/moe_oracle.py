@@ -211,6 +211,60 @@ def route(logits, k: int, normalize: bool = True, gating: int = GATING_SOFTMAX,
     return ids, w
 
 
+# ------------------------------------------------------------------ backward
+# The two backward steps mlx-native's moe_dispatch.rs adds for training
+# (moe_weighted_sum_seq and moe_swiglu_seq backward), as printed there.
+def weighted_sum(w, y):
+    """out[t, d] = sum_j w[t, j] y[t, j, d] (the routing-weighted combine)."""
+    return np.einsum("tj,tjd->td", np.asarray(w, np.float64), np.asarray(y, np.float64))
+
+
+def weighted_sum_backward(w, y, dout):
+    """dy[t,j,d] = w[t,j] dout[t,d];  dw[t,j] = sum_d y[t,j,d] dout[t,d]."""
+    w = np.asarray(w, np.float64)
+    y = np.asarray(y, np.float64)
+    dout = np.asarray(dout, np.float64)
+    return w[:, :, None] * dout[:, None, :], np.einsum("tjd,td->tj", y, dout)
+
+
+def silu_grad(z):
+    """d/dz of z sigmoid(z) = sigmoid(z) (1 + z (1 - sigmoid(z)))."""
+    s = sigmoid(z)
+    return s * (1.0 + np.asarray(z, np.float64) * (1.0 - s))
+
+
+def gelu_tanh_grad(z):
+    """d/dz of 0.5 z (1 + tanh(c (z + a z^3))), by the product and chain rules."""
+    z = np.asarray(z, dtype=np.float64)
+    th = np.tanh(SQRT_2_OVER_PI * (z + GELU_CUBIC * z ** 3))
+    return 0.5 * (1.0 + th) + 0.5 * z * (1.0 - th * th) * SQRT_2_OVER_PI * (
+        1.0 + 3.0 * GELU_CUBIC * z * z)
+
+
+def activation_grad(kind: int, z):
+    if kind == ACT_SILU:
+        return silu_grad(z)
+    if kind == ACT_GELU_TANH:
+        return gelu_tanh_grad(z)
+    raise ValueError(f"unknown activation {kind}")
+
+
+def glu(gate_up, kind: int):
+    """h = act(g) * u for rows gate_up = g | u."""
+    gu = np.asarray(gate_up, np.float64)
+    I = gu.shape[1] // 2
+    return activation(kind, gu[:, :I]) * gu[:, I:]
+
+
+def glu_backward(gate_up, dh, kind: int):
+    """dg = dh u act'(g), du = dh act(g), returned in the gate_up layout."""
+    gu = np.asarray(gate_up, np.float64)
+    dh = np.asarray(dh, np.float64)
+    I = gu.shape[1] // 2
+    g, u = gu[:, :I], gu[:, I:]
+    return np.concatenate([dh * u * activation_grad(kind, g), dh * activation(kind, g)], axis=1)
+
+
 # ---------------------------------------------------------------- permutation
 def permutation(ids, E: int):
     """Stable grouping of the flat routes r = t*k + j by expert.

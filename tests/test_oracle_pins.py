@@ -234,6 +234,61 @@ def test_residual_is_added_to_out():
     np.testing.assert_allclose(c, 0.0, atol=1e-14)
 
 
+# ----------------------------------------------------------------- backward
+def _fd(f, x, eps=1e-6):
+    """Central differences of the scalar f at x, every element."""
+    x = np.array(x, dtype=np.float64)
+    g = np.zeros_like(x)
+    it = np.nditer(x, flags=["multi_index"])
+    for _ in it:
+        i = it.multi_index
+        xp, xm = x.copy(), x.copy()
+        xp[i] += eps
+        xm[i] -= eps
+        g[i] = (f(xp) - f(xm)) / (2 * eps)
+    return g
+
+
+def test_weighted_sum_backward_finite_differences():
+    # the page's falsifier: L = sum(out * seed); dL/dy and dL/dw by differences
+    rng = np.random.default_rng(61)
+    T, k, H = 3, 4, 7
+    y = rng.normal(size=(T, k, H))
+    w = rng.uniform(0.2, 1.0, size=(T, k))
+    seed = rng.normal(size=(T, H))
+    dy, dw = O.weighted_sum_backward(w, y, seed)
+    np.testing.assert_allclose(dy, _fd(lambda v: (O.weighted_sum(w, v) * seed).sum(), y),
+                               rtol=1e-7, atol=1e-8)
+    np.testing.assert_allclose(dw, _fd(lambda v: (O.weighted_sum(v, y) * seed).sum(), w),
+                               rtol=1e-7, atol=1e-8)
+
+
+@pytest.mark.parametrize("act", [ACT_SILU, ACT_GELU_TANH])
+def test_glu_backward_finite_differences_and_autograd(act):
+    rng = np.random.default_rng(62 + act)
+    R, I = 4, 5
+    gu = rng.normal(size=(R, 2 * I)) * 3
+    seed = rng.normal(size=(R, I))
+    got = O.glu_backward(gu, seed, act)
+    np.testing.assert_allclose(got, _fd(lambda v: (O.glu(v, act) * seed).sum(), gu),
+                               rtol=1e-6, atol=1e-8)
+    t = torch.from_numpy(gu).requires_grad_(True)
+    g, u = t[:, :I], t[:, I:]
+    a = F.silu(g) if act == ACT_SILU else F.gelu(g, approximate="tanh")
+    (a * u * torch.from_numpy(seed)).sum().backward()
+    np.testing.assert_allclose(got, t.grad.numpy(), rtol=1e-8, atol=1e-12)
+
+
+def test_glu_backward_asymptotics_from_page():
+    rows = {r[0]: [float(v) for v in r[1:]] for r in read_golden_rows("glu_backward_asymptotics.txt")}
+    gu = np.array([rows["g"] + rows["u"]])
+    d = np.array([rows["d"]])
+    out = O.glu_backward(gu, d, ACT_GELU_TANH)[0]
+    tol = np.array(rows["tol"])
+    assert (np.abs(out[:3] - rows["dg"]) <= tol).all()
+    assert (np.abs(out[3:] - rows["du"]) <= tol).all()
+
+
 def test_router_logits_transpose_and_bias():
     # l[t, e] = x_t . Wr[e]: a rectangular check that catches a transposed Wr
     x = np.array([[1.0, 2.0, 3.0]])
