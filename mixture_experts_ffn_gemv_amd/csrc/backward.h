@@ -11,18 +11,24 @@ namespace moe {
 
 // Combine backward, one workgroup per (token t, slot j):
 //   dy[t,j,:] = w[t,j] * dout[t,:]     dw[t,j] = y[t,j,:] . dout[t,:]
-// dout[t] is read by the k workgroups of token t (an L2 hit after the
-// first).  The dot product is summed per thread in a fixed order, then
-// over the wave and over the 4 waves in wave order: repeat runs agree.
+// dout[t] is read by the k workgroups of token t.  Workgroups are handed
+// to the 8 XCDs round-robin (block b to XCD b % 8), so block b serves
+// token 8 * (q / k) + b % 8, slot q % k (q = b / 8): the k workgroups of a
+// token share one XCD and its L2, and start together, so dout[t] comes
+// from HBM once.  The dot product is summed per thread in a fixed order,
+// then over the wave and over the 4 waves in wave order: repeat runs agree.
 template <bool DY, bool DW>
 __global__ __launch_bounds__(256) void k_wsum_backward(const float* __restrict__ w,
                                                        const float* __restrict__ y,
                                                        const float* __restrict__ dout,
                                                        float* __restrict__ dy,
-                                                       float* __restrict__ dw, int k, int H) {
+                                                       float* __restrict__ dw, int k, int H,
+                                                       int64_t T) {
   __shared__ float s_part[4];
-  const size_t tj = blockIdx.x;
-  const size_t t = tj / (size_t)k;
+  const size_t q = blockIdx.x >> 3;
+  const size_t t = (q / (size_t)k) * 8 + (blockIdx.x & 7);
+  if (t >= (size_t)T) return;
+  const size_t tj = t * (size_t)k + q % (size_t)k;
   const float wt = w[tj];
   const float* dr = dout + t * H;
   const float* yr = y + tj * H;

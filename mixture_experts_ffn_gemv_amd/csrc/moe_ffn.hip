@@ -809,18 +809,23 @@ moe_status moe_weighted_sum_backward(int64_t num_tokens, int32_t top_k, int32_t 
     return fail(MOE_INVALID_ARGUMENT, "top_k %d outside 1..%d", top_k, MOE_MAX_TOP_K);
   if (hidden <= 0) return fail(MOE_INVALID_ARGUMENT, "hidden must be positive");
   if (hidden % 4) return fail(MOE_UNSUPPORTED, "hidden must be a multiple of 4");
-  if (num_tokens * top_k > INT32_MAX)
+  if ((num_tokens + 7) / 8 * 8 * top_k > INT32_MAX)
     return fail(MOE_UNSUPPORTED, "num_tokens * top_k too large");
   if (num_tokens == 0 || (!dy && !dw)) return MOE_OK;
   if (!w || !dout || (dw && !y)) return fail(MOE_INVALID_ARGUMENT, "w, y or dout is NULL");
   if (!aligned16(y) || !aligned16(dout) || !aligned16(dy))
     return fail(MOE_UNSUPPORTED, "y, dout and dy must be 16-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const unsigned grid = (unsigned)(num_tokens * top_k);
+  // whole groups of 8 tokens (one per XCD); the blocks past T return at once
+  const unsigned grid = (unsigned)((num_tokens + 7) / 8 * 8 * top_k);
+  const int64_t T = num_tokens;
   return launch("wsum_backward", s, [&] {
-    if (dy && dw) k_wsum_backward<true, true><<<grid, 256, 0, s>>>(w, y, dout, dy, dw, top_k, hidden);
-    else if (dy) k_wsum_backward<true, false><<<grid, 256, 0, s>>>(w, y, dout, dy, dw, top_k, hidden);
-    else k_wsum_backward<false, true><<<grid, 256, 0, s>>>(w, y, dout, dy, dw, top_k, hidden);
+    if (dy && dw)
+      k_wsum_backward<true, true><<<grid, 256, 0, s>>>(w, y, dout, dy, dw, top_k, hidden, T);
+    else if (dy)
+      k_wsum_backward<true, false><<<grid, 256, 0, s>>>(w, y, dout, dy, dw, top_k, hidden, T);
+    else
+      k_wsum_backward<false, true><<<grid, 256, 0, s>>>(w, y, dout, dy, dw, top_k, hidden, T);
   });
 }
 
