@@ -90,6 +90,7 @@ __device__ __forceinline__ void u4_stage(f32x4* __restrict__ xs, float* __restri
 // mins) with the staged activations of nr routes:
 //   acc[k][r] += sc_k * sum_i c_ki x_ri + mn_k * xsum_r.
 // Each activation read from LDS serves both rows.
+template <bool BATCH>
 __device__ __forceinline__ void u4_group_dot2(const u32x4& v0, uint32_t sm0, const u32x4& v1,
                                               uint32_t sm1, const f32x4* __restrict__ xs,
                                               const float* __restrict__ xsum, int G, int c, int nr,
@@ -108,17 +109,36 @@ __device__ __forceinline__ void u4_group_dot2(const u32x4& v0, uint32_t sm0, con
 #pragma unroll
   for (int r = 0; r < kU4Routes; ++r) {
     if (r < nr) {
+      // BATCH: the route's 8 LDS reads are all issued before the first
+      // multiply-add (read and use interleaved, each read's latency is
+      // exposed), at the cost of 32 more registers; without it the reads
+      // stream one by one
+      const f32x4* xr = xs + (size_t)r * 8 * G + c;
+      const float xsr = xsum[r * G + c];
       float d0 = 0.f, d1 = 0.f;
+      if constexpr (BATCH) {
+        f32x4 x4[8];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const f32x4 x4 = xs[(r * 8 + q) * G + c];
+        for (int q = 0; q < 8; ++q) x4[q] = xr[q * G];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          d0 = fmaf(w0[4 * q + e], x4[e], d0);
-          d1 = fmaf(w1[4 * q + e], x4[e], d1);
+        for (int q = 0; q < 8; ++q) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            d0 = fmaf(w0[4 * q + e], x4[q][e], d0);
+            d1 = fmaf(w1[4 * q + e], x4[q][e], d1);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const f32x4 x4 = xr[q * G];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            d0 = fmaf(w0[4 * q + e], x4[e], d0);
+            d1 = fmaf(w1[4 * q + e], x4[e], d1);
+          }
         }
       }
-      const float xsr = xsum[r * G + c];
       acc0[r] = fmaf(sc0, d0, fmaf(mn0, xsr, acc0[r]));
       acc1[r] = fmaf(sc1, d1, fmaf(mn1, xsr, acc1[r]));
     }
@@ -220,7 +240,9 @@ __global__ __launch_bounds__(256) void k_dec_u4(Dec2Params p) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int c = lane + 64 * u;
-        if (c < G) u4_group_dot2(va[u], sa[u], vb[u], sb[u], xs, xsum, G, c, nr, a0, a1);
+        // gate/up stages more activations (fewer workgroups per CU) and has
+        // registers to spare at its occupancy; down does not
+        if (c < G) u4_group_dot2<MODE == 0>(va[u], sa[u], vb[u], sb[u], xs, xsum, G, c, nr, a0, a1);
       }
       size_t ra, rb2;
       int na, nb;
