@@ -35,14 +35,28 @@ constexpr int kU4LdsMax = 160 * 1024 - 4096;  // LDS bytes available to the stag
 // LDS bytes per staged route of row length K: activations plus group sums.
 __host__ __device__ constexpr int u4_route_bytes(int K) { return K * 4 + (K / 32) * 4; }
 
-// 8 nibbles of one 32-bit word -> floats, in element order (low nibble first).
+// Byte n of v as a float, one v_cvt_f32_ubyte{n} (written out: from the
+// shifted-and-masked C expression the compiler emits a bit-field extract
+// and then the byte-0 conversion, two instructions).
+template <int N>
+__device__ __forceinline__ float ubyte_f(uint32_t v) {
+  float f;
+  if constexpr (N == 0) asm("v_cvt_f32_ubyte0 %0, %1" : "=v"(f) : "v"(v));
+  else if constexpr (N == 1) asm("v_cvt_f32_ubyte1 %0, %1" : "=v"(f) : "v"(v));
+  else if constexpr (N == 2) asm("v_cvt_f32_ubyte2 %0, %1" : "=v"(f) : "v"(v));
+  else asm("v_cvt_f32_ubyte3 %0, %1" : "=v"(f) : "v"(v));
+  return f;
+}
+
+// 8 nibbles of one 32-bit word -> floats, in element order (low nibble
+// first): two masks, one shift and eight byte conversions.
 __device__ __forceinline__ void nib8(uint32_t w, float (&f)[8]) {
   const uint32_t lo = w & 0x0F0F0F0Fu;          // elements 0, 2, 4, 6 in bytes 0..3
   const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;   // elements 1, 3, 5, 7
-  f[0] = (float)(lo & 0xFFu);         f[1] = (float)(hi & 0xFFu);
-  f[2] = (float)((lo >> 8) & 0xFFu);  f[3] = (float)((hi >> 8) & 0xFFu);
-  f[4] = (float)((lo >> 16) & 0xFFu); f[5] = (float)((hi >> 16) & 0xFFu);
-  f[6] = (float)(lo >> 24);           f[7] = (float)(hi >> 24);
+  f[0] = ubyte_f<0>(lo); f[1] = ubyte_f<0>(hi);
+  f[2] = ubyte_f<1>(lo); f[3] = ubyte_f<1>(hi);
+  f[4] = ubyte_f<2>(lo); f[5] = ubyte_f<2>(hi);
+  f[6] = ubyte_f<3>(lo); f[7] = ubyte_f<3>(hi);
 }
 
 // Stage the activations of nr routes (rows[rr], f32 or bf16, length K) and
