@@ -171,9 +171,13 @@ __device__ __forceinline__ void u4_load(const MatStack& m, size_t row, int G, in
 }
 
 // MODE 0: gate/up (K = H, rows = I features, two matrices); 1: down (K = I,
-// rows = H outputs).  U groups per lane cover a row (64*U >= K/32).
-template <int MODE, int ACT, int U>
+// rows = H outputs).  LPR lanes share a row (64: the whole wave; 16: four
+// rows side by side, for rows whose group count is not a multiple of 64,
+// e.g. 48 groups at K = 1536 would leave a quarter of a 64-lane wave
+// idle); U groups per lane cover it (LPR*U >= K/32).
+template <int MODE, int ACT, int U, int LPR>
 __global__ __launch_bounds__(256) void k_dec_u4(Dec2Params p) {
+  constexpr int SEGS = 64 / LPR;  // rows side by side in a wave
   extern __shared__ __attribute__((aligned(16))) float u4lds[];
   const int s = blockIdx.x;
   if (s >= *p.n_active) return;
@@ -182,7 +186,7 @@ __global__ __launch_bounds__(256) void k_dec_u4(Dec2Params p) {
   const int K = MODE == 0 ? p.H : p.I;
   const int N = MODE == 0 ? p.I : p.H;
   const int G = K / 32;
-  const int rb = blockIdx.y * kU4Rows;
+  const int rb = blockIdx.y * kU4Rows * SEGS;
   if (rb >= N) return;
   int count = p.counts[g], base = p.offsets[g];
   ws_span(base, count, R);
@@ -190,7 +194,8 @@ __global__ __launch_bounds__(256) void k_dec_u4(Dec2Params p) {
   f32x4* xs = reinterpret_cast<f32x4*>(u4lds);
   float* xsum = u4lds + rc * K;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  constexpr int RPW = kU4Rows / 4;  // rows per wave
+  const int seg = lane / LPR, sl = lane % LPR;  // the lane's row segment, lane in it
+  constexpr int RPW = kU4Rows / 4;  // rows per wave segment
 
   for (int r0 = 0; r0 < count; r0 += rc) {
     const int nr = min(rc, count - r0);
@@ -214,10 +219,11 @@ __global__ __launch_bounds__(256) void k_dec_u4(Dec2Params p) {
     // n and n+1 (down); each activation read from LDS serves both.
     constexpr int STEPS = MODE == 0 ? RPW : RPW / 2;
     auto rows_of = [&](int i, size_t& ra, size_t& rb2, int& na, int& nb) {
+      const int r0w = rb + (wave * SEGS + seg) * RPW;
       if constexpr (MODE == 0) {
-        na = nb = rb + wave * RPW + i;
+        na = nb = r0w + i;
       } else {
-        na = rb + wave * RPW + 2 * i;
+        na = r0w + 2 * i;
         nb = na + 1;
       }
       ra = (size_t)g * N + min(na, N - 1);  // rows past N are clamped and never stored
@@ -230,7 +236,7 @@ __global__ __launch_bounds__(256) void k_dec_u4(Dec2Params p) {
       rows_of(i, ra, rb2, na, nb);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int c = lane + 64 * u;
+        const int c = sl + LPR * u;
         if constexpr (MODE == 0) {
           u4_load(p.gate, ra, G, c, va[u], sa[u]);
           u4_load(p.up, rb2, G, c, vb[u], sb[u]);
@@ -253,7 +259,7 @@ __global__ __launch_bounds__(256) void k_dec_u4(Dec2Params p) {
       for (int r = 0; r < kU4Routes; ++r) { a0[r] = 0.f; a1[r] = 0.f; }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int c = lane + 64 * u;
+        const int c = sl + LPR * u;
         // gate/up stages more activations (fewer workgroups per CU) and has
         // registers to spare at its occupancy; down does not
         if (c < G) u4_group_dot2<MODE == 0>(va[u], sa[u], vb[u], sb[u], xs, xsum, G, c, nr, a0, a1);
@@ -264,9 +270,9 @@ __global__ __launch_bounds__(256) void k_dec_u4(Dec2Params p) {
 #pragma unroll
       for (int r = 0; r < kU4Routes; ++r) {
         if (r < nr) {
-          const float d0 = wave_sum(a0[r]);
-          const float d1 = wave_sum(a1[r]);
-          if (lane == 0) {
+          const float d0 = LPR == 64 ? wave_sum(a0[r]) : group_sum<LPR>(a0[r]);
+          const float d1 = LPR == 64 ? wave_sum(a1[r]) : group_sum<LPR>(a1[r]);
+          if (sl == 0) {
             if constexpr (MODE == 0) {
               const int route = ws_route(p.perm[base + r0 + r], R);
               if (na < N) p.h[(size_t)route * N + na] = act_f<ACT>(d0) * d1;

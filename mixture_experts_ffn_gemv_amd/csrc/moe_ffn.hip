@@ -506,8 +506,12 @@ void launch_dn3(int u, dim3 grid, hipStream_t s, const Dec2Params& dp) {
   }
 }
 
+// Lanes per row of the 4-bit kernels for rows of G groups: the whole wave,
+// or 16 when G is a multiple of 16 but not of 64 (at most 8 groups a lane).
+int u4_lpr(int G) { return (G % 64 != 0 && G % 16 == 0 && G <= 16 * 8) ? 16 : 64; }
+
 template <int MODE, int ACT>
-moe_status launch_u4(const char* name, int u, dim3 grid, size_t lds, hipStream_t s,
+moe_status launch_u4(const char* name, int G, dim3 grid, size_t lds, hipStream_t s,
                      const Dec2Params& dp) {
   auto go = [&](auto kern) -> moe_status {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -517,14 +521,21 @@ moe_status launch_u4(const char* name, int u, dim3 grid, size_t lds, hipStream_t
                   hipGetErrorString(e));
     return launch(name, s, [&] { kern<<<grid, 256, lds, s>>>(dp); });
   };
-  switch (u) {
-    case 1: return go(k_dec_u4<MODE, ACT, 1>);
-    case 2: return go(k_dec_u4<MODE, ACT, 2>);
-    case 3: return go(k_dec_u4<MODE, ACT, 3>);
-    case 4: return go(k_dec_u4<MODE, ACT, 4>);
-    case 6: return go(k_dec_u4<MODE, ACT, 6>);
-    default: return go(k_dec_u4<MODE, ACT, 8>);
-  }
+  const int lpr = u4_lpr(G);
+  const int u = pick_u(G * 64 / lpr);  // groups per lane, as if the row had 64/lpr times G
+  auto by_u = [&](auto lpr_c) -> moe_status {
+    constexpr int L = decltype(lpr_c)::value;
+    switch (u) {
+      case 1: return go(k_dec_u4<MODE, ACT, 1, L>);
+      case 2: return go(k_dec_u4<MODE, ACT, 2, L>);
+      case 3: return go(k_dec_u4<MODE, ACT, 3, L>);
+      case 4: return go(k_dec_u4<MODE, ACT, 4, L>);
+      case 6: return go(k_dec_u4<MODE, ACT, 6, L>);
+      default: return go(k_dec_u4<MODE, ACT, 8, L>);
+    }
+  };
+  return lpr == 16 ? by_u(std::integral_constant<int, 16>{})
+                   : by_u(std::integral_constant<int, 64>{});
 }
 
 // 4-bit weights, T <= 32: gate/up and down with the routes' activations
@@ -541,17 +552,18 @@ moe_status run_experts_u4(const moe_desc* d, const Plan& p, Dec2Params dp, float
     Dec2Params g = dp;
     g.rc = rc_for(p.H);
     const size_t lds = (size_t)g.rc * u4_route_bytes(p.H);
-    dim3 grid(p.max_groups, (p.I + kU4Rows - 1) / kU4Rows);
-    const int u = pick_u(p.H / 32);
-    if (d->activation == MOE_ACT_SILU) MOE_TRY((launch_u4<0, ACT_SILU>("gemv_gateup", u, grid, lds, s, g)));
-    else MOE_TRY((launch_u4<0, ACT_GELU_TANH>("gemv_gateup", u, grid, lds, s, g)));
+    const int G = p.H / 32, rows = kU4Rows * (64 / u4_lpr(G));
+    dim3 grid(p.max_groups, (p.I + rows - 1) / rows);
+    if (d->activation == MOE_ACT_SILU) MOE_TRY((launch_u4<0, ACT_SILU>("gemv_gateup", G, grid, lds, s, g)));
+    else MOE_TRY((launch_u4<0, ACT_GELU_TANH>("gemv_gateup", G, grid, lds, s, g)));
   }
   {
     Dec2Params g = dp;
     g.rc = rc_for(p.I);
     const size_t lds = (size_t)g.rc * u4_route_bytes(p.I);
-    dim3 grid(p.max_groups, (p.H + kU4Rows - 1) / kU4Rows);
-    MOE_TRY((launch_u4<1, 0>("gemv_down", pick_u(p.I / 32), grid, lds, s, g)));
+    const int G = p.I / 32, rows = kU4Rows * (64 / u4_lpr(G));
+    dim3 grid(p.max_groups, (p.H + rows - 1) / rows);
+    MOE_TRY((launch_u4<1, 0>("gemv_down", G, grid, lds, s, g)));
   }
   const size_t nthr = (size_t)p.T * (p.H / 4);
   return launch("combine", s, [&] {
