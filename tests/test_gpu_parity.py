@@ -274,3 +274,46 @@ def test_workspace_reuse_across_calls_and_token_counts():
         assert rel_err(out.cpu().numpy(), ref_out[:T]) <= 2e-2
     assert int(ws[:M.WORKSPACE_ZERO_BYTES].count_nonzero()) == 0
 
+
+
+@pytest.mark.parametrize("name", ["decode_geglu_t1", "decode_u4_t32", "prefill_shared_t4096"])
+def test_graph_replay_matches_eager(name):
+    """The launch configuration bench.py times: the forward captured in a HIP
+    graph and replayed.  Several replays, with eager work and
+    synchronisations between them; each must equal the eager result bit for
+    bit (the routing ticket is reset by the kernels, not by a memset)."""
+    import mixture_experts_ffn_gemv_amd as M
+    case = Case(CONFIGS[name])
+    T = CONFIGS[name].T
+    ws = M.alloc_workspace(case.desc, T)
+    out = torch.empty((T, CONFIGS[name].H), dtype=torch.float32, device="cuda")
+    ref = M.moe_ffn_forward(case.desc, case.dev.x, case.weights, workspace=ws).clone()
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        M.moe_ffn_forward(case.desc, case.dev.x, case.weights, out=out, workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        M.moe_ffn_forward(case.desc, case.dev.x, case.weights, out=out, workspace=ws)
+    for it in range(4):
+        out.fill_(float("nan"))
+        log(f"[gpu] graph replay {it} {name}")
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"replay {it} differs from the eager result"
+        # eager work on the same workspace between replays
+        e = M.moe_ffn_forward(case.desc, case.dev.x, case.weights, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(e, ref)
+    assert int(ws[:M.WORKSPACE_ZERO_BYTES].count_nonzero()) == 0
+
+
+def test_max_hidden_decode():
+    """hidden = 16384, the largest the decode kernels take (several K passes
+    per lane), bf16 weights, two tokens."""
+    cfg = MoeConfig(name="decode_h16384", T=2, H=16384, I=256, E=8, k=2, weight_format=WF_BF16,
+                    router_dtype=DT_BF16, seed_index=55)
+    check_case(Case(cfg))
