@@ -4,10 +4,12 @@
 // One workgroup per (touched expert, block of output rows).  The activations
 // of the expert's routes (x for gate/up, h for down), up to kU4Routes per
 // pass, are staged once in LDS and shared by every row of the block, in a
-// chunk-interleaved layout: 16-byte piece q of 32-element group c of route r
-// sits at float4 index (r*8 + q)*G + c (G groups per row), so the lanes of a
-// wave, which own consecutive groups, read consecutive 16-byte words.  Next
-// to them, the sum of each group's 32 activations.
+// group-contiguous layout: 16-byte piece q of 32-element group c of route r
+// sits at float4 index (r*G + c)*9 + q (G groups per row, one float4 of
+// padding per group), so a lane reads its group's 8 pieces at immediate
+// offsets from one address, and the 144-byte stride between the lanes'
+// groups keeps every 8 or 16 lanes of a ds_read_b128 on distinct banks.
+// Next to them, the sum of each group's 32 activations.
 //
 // A group of one row is dequantised once and reused for every route:
 //   sum_i (c_i*s + m) x_i = s * sum_i c_i x_i + m * sum_i x_i,
@@ -33,7 +35,8 @@ constexpr int kU4Rows = 32;      // output rows (features) per workgroup
 constexpr int kU4LdsMax = 160 * 1024 - 4096;  // LDS bytes available to the staging
 
 // LDS bytes per staged route of row length K: activations plus group sums.
-__host__ __device__ constexpr int u4_route_bytes(int K) { return K * 4 + (K / 32) * 4; }
+constexpr int kU4GroupF4 = 9;   // float4 slots per staged group (8 pieces + padding)
+__host__ __device__ constexpr int u4_route_bytes(int K) { return (K / 32) * (kU4GroupF4 * 16 + 4); }
 
 // Byte n of v as a float, one v_cvt_f32_ubyte{n} (written out: from the
 // shifted-and-masked C expression the compiler emits a bit-field extract
@@ -90,7 +93,7 @@ __device__ __forceinline__ void u4_stage(f32x4* __restrict__ xs, float* __restri
       const bool ok = i < n;
       const int q = i & 7, rc = i >> 3;
       const int rr = rc / G, c = rc - rr * G;
-      if (ok) xs[(rr * 8 + q) * G + c] = v[j];
+      if (ok) xs[(rr * G + c) * kU4GroupF4 + q] = v[j];
       float sm = ok ? (v[j][0] + v[j][1]) + (v[j][2] + v[j][3]) : 0.f;
       sm += __shfl_xor(sm, 1, 64);
       sm += __shfl_xor(sm, 2, 64);
@@ -127,13 +130,13 @@ __device__ __forceinline__ void u4_group_dot2(const u32x4& v0, uint32_t sm0, con
       // multiply-add (read and use interleaved, each read's latency is
       // exposed), at the cost of 32 more registers; without it the reads
       // stream one by one
-      const f32x4* xr = xs + (size_t)r * 8 * G + c;
+      const f32x4* xr = xs + ((size_t)r * G + c) * kU4GroupF4;
       const float xsr = xsum[r * G + c];
       float d0 = 0.f, d1 = 0.f;
       if constexpr (BATCH) {
         f32x4 x4[8];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) x4[q] = xr[q * G];
+        for (int q = 0; q < 8; ++q) x4[q] = xr[q];
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
 #pragma unroll
@@ -145,7 +148,7 @@ __device__ __forceinline__ void u4_group_dot2(const u32x4& v0, uint32_t sm0, con
       } else {
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
-          const f32x4 x4 = xr[q * G];
+          const f32x4 x4 = xr[q];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             d0 = fmaf(w0[4 * q + e], x4[e], d0);
@@ -192,7 +195,7 @@ __global__ __launch_bounds__(256) void k_dec_u4(Dec2Params p) {
   ws_span(base, count, R);
   const int rc = p.rc;  // routes per pass (<= kU4Routes), sized to the LDS
   f32x4* xs = reinterpret_cast<f32x4*>(u4lds);
-  float* xsum = u4lds + rc * K;
+  float* xsum = u4lds + (size_t)rc * G * kU4GroupF4 * 4;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int seg = lane / LPR, sl = lane % LPR;  // the lane's row segment, lane in it
   constexpr int RPW = kU4Rows / 4;  // rows per wave segment
