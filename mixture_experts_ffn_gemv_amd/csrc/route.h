@@ -211,7 +211,12 @@ struct ScanOut {
   int32_t* user_offsets;  // [E+1] or null
 };
 
-// One workgroup of 256 threads; thread e owns expert e (E <= 256).
+// One workgroup of 256 threads; thread e owns expert e (E <= 256).  The
+// per-block counts of a column are read kScanBatch at a time, every load of
+// a batch issued before any is added (indices clamped, so the loads need no
+// branch): read one by one, each load's latency would add up over the
+// blocks.
+constexpr int kScanBatch = 16;
 __global__ __launch_bounds__(256) void k_perm_scan(const int32_t* __restrict__ block_hist,
                                                    int nblk, int E, int T, int has_shared,
                                                    int tile_rows, int build_tiles, ScanOut o) {
@@ -219,9 +224,19 @@ __global__ __launch_bounds__(256) void k_perm_scan(const int32_t* __restrict__ b
   __shared__ int sa[256];
   __shared__ int st[256];
   const int e = threadIdx.x;
+  const int ec = min(e, E - 1);
+  auto batch = [&](int b0, int (&v)[kScanBatch]) {
+#pragma unroll
+    for (int j = 0; j < kScanBatch; ++j) v[j] = block_hist[(size_t)min(b0 + j, nblk - 1) * E + ec];
+  };
   int cnt = 0;
-  if (e < E)
-    for (int b = 0; b < nblk; ++b) cnt += block_hist[(size_t)b * E + e];
+  for (int b0 = 0; b0 < nblk; b0 += kScanBatch) {
+    int v[kScanBatch];
+    batch(b0, v);
+#pragma unroll
+    for (int j = 0; j < kScanBatch; ++j) cnt += (b0 + j < nblk) ? v[j] : 0;
+  }
+  if (e >= E) cnt = 0;
   const int act = (e < E && cnt > 0) ? 1 : 0;
   const int tiles = (e < E) ? (cnt + tile_rows - 1) / tile_rows : 0;
   sc[e] = cnt;
@@ -252,9 +267,16 @@ __global__ __launch_bounds__(256) void k_perm_scan(const int32_t* __restrict__ b
     if (o.user_offsets) o.user_offsets[e] = off;
     if (act) o.active[aoff] = e;
     int run = off;
-    for (int b = 0; b < nblk; ++b) {
-      o.block_off[(size_t)b * E + e] = run;
-      run += block_hist[(size_t)b * E + e];
+    for (int b0 = 0; b0 < nblk; b0 += kScanBatch) {
+      int v[kScanBatch];
+      batch(b0, v);
+#pragma unroll
+      for (int j = 0; j < kScanBatch; ++j) {
+        if (b0 + j < nblk) {
+          o.block_off[(size_t)(b0 + j) * E + e] = run;
+          run += v[j];
+        }
+      }
     }
     if (build_tiles)
       for (int i = 0; i < tiles; ++i) {

@@ -57,6 +57,10 @@ SMALL = [
     MoeConfig(name="mfma_dma_gelu_bias", T=1100, H=128, I=320, E=2, k=1, act=ACT_GELU_TANH,
               weight_format=WF_BF16, act_dtype=DT_BF16, router_dtype=DT_BF16, bias=BIAS_ZIPF,
               seed_index=31),
+    # longer K walk (20 steps of 64) and 41 logit columns: ragged router tile
+    MoeConfig(name="mfma_router_long_k", T=333, H=1280, I=64, E=40, k=3, weight_format=WF_BF16,
+              act_dtype=DT_BF16, router_dtype=DT_BF16, bias=BIAS_ZIPF, shared=True, Is=64,
+              seed_index=64),
     MoeConfig(name="mfma_t33", T=33, H=128, I=64, E=8, k=2, weight_format=WF_BF16,
               act_dtype=DT_BF16, router_dtype=DT_BF16, seed_index=14),
     MoeConfig(name="mfma_dense_e1", T=40, H=128, I=64, E=1, k=1, weight_format=WF_BF16,
