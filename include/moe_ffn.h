@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define MOE_FFN_ABI_VERSION 5
+#define MOE_FFN_ABI_VERSION 6
 
 /* Leading workspace bytes that must be zero before a workspace's first use. */
 #define MOE_WORKSPACE_ZERO_BYTES 256
@@ -158,6 +158,17 @@ typedef struct moe_weights {
   const void* shared_up;       /* [Is, H]                                    */
   const void* shared_down;     /* [H, Is]                                    */
   const float* norm_weight;    /* [H] f32 (pre_norm only)                    */
+  /* Optional, bf16 weights only: the same expert weights in the packed
+   * layout moe_pack_weights writes.  When the prefill GEMMs stream weight
+   * tiles (bf16 weights and activations, many routes per expert) they read
+   * these instead of gate/up/down, as contiguous 32 KB blocks.  The
+   * row-major pointers above stay required (the other paths read them).
+   * gate_up_packed and shared_gate_up_packed are used together or not at
+   * all, and so are down_packed and shared_down_packed; NULL: not used.  */
+  const void* gate_up_packed;
+  const void* down_packed;
+  const void* shared_gate_up_packed;
+  const void* shared_down_packed;
 } moe_weights;
 
 /* ABI version (MOE_FFN_ABI_VERSION of the built library). */
@@ -259,6 +270,44 @@ moe_status moe_weighted_sum_backward(int64_t num_tokens, int32_t top_k, int32_t 
  */
 moe_status moe_glu_backward(int64_t rows, int32_t intermediate, int32_t activation,
                             const float* gate_up, const float* dh, float* d_gate_up,
+                            void* stream);
+
+/*
+ * Packed expert weights: a layout of the bf16 expert weights for the prefill
+ * grouped GEMMs (the FFN of Switch Transformers section 2, or the gated FFN of
+ * Mixtral's sparse MoE layer, per expert).  Those GEMMs stream weight tiles
+ * 64 K-elements at a time; the packed layout stores each tile's K-step as one
+ * contiguous 32 KB block, so HBM serves it as a sequential run instead of 256
+ * rows of 128 bytes.  The arithmetic, and so every result, is unchanged.
+ *
+ * Layout (bf16 elements, 16-byte chunks): block (t, s) of an expert holds
+ * K-elements 64s .. 64s+63 of its weight tile t as 256 rows of 128 bytes.
+ * Gate/up tiles cover 128 features: row r < 128 is gate feature 128t + r,
+ * row r >= 128 up feature 128t + r - 128 (t < ceil(I/128)).  Down tiles cover
+ * 256 outputs: row r is output 256t + r (t < ceil(H/256)); its K is I.  Chunk
+ * c of row r (elements 64s + 8c .. 64s + 8c + 7) is stored at chunk slot
+ * c ^ ((r >> 1) & 7) of the row.  Rows past the matrix are zero.  An expert's
+ * blocks are ordered t * (K/64) + s; experts are consecutive.  The shared
+ * expert is packed the same way with Is for I.
+ *
+ * moe_packed_weight_bytes: the four arrays' sizes (0 for the shared expert's
+ * when there is none).  Any output pointer may be NULL.  Host only.  Errors:
+ * MOE_INVALID_ARGUMENT for a bad descriptor; MOE_UNSUPPORTED unless the
+ * weights are bf16, hidden, intermediate and shared_intermediate are
+ * multiples of 64, and one expert's packed matrix fits in 4 GiB.
+ *
+ * moe_pack_weights: enqueues the packing of weights->gate/up/down (and the
+ * shared expert's) into the caller's device arrays, 16-byte aligned, of the
+ * sizes above, on `stream`.  Reads only those weights; the destinations must
+ * not overlap them.  Errors: as above, plus MOE_INVALID_ARGUMENT for a NULL
+ * source or destination and MOE_UNSUPPORTED for a misaligned one.
+ */
+moe_status moe_packed_weight_bytes(const moe_desc* desc, size_t* gate_up_bytes,
+                                   size_t* down_bytes, size_t* shared_gate_up_bytes,
+                                   size_t* shared_down_bytes);
+moe_status moe_pack_weights(const moe_desc* desc, const moe_weights* weights,
+                            void* gate_up_packed, void* down_packed,
+                            void* shared_gate_up_packed, void* shared_down_packed,
                             void* stream);
 
 /*

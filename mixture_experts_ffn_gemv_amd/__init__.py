@@ -35,6 +35,7 @@ DT_F32, DT_BF16 = 0, 1
 
 EXPORTED_SYMBOLS = ("moe_abi_version", "moe_last_error", "moe_workspace_size", "moe_route",
                     "moe_ffn_forward", "moe_weighted_sum_backward", "moe_glu_backward",
+                    "moe_packed_weight_bytes", "moe_pack_weights",
                     "moe_timing_enable", "moe_timing_read", "moe_timing_reset")
 
 
@@ -63,7 +64,10 @@ class Weights(ctypes.Structure):
                 ("gate_u4", U4Matrix), ("up_u4", U4Matrix), ("down_u4", U4Matrix),
                 ("shared_gate_inp", ctypes.c_void_p), ("shared_gate", ctypes.c_void_p),
                 ("shared_up", ctypes.c_void_p), ("shared_down", ctypes.c_void_p),
-                ("norm_weight", ctypes.c_void_p)]
+                ("norm_weight", ctypes.c_void_p),
+                ("gate_up_packed", ctypes.c_void_p), ("down_packed", ctypes.c_void_p),
+                ("shared_gate_up_packed", ctypes.c_void_p),
+                ("shared_down_packed", ctypes.c_void_p)]
 
 
 _lib = None
@@ -94,6 +98,12 @@ def load(path: Optional[str] = None):
     lib.moe_weighted_sum_backward.restype = i32
     lib.moe_glu_backward.argtypes = [i64, i32, i32, vp, vp, vp, vp]
     lib.moe_glu_backward.restype = i32
+    szp = ctypes.POINTER(ctypes.c_size_t)
+    lib.moe_packed_weight_bytes.argtypes = [ctypes.POINTER(Desc), szp, szp, szp, szp]
+    lib.moe_packed_weight_bytes.restype = i32
+    lib.moe_pack_weights.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(Weights), vp, vp, vp,
+                                     vp, vp]
+    lib.moe_pack_weights.restype = i32
     lib.moe_timing_enable.argtypes = [i32]
     lib.moe_timing_enable.restype = i32
     lib.moe_timing_read.argtypes = [ctypes.c_char_p, i32, ctypes.POINTER(ctypes.c_int64),
@@ -146,6 +156,32 @@ def workspace_size(desc: Desc, num_tokens: int) -> int:
     n = ctypes.c_size_t(0)
     _check(load().moe_workspace_size(ctypes.byref(desc), num_tokens, ctypes.byref(n)))
     return n.value
+
+
+PACKED_FIELDS = ("gate_up_packed", "down_packed", "shared_gate_up_packed", "shared_down_packed")
+
+
+def packed_weight_bytes(desc: Desc) -> tuple:
+    """Sizes of (gate_up, down, shared_gate_up, shared_down) packed arrays."""
+    n = [ctypes.c_size_t(0) for _ in range(4)]
+    _check(load().moe_packed_weight_bytes(ctypes.byref(desc), *[ctypes.byref(v) for v in n]))
+    return tuple(v.value for v in n)
+
+
+def pack_weights(desc: Desc, weights: Weights, device="cuda", stream=None) -> dict:
+    """Packs the bf16 expert weights of ``weights`` into new device arrays and
+    points ``weights``' packed fields at them; returns the arrays (keep them
+    alive while ``weights`` is in use)."""
+    import torch
+    sizes = packed_weight_bytes(desc)
+    bufs = {n: torch.empty(sz, dtype=torch.uint8, device=device)
+            for n, sz in zip(PACKED_FIELDS, sizes) if sz}
+    ptrs = [_ptr(bufs.get(n)) for n in PACKED_FIELDS]
+    _check(load().moe_pack_weights(ctypes.byref(desc), ctypes.byref(weights), *ptrs,
+                                   _stream(stream)))
+    for n, q in zip(PACKED_FIELDS, ptrs):
+        setattr(weights, n, q)
+    return bufs
 
 
 def _stream(stream):

@@ -54,6 +54,11 @@ struct GemmParams {
   const int32_t* tile_m0;
   const int32_t* n_tiles;
   int E, T, H, I, Is, ncols;
+  // GATEUP/DOWN on the direct-to-LDS kernel: weights packed into K-step
+  // blocks (moe_pack_weights layout) for the routed experts and the shared
+  // one; null: the row-major w0/w1/sw0/sw1 are read
+  const uint8_t* pk;
+  const uint8_t* spk;
 };
 
 // LDS tiles are rows of 64 bf16 (128 bytes = 8 chunks of 16 bytes).  A

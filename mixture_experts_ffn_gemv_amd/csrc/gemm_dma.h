@@ -8,13 +8,19 @@
 // wait insertion cannot tell the ring's stages apart and drains every load
 // in flight at the top of the loop.  K-steps of 64 make every load cover
 // whole 128-byte lines (half as many outstanding requests per byte as steps
-// of 32, whose extra ring depth measured no faster); a 2-stage ring of 64 KB
-// stages keeps one K-step in flight while the other is multiplied.
+// of 32, whose extra ring depth measured no faster).  The weight operand has
+// three 32 KB slots and the route operand two, so that the weight stream
+// keeps two K-steps in flight while one is multiplied.
 //
 // Each load instruction of a wave fills 1 KB of LDS, lane i writing bytes
 // 16i..16i+15 of it.  A swizzled layout (16-byte chunk c of row r at slot
 // c ^ ((r >> 1) & 7) for 128-byte rows) is obtained by the choice of source:
 // lane i of 1-KB block b loads row b*8 + i/8, chunk (i & 7) ^ ((row >> 1) & 7).
+//
+// Weights may instead come packed (k_pack below): each (expert, weight tile,
+// K-step) block is the 32 KB LDS image of that stage's weight operand, so a
+// stage's weight loads read one contiguous 32 KB run instead of 256 rows of
+// 128 bytes, which HBM serves at a far higher rate.
 //
 // kDmaWaves waves in a 2 (weight rows) x kDmaWaves/2 (routes) grid, each owning
 // 128 weight rows x 512/kDmaWaves routes of f32 accumulators (tiles of
@@ -34,12 +40,14 @@ constexpr int kDmaBT = 256;                    // routes per tile
 constexpr int kDmaWaves = 8;                   // waves per workgroup (2 per SIMD)
 constexpr int kDmaThreads = 64 * kDmaWaves;
 constexpr int kDmaBK = 64;                     // K per stage: full 128-byte rows
-constexpr int kDmaRing = 2;                    // LDS stages (2 x 64 KB)
+constexpr int kDmaSlotsB = 2;                  // LDS slots of the route operand (32 KB each)
 constexpr int kDmaGroupT = 8;                  // route tiles per tile-order group
 #ifndef MOE_DMA_MIN_AVG_ROUTES
 #define MOE_DMA_MIN_AVG_ROUTES 96
 #endif
 constexpr int kDmaMinAvgRoutes = MOE_DMA_MIN_AVG_ROUTES;  // mean routes per expert
+constexpr int kPackRows = 256;                   // weight rows per packed block
+constexpr int kPackBlock = kPackRows * kDmaBK * 2;  // bytes per packed block (32 KB)
 
 // One 1-KB direct load per wave: lane i reads 16 bytes at sbase + voff and
 // writes them to LDS byte address lds + 16 i.  M0, which carries the LDS
@@ -92,30 +100,22 @@ __device__ __forceinline__ void dma_tile_order(int L, int ntt, int nnt, int& tt,
   nt = r / gt;
 }
 
-template <int PER>
-__device__ __forceinline__ void wait_tiles(int ahead) {  // leave `ahead` tiles in flight
-  if (ahead >= 3) wait_vmem<3 * PER>();
-  else if (ahead == 2) wait_vmem<2 * PER>();
-  else if (ahead == 1) wait_vmem<PER>();
-  else wait_vmem<0>();
-}
-
-// BKD: K per stage (32 or 64); STAGES: LDS ring depth.
-template <int MODE, int ACT, int BKD, int STAGES>
+// BKD: K per stage (32 or 64); RA: LDS slots of the weight operand (2 or 3).
+template <int MODE, int ACT, int BKD, int RA>
 __global__ __launch_bounds__(kDmaThreads, 1) void k_gemm_dma(GemmParams p) {
   constexpr int NW = kDmaWaves;
   constexpr int CH = BKD / 8;              // 16-byte chunks per LDS row
   constexpr int RPB = 64 / CH;             // rows per 1-KB load block
   constexpr int BLK = 256 / RPB;           // blocks per operand per stage
   constexpr int NH = BLK / NW;             // blocks per operand per wave
-  constexpr int PER = 2 * NH;              // loads per wave per stage
   constexpr int S = BKD / 16;              // k-steps of 16 per stage
   constexpr int WTR = kDmaBT / (NW / 2);   // routes per wave
   constexpr int NJ = WTR / 32;             // 32-wide route blocks per wave
   constexpr int REGION = 256 * BKD * 2;    // bytes of A (and of B) per stage
-  constexpr int STAGE = 2 * REGION;
-  static_assert(S % 2 == 0 && BLK % NW == 0 && 3 * PER <= 63, "tile shape");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE];
+  static_assert(S % 2 == 0 && BLK % NW == 0 && 3 * NH <= 63, "tile shape");
+  static_assert((RA == 2 || RA == 3) && kDmaSlotsB == 2, "the issue order below");
+  // slots 0..RA-1: weight operand; RA, RA+1: route operand
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[(RA + kDmaSlotsB) * REGION];
   const uint32_t lds0 =
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
 
@@ -141,6 +141,8 @@ __global__ __launch_bounds__(kDmaThreads, 1) void k_gemm_dma(GemmParams p) {
   if (n0 >= Nw) return;
 
   // ---- load sources: wave w fills blocks w, w+NW, ... of A and of B -----------
+  const bool packed = p.pk != nullptr;  // the host passes both or neither
+  const int nk = K / BKD;
   const uint8_t* a_base[NH];
   uint32_t a_off[NH], b_off[NH];
 #pragma unroll
@@ -148,18 +150,27 @@ __global__ __launch_bounds__(kDmaThreads, 1) void k_gemm_dma(GemmParams p) {
     const int blk = wave + NW * h;
     const int row = blk * RPB + lane / CH;
     const int c = dma_slot<CH>(row, lane % CH);  // the XOR is its own inverse
-    const uint16_t* m;
-    int wr;
-    if constexpr (MODE == GM_GATEUP) {  // first half of the blocks: gate rows, then up
-      m = blk < BLK / 2 ? (shared ? p.sw0 : p.w0) : (shared ? p.sw1 : p.w1);
-      wr = min(n0 + (row & 127), Nw - 1);  // clamped rows are never stored
+    if (packed) {
+      static_assert(BKD == kDmaBK, "packed blocks hold K-steps of kDmaBK");
+      // tiles of this expert: 128 features (gate/up) or 256 outputs (down)
+      const int nwt = (MODE == GM_GATEUP) ? (Nw + 127) / 128 : (Nw + 255) / 256;
+      a_base[h] = uniform_ptr(shared ? p.spk : p.pk + (size_t)g * nwt * nk * kPackBlock);
+      a_off[h] = (uint32_t)(nt * nk) * (uint32_t)kPackBlock + (uint32_t)blk * 1024u +
+                 (uint32_t)lane * 16u;
     } else {
-      m = shared ? p.sw0 : p.w0;
-      wr = min(n0 + row, Nw - 1);
+      const uint16_t* m;
+      int wr;
+      if constexpr (MODE == GM_GATEUP) {  // first half of the blocks: gate rows, then up
+        m = blk < BLK / 2 ? (shared ? p.sw0 : p.w0) : (shared ? p.sw1 : p.w1);
+        wr = min(n0 + (row & 127), Nw - 1);  // clamped rows are never stored
+      } else {
+        m = shared ? p.sw0 : p.w0;
+        wr = min(n0 + row, Nw - 1);
+      }
+      a_base[h] = reinterpret_cast<const uint8_t*>(
+          uniform_ptr(m + (shared ? (size_t)0 : (size_t)g * Nw * K)));
+      a_off[h] = (uint32_t)wr * (uint32_t)K * 2u + (uint32_t)c * 16u;
     }
-    a_base[h] = reinterpret_cast<const uint8_t*>(
-        uniform_ptr(m + (shared ? (size_t)0 : (size_t)g * Nw * K)));
-    a_off[h] = (uint32_t)wr * (uint32_t)K * 2u + (uint32_t)c * 16u;
     const int rm = min(m0 + row, count - 1);  // clamped routes are never stored
     uint32_t br;
     if constexpr (MODE == GM_DOWN) br = (uint32_t)(shared ? rm : base + rm);
@@ -169,14 +180,18 @@ __global__ __launch_bounds__(kDmaThreads, 1) void k_gemm_dma(GemmParams p) {
   const uint8_t* b_base = reinterpret_cast<const uint8_t*>(
       uniform_ptr((MODE == GM_DOWN && shared) ? p.sact : p.act));
 
-  auto issue = [&](int kt, int st) {
-    const uint32_t sb = lds0 + (uint32_t)(st * STAGE);
+  const size_t a_step = packed ? (size_t)kPackBlock : (size_t)BKD * 2;  // bytes per K-step
+  auto issue_a = [&](int kt, int slot) {
+    const uint32_t sb = lds0 + (uint32_t)(slot * REGION);
+    const size_t koa = (size_t)kt * a_step;
+#pragma unroll
+    for (int h = 0; h < NH; ++h) lds_dma16(a_off[h], a_base[h] + koa, sb + (wave + NW * h) * 1024);
+  };
+  auto issue_b = [&](int kt, int slot) {
+    const uint32_t sb = lds0 + (uint32_t)((RA + slot) * REGION);
     const size_t ko = (size_t)kt * BKD * 2;
 #pragma unroll
-    for (int h = 0; h < NH; ++h) lds_dma16(a_off[h], a_base[h] + ko, sb + (wave + NW * h) * 1024);
-#pragma unroll
-    for (int h = 0; h < NH; ++h)
-      lds_dma16(b_off[h], b_base + ko, sb + REGION + (wave + NW * h) * 1024);
+    for (int h = 0; h < NH; ++h) lds_dma16(b_off[h], b_base + ko, sb + (wave + NW * h) * 1024);
   };
 
   // ---- wave sub-tile: 128 weight rows x WTR routes ----------------------------
@@ -206,24 +221,31 @@ __global__ __launch_bounds__(kDmaThreads, 1) void k_gemm_dma(GemmParams p) {
   const int fr = lane & 31, fk = lane >> 5;
 
   // ---- pipeline ---------------------------------------------------------------
-  // Iteration kt: for each k-step of tile kt, read the next k-step's fragments
-  // while multiplying the current ones; before the last k-step, wait for tile
-  // kt+1 and synchronise (after which nobody reads stage kt any more), refill
-  // that stage with tile kt+STAGES, and read the first fragments of tile
-  // kt+1 while the last k-step of tile kt is multiplied.  Fragment reads
-  // always overlap multiplies, and the barrier sits between two runs of
-  // multiplies.  The last tile is peeled off: a branch inside the loop body
-  // would make the wait-count pass merge two paths and wait for the
-  // prefetched reads.  NA (the wave's non-empty route blocks) is a template
-  // constant so that no branch sits between the reads and the multiplies.
-  const int nk = K / BKD;
+  // The route operand (gathered rows) runs one K-step ahead; the weight
+  // operand RA-1 steps: with RA = 3 (3 + 2 slots of 32 KB, the whole 160 KB
+  // of LDS) for weights streamed from HBM once, whose latency one step of
+  // multiplies does not cover.  Issue order: A0 B0 A1 B1 [A2], then after the
+  // barrier of iteration kt: B(kt+2) into kt's route slot, A(kt+RA) into kt's
+  // weight slot.  So when iteration kt waits for step kt+1, the loads issued
+  // after B(kt+1) are A(kt+2)'s if RA = 3 and none if RA = 2: wait until
+  // (RA-2)*NH (per wave) remain.
+  // Iteration kt: for each k-step of step kt, read the next k-step's
+  // fragments while multiplying the current ones; before the last k-step,
+  // wait for step kt+1 and synchronise (after which nobody reads kt's slots
+  // any more), refill them, and read the first fragments of step kt+1 while
+  // the last k-step of kt is multiplied.  Fragment reads always overlap
+  // multiplies, and the barrier sits between two runs of multiplies.  The
+  // last step is peeled off: a branch inside the loop body would make the
+  // wait-count pass merge two paths and wait for the prefetched reads.  NA
+  // (the wave's non-empty route blocks) is a template constant so that no
+  // branch sits between the reads and the multiplies.
   auto pipeline = [&](auto na_c) {
     constexpr int NA = decltype(na_c)::value;
-    // Fragments of k-step s (16 deep) of the tile in stage st.
-    auto frag = [&](int st, int s, bf16x8 (&af)[4], bf16x8 (&bfr)[NJ]) {
+    // Fragments of k-step s (16 deep) from weight slot sa and route slot sb.
+    auto frag = [&](int sa, int sb, int s, bf16x8 (&af)[4], bf16x8 (&bfr)[NJ]) {
       if constexpr (NA > 0) {
-        const uint16_t* sA = reinterpret_cast<const uint16_t*>(smem + st * STAGE);
-        const uint16_t* sB = reinterpret_cast<const uint16_t*>(smem + st * STAGE + REGION);
+        const uint16_t* sA = reinterpret_cast<const uint16_t*>(smem + sa * REGION);
+        const uint16_t* sB = reinterpret_cast<const uint16_t*>(smem + (RA + sb) * REGION);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = arow[i] + fr;
@@ -245,31 +267,41 @@ __global__ __launch_bounds__(kDmaThreads, 1) void k_gemm_dma(GemmParams p) {
         for (int i = 0; i < 4; ++i)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     };
-#pragma unroll
-    for (int t = 0; t < STAGES; ++t)
-      if (t < nk) issue(t, t);
-    wait_tiles<PER>(min(nk - 1, STAGES - 1));
+    issue_a(0, 0);
+    issue_b(0, 0);
+    if (nk > 1) {
+      issue_a(1, 1);
+      issue_b(1, 1);
+    }
+    if (RA == 3 && nk > 2) issue_a(2, 2);
+    if (RA == 3 && nk > 2) wait_vmem<3 * NH>();  // A1 B1 A2 may stay in flight
+    else if (nk > 1) wait_vmem<2 * NH>();
+    else wait_vmem<0>();
     __syncthreads();
     bf16x8 fa[2][4], fb[2][NJ];
-    frag(0, 0, fa[0], fb[0]);
+    frag(0, 0, 0, fa[0], fb[0]);
+    int sa = 0;  // weight slot of step kt
     for (int kt = 0; kt + 1 < nk; ++kt) {
-      const int st = kt % STAGES;
+      const int sb = kt & 1;
 #pragma unroll
       for (int s = 1; s < S; ++s) {
-        frag(st, s, fa[s & 1], fb[s & 1]);
+        frag(sa, sb, s, fa[s & 1], fb[s & 1]);
         mma(fa[(s - 1) & 1], fb[(s - 1) & 1]);
       }
-      wait_tiles<PER>(min(nk - 2 - kt, STAGES - 2));
+      if (RA == 3 && kt + 2 < nk) wait_vmem<NH>();  // A(kt+2) may stay in flight
+      else wait_vmem<0>();
       __syncthreads();
-      if (kt + STAGES < nk) issue(kt + STAGES, st);
-      frag((kt + 1) % STAGES, 0, fa[0], fb[0]);
+      if (kt + 2 < nk) issue_b(kt + 2, sb);
+      if (kt + RA < nk) issue_a(kt + RA, sa);
+      sa = sa == RA - 1 ? 0 : sa + 1;
+      frag(sa, sb ^ 1, 0, fa[0], fb[0]);
       mma(fa[1], fb[1]);
     }
     {
-      const int st = (nk - 1) % STAGES;
+      const int sb = (nk - 1) & 1;
 #pragma unroll
       for (int s = 1; s < S; ++s) {
-        frag(st, s, fa[s & 1], fb[s & 1]);
+        frag(sa, sb, s, fa[s & 1], fb[s & 1]);
         mma(fa[(s - 1) & 1], fb[(s - 1) & 1]);
       }
       mma(fa[1], fb[1]);
@@ -322,6 +354,44 @@ __global__ __launch_bounds__(kDmaThreads, 1) void k_gemm_dma(GemmParams p) {
           }
         }
     }
+  }
+}
+
+// Weight packing for the kernel above.  Block (t, s) of an expert holds
+// weight tile t at K-step s as 256 rows of 128 bytes: for gate/up, rows
+// 0-127 are gate features 128t + r and rows 128-255 the up features
+// 128t + r - 128; for down, row r is output 256t + r.  Row r's 16-byte chunk
+// c (K elements 64s + 8c .. 64s + 8c + 7) sits in slot dma_slot<8>(r, c) of
+// the row, so the block is byte for byte what the kernel's stage holds.  Rows
+// past the matrix are zero.  Blocks of an expert are ordered t-major
+// (t * K/64 + s) and experts follow one another.  One workgroup per block:
+// blockIdx.x = t * K/64 + s, blockIdx.y = expert.
+template <int MODE>
+__global__ __launch_bounds__(256) void k_pack(const uint16_t* __restrict__ w0,
+                                              const uint16_t* __restrict__ w1,
+                                              uint8_t* __restrict__ dst, int Nw, int K, int nwt) {
+  const int ks = K / kDmaBK;
+  const int t = blockIdx.x / ks, s = blockIdx.x - t * ks;
+  const size_t src0 = (size_t)blockIdx.y * Nw * K + (size_t)s * kDmaBK;
+  uint8_t* db = dst + ((size_t)blockIdx.y * nwt * ks + blockIdx.x) * kPackBlock;
+  constexpr int CH = kDmaBK / 8;  // 16-byte chunks per row
+#pragma unroll
+  for (int i = 0; i < kPackBlock / 16 / 256; ++i) {
+    const int q = threadIdx.x + 256 * i;  // destination chunk
+    const int r = q / CH;
+    const int c = dma_slot<CH>(r, q % CH);  // the XOR is its own inverse
+    int f;
+    const uint16_t* m;
+    if constexpr (MODE == GM_GATEUP) {
+      f = 128 * t + (r & 127);
+      m = r < 128 ? w0 : w1;
+    } else {
+      f = 256 * t + r;
+      m = w0;
+    }
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (f < Nw) v = *reinterpret_cast<const u32x4*>(m + src0 + (size_t)f * K + 8 * c);
+    *reinterpret_cast<u32x4*>(db + (size_t)q * 16) = v;
   }
 }
 

@@ -53,6 +53,7 @@ struct Plan {
   int E = 0, k = 0, H = 0, I = 0, Is = 0, G = 0, ncols = 0;
   bool shared = false;
   bool mfma = false;       // prefill path (bf16 MFMA grouped GEMM)
+  int ra = 2;              // direct-to-LDS GEMM: LDS slots of the weight operand
   bool small = false;      // decode path (T <= 32, GEMV kernels, one-workgroup routing)
   int rc = 0;              // decode: routes staged in LDS per pass
   int nblk = 0;            // permutation blocks
@@ -146,6 +147,11 @@ Plan make_plan(const moe_desc* d, int64_t T) {
     const bool fits = (uint64_t)T * p.H * 2 < lim && (uint64_t)p.R * maxI * 2 < lim &&
                       maxI * p.H * 2 < lim;
     if (fits) p.bt = kDmaBT;
+    // Fewer routes per expert than one route tile holds: each weight byte is
+    // fetched from HBM about once, and the weight operand runs two K-steps
+    // ahead.  More: weights and routes both come largely from L2, and the
+    // weight operand keeps the route operand's one step.
+    p.ra = p.R < (int64_t)kDmaBT * p.E ? 3 : 2;
   }
   p.max_tiles = (int)((p.R + p.bt - 1) / p.bt) + p.E + (p.shared ? (int)((T + p.bt - 1) / p.bt) : 0);
   p.max_groups = (int)std::min<int64_t>(p.E, p.R) + (p.shared ? 1 : 0);
@@ -650,13 +656,20 @@ moe_status run_experts_mfma(const moe_desc* d, const Plan& p, const void* x,
   gu.act = static_cast<const uint16_t*>(x);
   gu.out = wsp<uint16_t>(ws, p.o_h);
   gu.sout = wsp<uint16_t>(ws, p.o_hs);
+  if (p.bt == kDmaBT && w->gate_up_packed) {
+    gu.pk = static_cast<const uint8_t*>(w->gate_up_packed);
+    gu.spk = static_cast<const uint8_t*>(w->shared_gate_up_packed);
+  }
   const int maxN = std::max(p.I, p.Is);
   dim3 g1(p.max_tiles, (maxN + kBW / 2 - 1) / (kBW / 2));
   MOE_TRY(launch("gemm_gateup", s, [&] {
     const bool silu = d->activation == MOE_ACT_SILU;
-    if (p.bt == kDmaBT) {
-      if (silu) k_gemm_dma<GM_GATEUP, ACT_SILU, kDmaBK, kDmaRing><<<g1, kDmaThreads, 0, s>>>(gu);
-      else k_gemm_dma<GM_GATEUP, ACT_GELU_TANH, kDmaBK, kDmaRing><<<g1, kDmaThreads, 0, s>>>(gu);
+    if (p.bt == kDmaBT && p.ra == 3) {
+      if (silu) k_gemm_dma<GM_GATEUP, ACT_SILU, kDmaBK, 3><<<g1, kDmaThreads, 0, s>>>(gu);
+      else k_gemm_dma<GM_GATEUP, ACT_GELU_TANH, kDmaBK, 3><<<g1, kDmaThreads, 0, s>>>(gu);
+    } else if (p.bt == kDmaBT) {
+      if (silu) k_gemm_dma<GM_GATEUP, ACT_SILU, kDmaBK, 2><<<g1, kDmaThreads, 0, s>>>(gu);
+      else k_gemm_dma<GM_GATEUP, ACT_GELU_TANH, kDmaBK, 2><<<g1, kDmaThreads, 0, s>>>(gu);
     } else {
       if (silu) k_gemm_big<GM_GATEUP, ACT_SILU, 128><<<g1, 256, 0, s>>>(gu);
       else k_gemm_big<GM_GATEUP, ACT_GELU_TANH, 128><<<g1, 256, 0, s>>>(gu);
@@ -670,9 +683,14 @@ moe_status run_experts_mfma(const moe_desc* d, const Plan& p, const void* x,
   gd.sact = wsp<uint16_t>(ws, p.o_hs);
   gd.out = wsp<uint16_t>(ws, p.o_y);
   gd.sout = wsp<uint16_t>(ws, p.o_ys);
+  if (p.bt == kDmaBT && w->down_packed) {
+    gd.pk = static_cast<const uint8_t*>(w->down_packed);
+    gd.spk = static_cast<const uint8_t*>(w->shared_down_packed);
+  }
   dim3 g2(p.max_tiles, (p.H + kBW - 1) / kBW);
   MOE_TRY(launch("gemm_down", s, [&] {
-    if (p.bt == kDmaBT) k_gemm_dma<GM_DOWN, 0, kDmaBK, kDmaRing><<<g2, kDmaThreads, 0, s>>>(gd);
+    if (p.bt == kDmaBT && p.ra == 3) k_gemm_dma<GM_DOWN, 0, kDmaBK, 3><<<g2, kDmaThreads, 0, s>>>(gd);
+    else if (p.bt == kDmaBT) k_gemm_dma<GM_DOWN, 0, kDmaBK, 2><<<g2, kDmaThreads, 0, s>>>(gd);
     else k_gemm_big<GM_DOWN, 0, 128><<<g2, 256, 0, s>>>(gd);
   }));
 
@@ -700,6 +718,49 @@ moe_status layer_input(const moe_desc* d, const Plan& p, const void* x, const mo
       k_rmsnorm<float><<<(unsigned)p.T, 256, 0, s>>>(static_cast<const float*>(x),
           w->norm_weight, d->norm_eps, p.H, static_cast<float*>(xn));
   });
+}
+
+// Sizes of the packed weight arrays (the direct-to-LDS GEMM's layout).
+struct PackSizes {
+  size_t gu = 0, dn = 0, sgu = 0, sdn = 0;
+};
+
+moe_status pack_sizes(const moe_desc* d, PackSizes* o) {
+  MOE_TRY(check_desc(d));
+  if (d->weight_format != MOE_WEIGHTS_BF16)
+    return fail(MOE_UNSUPPORTED, "packed weights exist for bf16 weights only");
+  const int H = d->hidden, I = d->intermediate;
+  const int Is = d->has_shared_expert ? d->shared_intermediate : 0;
+  if (H % kDmaBK || I % kDmaBK || Is % kDmaBK)
+    return fail(MOE_UNSUPPORTED, "packed weights need hidden and intermediate sizes that are "
+                "multiples of %d", kDmaBK);
+  auto gu = [&](int n) { return (size_t)((n + 127) / 128) * (H / kDmaBK) * kPackBlock; };
+  auto dn = [&](int n) { return (size_t)((H + kPackRows - 1) / kPackRows) * (n / kDmaBK) * kPackBlock; };
+  const int n = std::max(I, Is);
+  if (gu(n) > UINT32_MAX || dn(n) > UINT32_MAX)
+    return fail(MOE_UNSUPPORTED, "one expert's packed weights exceed 4 GiB");
+  o->gu = (size_t)d->num_experts * gu(I);
+  o->dn = (size_t)d->num_experts * dn(I);
+  if (Is) {
+    o->sgu = gu(Is);
+    o->sdn = dn(Is);
+  }
+  return MOE_OK;
+}
+
+moe_status check_packed(const moe_desc* d, const moe_weights* w) {
+  const void* pp[4] = {w->gate_up_packed, w->down_packed, w->shared_gate_up_packed,
+                       w->shared_down_packed};
+  if (!pp[0] && !pp[1] && !pp[2] && !pp[3]) return MOE_OK;
+  PackSizes ps;
+  MOE_TRY(pack_sizes(d, &ps));
+  for (const void* q : pp)
+    if (!aligned16(q)) return fail(MOE_UNSUPPORTED, "packed weights must be 16-byte aligned");
+  if (d->has_shared_expert && ((!pp[0] != !pp[2]) || (!pp[1] != !pp[3])))
+    return fail(MOE_INVALID_ARGUMENT, "routed and shared packed weights go together");
+  if (!d->has_shared_expert && (pp[2] || pp[3]))
+    return fail(MOE_INVALID_ARGUMENT, "shared packed weights given without a shared expert");
+  return MOE_OK;
 }
 
 moe_status check_common(const moe_desc* d, int64_t T, const void* x, const moe_weights* w,
@@ -736,6 +797,7 @@ moe_status check_common(const moe_desc* d, int64_t T, const void* x, const moe_w
         return fail(MOE_UNSUPPORTED, "shared expert weights must be 16-byte aligned");
     }
   }
+  if (full) MOE_TRY(check_packed(d, w));
   if (d->pre_norm && (!w->norm_weight || !aligned16(w->norm_weight)))
     return fail(w->norm_weight ? MOE_UNSUPPORTED : MOE_INVALID_ARGUMENT,
                 "pre_norm needs weights->norm_weight, 16-byte aligned");
@@ -810,6 +872,67 @@ moe_status moe_ffn_forward(const moe_desc* desc, int64_t num_tokens, const void*
   MOE_TRY(run_route_and_group(desc, p, ws, topk_ids_out, topk_w_out, nullptr, nullptr, nullptr, s));
   if (p.mfma) return run_experts_mfma(desc, p, x, weights, out, residual, ws, s);
   return run_experts_gemv(desc, p, x, weights, out, residual, ws, s);
+}
+
+moe_status moe_packed_weight_bytes(const moe_desc* desc, size_t* gate_up_bytes,
+                                   size_t* down_bytes, size_t* shared_gate_up_bytes,
+                                   size_t* shared_down_bytes) {
+  g_err.clear();
+  PackSizes ps;
+  MOE_TRY(pack_sizes(desc, &ps));
+  if (gate_up_bytes) *gate_up_bytes = ps.gu;
+  if (down_bytes) *down_bytes = ps.dn;
+  if (shared_gate_up_bytes) *shared_gate_up_bytes = ps.sgu;
+  if (shared_down_bytes) *shared_down_bytes = ps.sdn;
+  return MOE_OK;
+}
+
+moe_status moe_pack_weights(const moe_desc* desc, const moe_weights* w, void* gate_up_packed,
+                            void* down_packed, void* shared_gate_up_packed,
+                            void* shared_down_packed, void* stream) {
+  g_err.clear();
+  PackSizes ps;
+  MOE_TRY(pack_sizes(desc, &ps));
+  if (!w) return fail(MOE_INVALID_ARGUMENT, "weights is NULL");
+  const bool sh = desc->has_shared_expert != 0;
+  const void* src[6] = {w->gate, w->up, w->down, sh ? w->shared_gate : w->gate,
+                        sh ? w->shared_up : w->gate, sh ? w->shared_down : w->gate};
+  void* dst[4] = {gate_up_packed, down_packed, sh ? shared_gate_up_packed : gate_up_packed,
+                  sh ? shared_down_packed : gate_up_packed};
+  for (const void* q : src)
+    if (!q) return fail(MOE_INVALID_ARGUMENT, "a weight matrix to pack is NULL");
+  for (void* q : dst)
+    if (!q) return fail(MOE_INVALID_ARGUMENT, "a packed destination is NULL");
+  for (const void* q : src)
+    if (!aligned16(q)) return fail(MOE_UNSUPPORTED, "weights must be 16-byte aligned");
+  for (void* q : dst)
+    if (!aligned16(q)) return fail(MOE_UNSUPPORTED, "packed destinations must be 16-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int H = desc->hidden, E = desc->num_experts;
+  auto pack_gu = [&](const void* g, const void* u, void* o, int n, int ne) {
+    const int nwt = (n + 127) / 128;
+    dim3 grid(nwt * (H / kDmaBK), ne);
+    return launch("pack_gate_up", s, [&] {
+      k_pack<GM_GATEUP><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(g),
+          static_cast<const uint16_t*>(u), static_cast<uint8_t*>(o), n, H, nwt);
+    });
+  };
+  auto pack_dn = [&](const void* dn, void* o, int n, int ne) {
+    const int nwt = (H + kPackRows - 1) / kPackRows;
+    dim3 grid(nwt * (n / kDmaBK), ne);
+    return launch("pack_down", s, [&] {
+      k_pack<GM_DOWN><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(dn), nullptr,
+          static_cast<uint8_t*>(o), H, n, nwt);
+    });
+  };
+  MOE_TRY(pack_gu(w->gate, w->up, gate_up_packed, desc->intermediate, E));
+  MOE_TRY(pack_dn(w->down, down_packed, desc->intermediate, E));
+  if (sh) {
+    MOE_TRY(pack_gu(w->shared_gate, w->shared_up, shared_gate_up_packed,
+                    desc->shared_intermediate, 1));
+    MOE_TRY(pack_dn(w->shared_down, shared_down_packed, desc->shared_intermediate, 1));
+  }
+  return MOE_OK;
 }
 
 moe_status moe_weighted_sum_backward(int64_t num_tokens, int32_t top_k, int32_t hidden,

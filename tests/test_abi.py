@@ -35,7 +35,7 @@ def test_header_declares_the_bound_functions():
 def test_library_exports_every_declared_symbol(lib):
     for name in _declared_functions():
         assert hasattr(lib, name), name
-    assert lib.moe_abi_version() == 5
+    assert lib.moe_abi_version() == 6
 
 
 def _desc(name="decode_geglu_t1", **over):
@@ -138,3 +138,79 @@ def test_pre_norm_needs_positive_eps_and_weight(lib):
     st = lib.moe_ffn_forward(ctypes.byref(d), 1, fake, ctypes.byref(w), fake, None, None, None,
                              fake, 1 << 30, None)
     assert st == M.MOE_INVALID_ARGUMENT and "norm_weight" in lib.moe_last_error().decode()
+
+
+def _packed_sizes_from_definition(H, I, E, Is):
+    """Block counts of the packed layout the header defines: gate/up tiles of
+    128 features and down tiles of 256 outputs, K-steps of 64, 32 KB blocks."""
+    blk = 256 * 64 * 2
+    gu = lambda n: -(-n // 128) * (H // 64) * blk
+    dn = lambda n: -(-H // 256) * (n // 64) * blk
+    return E * gu(I), E * dn(I), gu(Is) if Is else 0, dn(Is) if Is else 0
+
+
+@pytest.mark.parametrize("H,I,E,Is", [(2048, 512, 256, 512), (7168, 2048, 256, 2048),
+                                      (192, 64, 3, 192), (320, 192, 5, 0)])
+def test_packed_weight_bytes(lib, H, I, E, Is):
+    d = M.make_desc(hidden=H, intermediate=I, num_experts=E, top_k=2, weight_format=M.WEIGHTS_BF16,
+                    act_dtype=M.DT_BF16, router_dtype=M.DT_BF16, shared_intermediate=Is)
+    got = M.packed_weight_bytes(d)
+    assert got == _packed_sizes_from_definition(H, I, E, Is)
+    if I % 128 == 0:   # whole tiles: the same bytes as the row-major matrices
+        assert got[0] == E * 2 * I * H * 2 and got[1] == E * H * I * 2 * (-(-H // 256) * 256) // H
+
+
+@pytest.mark.parametrize("over", [dict(weight_format=M.WEIGHTS_F32, act_dtype=M.DT_F32),
+                                  dict(intermediate=96), dict(shared_intermediate=160)])
+def test_packed_weights_unsupported(lib, over):
+    kw = dict(hidden=256, intermediate=128, num_experts=4, top_k=2, weight_format=M.WEIGHTS_BF16,
+              act_dtype=M.DT_BF16, router_dtype=M.DT_BF16)
+    kw.update(over)
+    d = M.make_desc(**kw)
+    n = ctypes.c_size_t(0)
+    assert lib.moe_packed_weight_bytes(ctypes.byref(d), ctypes.byref(n), None, None,
+                                       None) == M.MOE_UNSUPPORTED
+    w = M.make_weights(router=None)
+    fake = 1 << 20
+    assert lib.moe_pack_weights(ctypes.byref(d), ctypes.byref(w), fake, fake, fake, fake,
+                                None) == M.MOE_UNSUPPORTED
+
+
+def test_pack_weights_rejects_null_and_misaligned_on_host(lib):
+    d = _desc("prefill_shared_t4096")
+    fake = 1 << 20
+    w = M.make_weights(router=None)
+    assert lib.moe_pack_weights(ctypes.byref(d), None, fake, fake, fake, fake,
+                                None) == M.MOE_INVALID_ARGUMENT
+    w.gate, w.up, w.down = fake, fake, fake          # shared expert's matrices missing
+    assert lib.moe_pack_weights(ctypes.byref(d), ctypes.byref(w), fake, fake, fake, fake,
+                                None) == M.MOE_INVALID_ARGUMENT
+    w.shared_gate, w.shared_up, w.shared_down = fake, fake, fake
+    assert lib.moe_pack_weights(ctypes.byref(d), ctypes.byref(w), fake, fake, fake, None,
+                                None) == M.MOE_INVALID_ARGUMENT
+    assert lib.moe_pack_weights(ctypes.byref(d), ctypes.byref(w), fake, fake + 8, fake, fake,
+                                None) == M.MOE_UNSUPPORTED
+
+
+def test_forward_rejects_unpaired_packed_weights_on_host(lib):
+    d = _desc("prefill_shared_t4096")
+    fake = 1 << 20
+    w = M.make_weights(router=None)
+    w.router, w.gate, w.up, w.down = fake, fake, fake, fake
+    w.shared_gate_inp, w.shared_gate, w.shared_up, w.shared_down = fake, fake, fake, fake
+    w.gate_up_packed = fake                          # routed without shared
+    st = lib.moe_ffn_forward(ctypes.byref(d), 4096, fake, ctypes.byref(w), fake, None, None, None,
+                             fake, 1 << 40, None)
+    assert st == M.MOE_INVALID_ARGUMENT and "packed" in lib.moe_last_error().decode()
+    w.shared_gate_up_packed = fake + 4               # misaligned
+    st = lib.moe_ffn_forward(ctypes.byref(d), 4096, fake, ctypes.byref(w), fake, None, None, None,
+                             fake, 1 << 40, None)
+    assert st == M.MOE_UNSUPPORTED
+    dd = _desc("decode_u4_t32")                      # no packed layout for 4-bit weights
+    w2 = M.make_weights(router=None)
+    w2.router, w2.down_packed = fake, fake
+    for name in ("gate_u4", "up_u4", "down_u4"):
+        setattr(w2, name, M.U4Matrix(fake, fake, fake))
+    st = lib.moe_ffn_forward(ctypes.byref(dd), 1, fake, ctypes.byref(w2), fake, None, None, None,
+                             fake, 1 << 40, None)
+    assert st == M.MOE_UNSUPPORTED

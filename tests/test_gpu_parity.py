@@ -57,6 +57,13 @@ SMALL = [
     MoeConfig(name="mfma_dma_gelu_bias", T=1100, H=128, I=320, E=2, k=1, act=ACT_GELU_TANH,
               weight_format=WF_BF16, act_dtype=DT_BF16, router_dtype=DT_BF16, bias=BIAS_ZIPF,
               seed_index=31),
+    # direct-to-LDS tiles with fewer routes per expert than a tile holds (the
+    # weight operand three K-steps deep); K walks of 1 to 4 steps
+    MoeConfig(name="mfma_dma_deep_shared", T=800, H=256, I=192, E=8, k=2, weight_format=WF_BF16,
+              act_dtype=DT_BF16, router_dtype=DT_BF16, shared=True, Is=64, seed_index=67),
+    MoeConfig(name="mfma_dma_deep_short", T=900, H=128, I=64, E=8, k=2, act=ACT_GELU_TANH,
+              weight_format=WF_BF16, act_dtype=DT_BF16, router_dtype=DT_BF16, bias=BIAS_ZIPF,
+              seed_index=68),
     # longer K walk (20 steps of 64) and 41 logit columns: ragged router tile
     MoeConfig(name="mfma_router_long_k", T=333, H=1280, I=64, E=40, k=3, weight_format=WF_BF16,
               act_dtype=DT_BF16, router_dtype=DT_BF16, bias=BIAS_ZIPF, shared=True, Is=64,
