@@ -315,13 +315,15 @@ __global__ __launch_bounds__(kDmaThreads, 1) void k_gemm_dma(GemmParams p) {
   // ---- epilogue: acc[i][j][4q + v] = weight row arow[i] + 8q + 4*(lane>>5) + v,
   //      route brow0 + 32 j + (lane & 31) -----------------------------------------
   const int rsub = 4 * (lane >> 5);
+  if constexpr (MODE == GM_GATEUP) {
+    // h = act(gate) * up straight from the accumulators: 8 bytes per route row
+    // and store (staging through LDS, as below, measured slower for h)
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    const int m = m0 + brow0 + 32 * j + (lane & 31);
-    if (m >= count) continue;
-    uint16_t* outp = shared ? reinterpret_cast<uint16_t*>(p.sout) + (size_t)m * Nw
-                            : reinterpret_cast<uint16_t*>(p.out) + (size_t)(base + m) * Nw;
-    if constexpr (MODE == GM_GATEUP) {
+    for (int j = 0; j < NJ; ++j) {
+      const int m = m0 + brow0 + 32 * j + (lane & 31);
+      if (m >= count) continue;
+      uint16_t* outp = shared ? reinterpret_cast<uint16_t*>(p.sout) + (size_t)m * Nw
+                              : reinterpret_cast<uint16_t*>(p.out) + (size_t)(base + m) * Nw;
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -340,19 +342,53 @@ __global__ __launch_bounds__(kDmaThreads, 1) void k_gemm_dma(GemmParams p) {
             *reinterpret_cast<u32x2*>(outp + f) = pk;
           }
         }
-    } else {
+    }
+  } else {
+    // y passes through LDS (route-major rows of 128 outputs, padded to 272
+    // bytes so that the 32 routes one write covers fall on distinct banks)
+    // and leaves as 16-byte stores, 16 lanes covering 256 contiguous bytes of
+    // a row, instead of 8 bytes in each of 32 rows per store instruction.
+    constexpr int ROWB = 128 * 2 + 16;
+    static_assert(256 * ROWB <= (RA + kDmaSlotsB) * REGION, "staging fits the operand slots");
+    auto stage8 = [&](int row, int col, float a, float b, float c, float d) {
+      u32x2 pk;
+      pk[0] = pack_bf16x2(a, b);
+      pk[1] = pack_bf16x2(c, d);
+      *reinterpret_cast<u32x2*>(smem + row * ROWB + col * 2) = pk;
+    };
+    // staged rows (routes m0 ..) x 128 values -> output columns n0 + colbase + 0..127
+    auto flush = [&](int colbase) {
+      __syncthreads();
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int n = n0 + arow[i] + 8 * q + rsub;
-          if (n < Nw) {
-            u32x2 pk;
-            pk[0] = pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
-            pk[1] = pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-            *reinterpret_cast<u32x2*>(outp + n) = pk;
-          }
+      for (int u = 0; u < 256 * 16 / kDmaThreads; ++u) {
+        const int ch = tid + kDmaThreads * u;
+        const int row = ch >> 4, cc = ch & 15;
+        const int m = m0 + row;
+        const int n = n0 + colbase + 8 * cc;
+        if (m < count && n < Nw) {
+          uint16_t* outp = shared ? reinterpret_cast<uint16_t*>(p.sout) + (size_t)m * Nw
+                                  : reinterpret_cast<uint16_t*>(p.out) + (size_t)(base + m) * Nw;
+          *reinterpret_cast<u32x4*>(outp + n) =
+              *reinterpret_cast<const u32x4*>(smem + row * ROWB + cc * 16);
         }
+      }
+    };
+    __syncthreads();  // every wave is done with the operand slots
+    // two passes of 128 outputs: pass h stages the waves with ww == h
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (h == 1) __syncthreads();  // pass 0's rows have been read out
+      if (ww == h) {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              stage8(brow0 + 32 * j + (lane & 31), 32 * i + 8 * q + rsub, acc[i][j][4 * q],
+                     acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+      }
+      flush(128 * h);
     }
   }
 }
