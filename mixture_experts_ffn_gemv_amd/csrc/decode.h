@@ -433,14 +433,31 @@ __device__ __forceinline__ void decode_chunk(const u32x4& v, float s, float mn,
 }
 
 // Load chunk c of a row (16 bytes) plus, for 4-bit rows, its group's scale/min.
-template <int WF>
+// `row` must be a row of m (callers clamp).  BRANCHLESS: lanes past the
+// row's end re-read its last chunk (a line their neighbours fetch anyway)
+// and keep zeros where !ok, so the loads carry no branch and a wave's loads
+// issue back to back (faster for the gate/up rows; the down kernel, whose
+// last chunks are mostly past the row, does better skipping them).
+template <int WF, bool BRANCHLESS = false>
 __device__ __forceinline__ void load_chunk(const MatStack& m, size_t row, int K, int c, bool ok,
                                            u32x4& v, float& s, float& mn) {
-  v = ok ? ld16_stream(row_ptr<WF>(m, row, K) + (size_t)c * 16) : u32x4{0, 0, 0, 0};
+  const int cc = BRANCHLESS ? min(c, K / WTraits<WF>::EPC - 1) : c;
+  if constexpr (BRANCHLESS) {
+    const u32x4 t = ld16_stream(row_ptr<WF>(m, row, K) + (size_t)cc * 16);
+    v = ok ? t : u32x4{0, 0, 0, 0};
+  } else {
+    v = ok ? ld16_stream(row_ptr<WF>(m, row, K) + (size_t)cc * 16) : u32x4{0, 0, 0, 0};
+  }
   if constexpr (WF == WF_U4) {
-    const size_t gi = row * (K / 32) + c;
-    s = ok ? f16_to_f32(m.sc[gi]) : 0.f;
-    mn = ok ? f16_to_f32(m.mn[gi]) : 0.f;
+    const size_t gi = row * (K / 32) + cc;
+    if constexpr (BRANCHLESS) {
+      const float ts = f16_to_f32(m.sc[gi]), tm = f16_to_f32(m.mn[gi]);
+      s = ok ? ts : 0.f;
+      mn = ok ? tm : 0.f;
+    } else {
+      s = ok ? f16_to_f32(m.sc[gi]) : 0.f;
+      mn = ok ? f16_to_f32(m.mn[gi]) : 0.f;
+    }
   } else {
     s = 0.f;
     mn = 0.f;
@@ -492,9 +509,18 @@ __global__ __launch_bounds__(256) void k_dec_gateup3(Dec2Params p) {
   constexpr int EPC = WTraits<WF>::EPC;
   extern __shared__ float xs[];  // [rc][H] (staged path only)
   const int s = blockIdx.x;
-  if (s >= *p.n_active) return;
+  // The slot's expert is read together with the slot count (the active list
+  // has an entry for every slot of the grid), and the first K block's weight
+  // loads go out as soon as the expert is known: the route and token lookups
+  // follow while they are in flight.
+  const int na = *p.n_active;
+  const int slot_g = p.active[s];
+  // one round trip for both (and for the weight pointers), ahead of the exit test
+  asm volatile("" ::"s"(na), "s"(slot_g), "s"(p.gate.p), "s"(p.up.p), "s"(p.sgate.p),
+               "s"(p.sup.p));
+  if (s >= na) return;
   const int R = p.T * p.k;
-  const int g = ws_group(p.active[s], p.E, p.Is > 0);
+  const int g = ws_group(slot_g, p.E, p.Is > 0);
   const bool shared = (g == p.E);
   const int N = shared ? p.Is : p.I;
   const int fblk = blockIdx.y * kGUWaves;
@@ -505,15 +531,11 @@ __global__ __launch_bounds__(256) void k_dec_gateup3(Dec2Params p) {
   const int cpr = p.H / EPC;
   const MatStack& Mg = shared ? p.sgate : p.gate;
   const MatStack& Mu = shared ? p.sup : p.up;
-  const size_t row = shared ? (size_t)f : (size_t)g * N + f;
-
-  int count = shared ? p.T : p.counts[g];
-  int base = shared ? 0 : p.offsets[g];
-  if (!shared) ws_span(base, count, R);
+  const int fc = min(f, N - 1);  // waves past the last feature read a valid row, unused
+  const size_t row = shared ? (size_t)fc : (size_t)g * N + fc;
 
   if constexpr (DIRECT) {
-    const int r = shared ? 0 : ws_route(p.perm[base], R);
-    const int t = shared ? 0 : r / p.k;
+    int r = 0, t = 0;
     float ag = 0.f, au = 0.f;
     for (int kb = 0; kb < cpr; kb += 64 * U) {
       // all weight loads of this wave (for this K block) first
@@ -523,8 +545,14 @@ __global__ __launch_bounds__(256) void k_dec_gateup3(Dec2Params p) {
       for (int u = 0; u < U; ++u) {
         const int c = kb + lane + 64 * u;
         const bool ok = fok && c < cpr;
-        load_chunk<WF>(Mg, row, p.H, c, ok, wg[u], sg[u], mg[u]);
-        load_chunk<WF>(Mu, row, p.H, c, ok, wu[u], su[u], mu[u]);
+        load_chunk<WF, true>(Mg, row, p.H, c, ok, wg[u], sg[u], mg[u]);
+        load_chunk<WF, true>(Mu, row, p.H, c, ok, wu[u], su[u], mu[u]);
+      }
+      if (kb == 0 && !shared) {  // the expert's one route, and its token
+        int count = p.counts[g], base = p.offsets[g];
+        ws_span(base, count, R);
+        r = ws_route(p.perm[base], R);
+        t = r / p.k;
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -546,6 +574,9 @@ __global__ __launch_bounds__(256) void k_dec_gateup3(Dec2Params p) {
       else p.h[(size_t)r * N + f] = hv;
     }
   } else {
+    int count = shared ? p.T : p.counts[g];
+    int base = shared ? 0 : p.offsets[g];
+    if (!shared) ws_span(base, count, R);
     for (int r0 = 0; r0 < count; r0 += p.rc) {
       const int nr = min(p.rc, count - r0);
       float ag[kRCMax], au[kRCMax];
@@ -558,8 +589,8 @@ __global__ __launch_bounds__(256) void k_dec_gateup3(Dec2Params p) {
         for (int u = 0; u < U; ++u) {
           const int c = kb + lane + 64 * u;
           const bool ok = fok && c < cpr;
-          load_chunk<WF>(Mg, row, p.H, c, ok, wg[u], sg[u], mg[u]);
-          load_chunk<WF>(Mu, row, p.H, c, ok, wu[u], su[u], mu[u]);
+          load_chunk<WF, true>(Mg, row, p.H, c, ok, wg[u], sg[u], mg[u]);
+          load_chunk<WF, true>(Mu, row, p.H, c, ok, wu[u], su[u], mu[u]);
         }
         if (kb == 0) {
           // stage this pass's activations (after the weight loads are issued)
@@ -632,8 +663,7 @@ __global__ __launch_bounds__(256) void k_dec_down3(Dec2Params p) {
 
   u32x4 wc[RPW][U], wn[RPW][U];
   float sc[RPW][U], mc[RPW][U], sn[RPW][U], mnx[RPW][U];
-  auto load_group = [&](int s, u32x4 (&w)[RPW][U], float (&sv)[RPW][U], float (&mv)[RPW][U]) {
-    const int g = ws_group(p.active[s], p.E, p.Is > 0);
+  auto load_group = [&](int g, u32x4 (&w)[RPW][U], float (&sv)[RPW][U], float (&mv)[RPW][U]) {
     const bool shared = (g == p.E);
     const int K = shared ? p.Is : p.I;
     const int cpr = K / EPC;
@@ -644,17 +674,19 @@ __global__ __launch_bounds__(256) void k_dec_down3(Dec2Params p) {
 #pragma unroll
       for (int q = 0; q < RPW; ++q) {
         const int n = n0 + q;
-        const size_t row = shared ? (size_t)n : (size_t)g * p.H + n;
+        const int nc = min(n, p.H - 1);
+        const size_t row = shared ? (size_t)nc : (size_t)g * p.H + nc;
         load_chunk<WF>(M, row, K, c, n < p.H && c < cpr, w[q][u], sv[q][u], mv[q][u]);
       }
     }
   };
   int s = wave;
-  if (s < na) load_group(s, wc, sc, mc);
+  int g = s < na ? ws_group(p.active[s], p.E, p.Is > 0) : 0;
+  if (s < na) load_group(g, wc, sc, mc);
   while (s < na) {
     const int sn_ = s + 4;
-    if (sn_ < na) load_group(sn_, wn, sn, mnx);
-    const int g = ws_group(p.active[s], p.E, p.Is > 0);
+    const int gn = sn_ < na ? ws_group(p.active[sn_], p.E, p.Is > 0) : 0;
+    if (sn_ < na) load_group(gn, wn, sn, mnx);
     const bool shared = (g == p.E);
     const int K = shared ? p.Is : p.I;
     const int cpr = K / EPC;
@@ -695,6 +727,7 @@ __global__ __launch_bounds__(256) void k_dec_down3(Dec2Params p) {
 #pragma unroll
       for (int q = 0; q < RPW; ++q) { wc[q][u] = wn[q][u]; sc[q][u] = sn[q][u]; mc[q][u] = mnx[q][u]; }
     s = sn_;
+    g = gn;
   }
   __syncthreads();
   for (int i = tid; i < p.T * RPW; i += 256) {
