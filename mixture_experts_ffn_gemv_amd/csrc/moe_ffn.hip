@@ -261,15 +261,11 @@ moe_status run_router(const moe_desc* d, const Plan& p, const void* x, const moe
   float* logits = wsp<float>(ws, p.o_logits);
   const int T = (int)p.T;
   if (p.mfma) {
-    GemmParams g{};
-    g.w0 = static_cast<const uint16_t*>(w->router);
-    g.sw0 = static_cast<const uint16_t*>(w->shared_gate_inp);
-    g.bias = w->router_bias;
-    g.act = static_cast<const uint16_t*>(x);
-    g.out = logits;
-    g.E = p.E; g.T = T; g.H = p.H; g.I = p.I; g.Is = p.Is; g.ncols = p.ncols;
+    RouterParams rp{static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w->router),
+                    static_cast<const uint16_t*>(w->shared_gate_inp), w->router_bias, logits,
+                    T, p.H, p.E, p.ncols};
     dim3 grid((T + kTileT - 1) / kTileT, (p.ncols + kTileW - 1) / kTileW);
-    return launch("router_mfma", s, [&] { k_gemm<GM_ROUTER, 0><<<grid, 256, 0, s>>>(g); });
+    return launch("router_mfma", s, [&] { k_router_mfma<<<grid, 256, 0, s>>>(rp); });
   }
   const bool xb = d->act_dtype == MOE_BF16, rb = d->router_dtype == MOE_BF16;
   dim3 grid(p.ncols);
@@ -646,7 +642,7 @@ moe_status run_experts_mfma(const moe_desc* d, const Plan& p, const void* x,
   g.tile_group = wsp<int32_t>(ws, p.o_tgroup);
   g.tile_m0 = wsp<int32_t>(ws, p.o_tm0);
   g.n_tiles = wsp<int32_t>(ws, p.o_ntiles);
-  g.E = p.E; g.T = (int)p.T; g.H = p.H; g.I = p.I; g.Is = p.Is; g.ncols = p.ncols;
+  g.E = p.E; g.T = (int)p.T; g.H = p.H; g.I = p.I; g.Is = p.Is;
 
   GemmParams gu = g;
   gu.w0 = static_cast<const uint16_t*>(w->gate);
