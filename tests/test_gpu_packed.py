@@ -91,10 +91,12 @@ def test_pack_layout_matches_definition(cfg):
         assert bad.size == 0, f"{name}: {bad.size} bytes differ, first at {bad[:4]}"
 
 
-# Workloads whose prefill GEMMs stream weight tiles (many routes per expert)
+# Workloads whose prefill GEMMs stream weight tiles (many routes per expert),
+# and two whose paths do not use the packed arrays (fewer routes per expert;
+# one-token decode), where giving them must change nothing
 FORWARD = [
     "mfma_dma_shared", "mfma_dma_gelu_bias", "mfma_dma_deep_shared", "prefill_shared_t4096",
-    "prefill_skew_t16384",
+    "prefill_skew_t16384", "mfma_shared", "gemv_bf16_shared_t1",
 ]
 SMALL = {
     "mfma_dma_shared": MoeConfig(name="mfma_dma_shared", T=700, H=256, I=192, E=4, k=2,
@@ -106,6 +108,12 @@ SMALL = {
     "mfma_dma_deep_shared": MoeConfig(name="mfma_dma_deep_shared", T=800, H=256, I=192, E=8, k=2,
                                       weight_format=WF_BF16, act_dtype=DT_BF16,
                                       router_dtype=DT_BF16, shared=True, Is=64, seed_index=67),
+    "mfma_shared": MoeConfig(name="mfma_shared", T=300, H=256, I=128, E=16, k=4,
+                             weight_format=WF_BF16, act_dtype=DT_BF16, router_dtype=DT_BF16,
+                             shared=True, Is=192, seed_index=11),
+    "gemv_bf16_shared_t1": MoeConfig(name="gemv_bf16_shared_t1", T=1, H=1024, I=320, E=16, k=4,
+                                     weight_format=WF_BF16, router_dtype=DT_BF16, shared=True,
+                                     Is=192, seed_index=35),
 }
 
 
