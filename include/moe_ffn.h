@@ -274,11 +274,13 @@ moe_status moe_glu_backward(int64_t rows, int32_t intermediate, int32_t activati
 
 /*
  * Packed expert weights: a layout of the bf16 expert weights for the prefill
- * grouped GEMMs (the FFN of Switch Transformers section 2, or the gated FFN of
- * Mixtral's sparse MoE layer, per expert).  Those GEMMs stream weight tiles
- * 64 K-elements at a time; the packed layout stores each tile's K-step as one
- * contiguous 32 KB block, so HBM serves it as a sequential run instead of 256
- * rows of 128 bytes.  The arithmetic, and so every result, is unchanged.
+ * grouped GEMMs.  DS4Server's qwen_mtplx.rs (its SwitchGLU weights) already
+ * offers gate and up either as separate [E, I, H] matrices or fused into one
+ * [E, 2I, H]; this layout goes further, for the way these GEMMs read weights.
+ * They stream weight tiles 64 K-elements at a time; the packed layout stores
+ * each tile's K-step as one contiguous 32 KB block, a sequential run instead
+ * of 256 rows of 128 bytes.  The arithmetic, and so every result, is
+ * unchanged.
  *
  * Layout (bf16 elements, 16-byte chunks): block (t, s) of an expert holds
  * K-elements 64s .. 64s+63 of its weight tile t as 256 rows of 128 bytes.

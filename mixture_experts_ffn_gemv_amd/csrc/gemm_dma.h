@@ -1,6 +1,6 @@
 // bf16 MFMA grouped GEMM for experts that average many routes (prefill with
-// at least 256 routes per expert): 256 weight rows x 256 routes per
-// workgroup, K in steps of 64.
+// at least kDmaMinAvgRoutes routes per expert on average): 256 weight rows x
+// 256 routes per workgroup, K in steps of 64.
 //
 // Operands reach LDS by direct global->LDS loads (global_load_lds_dwordx4):
 // no staging registers and no ds_write.  The loads are issued from inline
@@ -8,9 +8,11 @@
 // wait insertion cannot tell the ring's stages apart and drains every load
 // in flight at the top of the loop.  K-steps of 64 make every load cover
 // whole 128-byte lines (half as many outstanding requests per byte as steps
-// of 32, whose extra ring depth measured no faster).  The weight operand has
-// three 32 KB slots and the route operand two, so that the weight stream
-// keeps two K-steps in flight while one is multiplied.
+// of 32, whose extra ring depth measured no faster).  The route operand has
+// two 32 KB LDS slots; the weight operand two or three (RA): three when its
+// bytes stream from HBM once per launch (experts average fewer routes than a
+// tile holds), so that two of its K-steps are in flight while one is
+// multiplied.
 //
 // Each load instruction of a wave fills 1 KB of LDS, lane i writing bytes
 // 16i..16i+15 of it.  A swizzled layout (16-byte chunk c of row r at slot
@@ -20,7 +22,9 @@
 // Weights may instead come packed (k_pack below): each (expert, weight tile,
 // K-step) block is the 32 KB LDS image of that stage's weight operand, so a
 // stage's weight loads read one contiguous 32 KB run instead of 256 rows of
-// 128 bytes, which HBM serves at a far higher rate.
+// 128 bytes (a load-only stream of that pattern runs about 1.4x faster; in
+// this kernel, whose time the load pipeline's latency sets, the gain is a
+// few percent at most).
 //
 // kDmaWaves waves in a 2 (weight rows) x kDmaWaves/2 (routes) grid, each owning
 // 128 weight rows x 512/kDmaWaves routes of f32 accumulators (tiles of
