@@ -104,6 +104,12 @@ __device__ __forceinline__ uint64_t route_key(float l, int e) {
   return ((uint64_t)ord << 32) | (uint32_t)~(uint32_t)e;
 }
 
+// The logit a key was made from (inverse of route_key's ordering map).
+__device__ __forceinline__ float key_logit(uint64_t key) {
+  const uint32_t ord = (uint32_t)(key >> 32);
+  return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord);
+}
+
 typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
 
 template <int CTRL>
@@ -152,6 +158,64 @@ __device__ __forceinline__ void row_select(const float* __restrict__ s_l, int T,
       if (tok && l16 == 0) s_rid[t * k + j] = e;
     }
   }
+}
+
+// v of lane `src` (wave-uniform src) through the scalar unit: no LDS trip,
+// unlike a shuffle
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int src) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, src);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), src);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// One token's routing in one wave (E <= 256): the rank keys, selection
+// order and weights of route_small_impl at T = 1 (k rounds of a wave-wide
+// key maximum: a 16-lane row maximum by DPP, then the four rows' results
+// read through the scalar unit; the winner's lane clears it).  Lane j < k
+// returns slot j's expert and routing weight; every lane must take part.
+__device__ __forceinline__ void route_one_token(const float* __restrict__ l, int E, int k,
+                                                RouteMode rm, int& id, float& w) {
+  const int lane = threadIdx.x & 63;
+  float lv[4];
+  uint64_t key[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int e = lane + 64 * c;
+    lv[c] = e < E ? l[e] : 0.f;
+    key[c] = e < E ? route_key(lv[c], e) : 0;
+  }
+  uint64_t mine = 0;
+  for (int j = 0; j < k; ++j) {
+    uint64_t b = max_u64(max_u64(key[0], key[1]), max_u64(key[2], key[3]));
+    b = max_u64(b, dpp_u64<kDppXor1>(b));
+    b = max_u64(b, dpp_u64<kDppXor2>(b));
+    b = max_u64(b, dpp_u64<kDppHalfMirror>(b));
+    b = max_u64(b, dpp_u64<kDppMirror>(b));
+    b = max_u64(max_u64(readlane_u64(b, 0), readlane_u64(b, 16)),
+                max_u64(readlane_u64(b, 32), readlane_u64(b, 48)));
+#pragma unroll
+    for (int c = 0; c < 4; ++c) key[c] = key[c] == b ? 0 : key[c];
+    if (lane == j) mine = b;
+  }
+  id = lane < k ? (int)~(uint32_t)mine : 0;
+  // the selected logits come back out of their keys (the same value, -0
+  // read as +0), so nothing is read from memory again
+  const float li = key_logit(mine);
+  const float lmax = key_logit(readlane_u64(mine, 0));  // the top logit
+  const float ex = lane < k ? (rm.sigmoid ? sigmoid_f(li) : __expf(li - lmax)) : 0.f;
+  float denom;
+  if (rm.normalize) {
+    denom = wave_sum(ex);
+  } else if (rm.sigmoid) {
+    denom = 1.f;
+  } else {
+    float sum = 0.f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      if (lane + 64 * c < E) sum += __expf(lv[c] - lmax);
+    denom = wave_sum(sum);
+  }
+  w = ex / denom * rm.scale;
 }
 
 struct RouteLds {
@@ -404,6 +468,11 @@ struct Dec2Params {
   const float* residual;  // [T, H] or null, added to out (may be out)
   float* y;      // [R, H] per-route down outputs (4-bit path)
   int T, E, k, H, I, Is, rc;
+  // one token routed inside the gate/up kernel: the router's logits [ncols],
+  // the routing mode, and where workgroup (0, 0) writes the routing
+  const float* logits;
+  RouteMode rm;
+  SmallRouteOut ro;
 };
 
 template <int WF>
@@ -504,8 +573,9 @@ constexpr int kGUWaves = 4;  // features per gate/up workgroup (one per wave)
 // DIRECT (every expert has exactly one route, i.e. one token): the lane's
 // activation chunks are loaded straight into registers.  Otherwise the
 // activations of up to rc routes are staged in LDS as f32 per pass.
-template <int WF, int ACT, int U, bool DIRECT>
+template <int WF, int ACT, int U, bool DIRECT, bool ROUTE = false>
 __global__ __launch_bounds__(256) void k_dec_gateup3(Dec2Params p) {
+  static_assert(!ROUTE || DIRECT, "routing in the kernel is for one token");
   constexpr int EPC = WTraits<WF>::EPC;
   extern __shared__ float xs[];  // [rc][H] (staged path only)
   const int s = blockIdx.x;
@@ -513,11 +583,73 @@ __global__ __launch_bounds__(256) void k_dec_gateup3(Dec2Params p) {
   // has an entry for every slot of the grid), and the first K block's weight
   // loads go out as soon as the expert is known: the route and token lookups
   // follow while they are in flight.
-  const int na = *p.n_active;
-  const int slot_g = p.active[s];
-  // one round trip for both (and for the weight pointers), ahead of the exit test
-  asm volatile("" ::"s"(na), "s"(slot_g), "s"(p.gate.p), "s"(p.up.p), "s"(p.sgate.p),
-               "s"(p.sup.p));
+  int na, slot_g, route_r = 0;
+  if constexpr (ROUTE) {
+    // One token: every wave ranks the router logits itself (the same result
+    // in each), so the weight stream waits for no routing launch.  Slot s is
+    // the s-th smallest selected expert, its route the expert's top-k slot;
+    // slot k is the shared expert.  Workgroup (0, 0) writes the routing for
+    // the down kernel and the caller.
+    const int lane0 = threadIdx.x & 63;
+    int id;
+    float wv;
+    route_one_token(p.logits, p.E, p.k, p.rm, id, wv);
+    int asc = 0;  // selected experts below this lane's
+    for (int j = 0; j < p.k; ++j) asc += __builtin_amdgcn_readlane(id, j) < id ? 1 : 0;
+    const bool sh = p.Is > 0;
+    na = p.k + (sh ? 1 : 0);
+    if (s < p.k) {
+      const uint64_t m = __ballot(lane0 < p.k && asc == s);
+      route_r = __builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)m) - 1);
+      slot_g = __builtin_amdgcn_readlane(id, route_r);
+    } else {
+      slot_g = p.E;
+    }
+    if (blockIdx.x == 0 && blockIdx.y == 0 && (threadIdx.x >> 6) == 0) {
+      const SmallRouteOut& o = p.ro;
+      if (lane0 < p.k) {
+        o.ids[lane0] = id;
+        o.wts[lane0] = wv;
+        if (o.user_ids) o.user_ids[lane0] = id;
+        if (o.user_w) o.user_w[lane0] = wv;
+        o.active[asc] = id;
+        o.perm[asc] = lane0;  // route r = slot (token 0)
+        o.pos_of_route[lane0] = asc;
+        if (o.user_perm) o.user_perm[asc] = lane0;
+      }
+      for (int e0 = 0; e0 < p.E; e0 += 64) {  // uniform bounds: every lane shuffles
+        const int e = e0 + lane0;
+        int below = 0, cnt = 0;
+        for (int j = 0; j < p.k; ++j) {
+          const int o2 = __builtin_amdgcn_readlane(id, j);
+          below += o2 < e ? 1 : 0;
+          cnt += o2 == e ? 1 : 0;
+        }
+        if (e < p.E) {
+          o.counts[e] = cnt;
+          o.offsets[e] = below;
+          if (o.user_counts) o.user_counts[e] = cnt;
+          if (o.user_offsets) o.user_offsets[e] = below;
+        }
+      }
+      if (lane0 == 0) {
+        o.offsets[p.E] = p.k;
+        if (o.user_offsets) o.user_offsets[p.E] = p.k;
+        if (sh) {
+          o.counts[p.E] = 1;
+          o.active[p.k] = p.E;
+          o.sgate[0] = sigmoid_f(p.logits[p.E]);
+        }
+        *o.n_active = na;
+      }
+    }
+  } else {
+    na = *p.n_active;
+    slot_g = p.active[s];
+    // one round trip for both (and for the weight pointers), ahead of the exit test
+    asm volatile("" ::"s"(na), "s"(slot_g), "s"(p.gate.p), "s"(p.up.p), "s"(p.sgate.p),
+                 "s"(p.sup.p));
+  }
   if (s >= na) return;
   const int R = p.T * p.k;
   const int g = ws_group(slot_g, p.E, p.Is > 0);
@@ -549,9 +681,13 @@ __global__ __launch_bounds__(256) void k_dec_gateup3(Dec2Params p) {
         load_chunk<WF, true>(Mu, row, p.H, c, ok, wu[u], su[u], mu[u]);
       }
       if (kb == 0 && !shared) {  // the expert's one route, and its token
-        int count = p.counts[g], base = p.offsets[g];
-        ws_span(base, count, R);
-        r = ws_route(p.perm[base], R);
+        if constexpr (ROUTE) {
+          r = route_r;
+        } else {
+          int count = p.counts[g], base = p.offsets[g];
+          ws_span(base, count, R);
+          r = ws_route(p.perm[base], R);
+        }
         t = r / p.k;
       }
 #pragma unroll

@@ -480,21 +480,27 @@ int pick_u(int cpr) {
   return 8;
 }
 
-template <int WF, int ACT, bool DIRECT>
+template <int WF, int ACT, bool DIRECT, bool ROUTE>
 void launch_gu3_u(int u, dim3 grid, size_t lds, hipStream_t s, const Dec2Params& dp) {
   switch (u) {
-    case 1: k_dec_gateup3<WF, ACT, 1, DIRECT><<<grid, 256, lds, s>>>(dp); break;
-    case 2: k_dec_gateup3<WF, ACT, 2, DIRECT><<<grid, 256, lds, s>>>(dp); break;
-    case 3: k_dec_gateup3<WF, ACT, 3, DIRECT><<<grid, 256, lds, s>>>(dp); break;
-    case 4: k_dec_gateup3<WF, ACT, 4, DIRECT><<<grid, 256, lds, s>>>(dp); break;
-    case 6: k_dec_gateup3<WF, ACT, 6, DIRECT><<<grid, 256, lds, s>>>(dp); break;
-    default: k_dec_gateup3<WF, ACT, 8, DIRECT><<<grid, 256, lds, s>>>(dp); break;
+    case 1: k_dec_gateup3<WF, ACT, 1, DIRECT, ROUTE><<<grid, 256, lds, s>>>(dp); break;
+    case 2: k_dec_gateup3<WF, ACT, 2, DIRECT, ROUTE><<<grid, 256, lds, s>>>(dp); break;
+    case 3: k_dec_gateup3<WF, ACT, 3, DIRECT, ROUTE><<<grid, 256, lds, s>>>(dp); break;
+    case 4: k_dec_gateup3<WF, ACT, 4, DIRECT, ROUTE><<<grid, 256, lds, s>>>(dp); break;
+    case 6: k_dec_gateup3<WF, ACT, 6, DIRECT, ROUTE><<<grid, 256, lds, s>>>(dp); break;
+    default: k_dec_gateup3<WF, ACT, 8, DIRECT, ROUTE><<<grid, 256, lds, s>>>(dp); break;
   }
 }
+// direct: one token (its route read in place); route: also rank its router
+// logits in the kernel (one token, f32 or bf16 weights)
 template <int WF, int ACT>
-void launch_gu3(bool direct, int u, dim3 grid, size_t lds, hipStream_t s, const Dec2Params& dp) {
-  if (direct) launch_gu3_u<WF, ACT, true>(u, grid, 0, s, dp);
-  else launch_gu3_u<WF, ACT, false>(u, grid, lds, s, dp);
+void launch_gu3(bool direct, bool route, int u, dim3 grid, size_t lds, hipStream_t s,
+                const Dec2Params& dp) {
+  if constexpr (WF != WF_U4) {
+    if (route) return launch_gu3_u<WF, ACT, true, true>(u, grid, 0, s, dp);
+  }
+  if (direct) launch_gu3_u<WF, ACT, true, false>(u, grid, 0, s, dp);
+  else launch_gu3_u<WF, ACT, false, false>(u, grid, lds, s, dp);
 }
 template <int WF>
 void launch_dn3(int u, dim3 grid, hipStream_t s, const Dec2Params& dp) {
@@ -575,9 +581,13 @@ moe_status run_experts_u4(const moe_desc* d, const Plan& p, Dec2Params dp, float
   });
 }
 
+// route: one token with f32/bf16 weights, routed inside the gate/up kernel
+// from the logits the router GEMV left in the workspace (user_ids/user_w:
+// the caller's routing outputs, or null)
 moe_status run_experts_small(const moe_desc* d, const Plan& p, const void* x,
                              const moe_weights* w, float* out, const float* residual, void* ws,
-                             hipStream_t s) {
+                             hipStream_t s, bool route = false, int32_t* user_ids = nullptr,
+                             float* user_w = nullptr) {
   const int wf = d->weight_format;
   const int epc = epc_of(wf);
   Dec2Params dp;
@@ -601,6 +611,13 @@ moe_status run_experts_small(const moe_desc* d, const Plan& p, const void* x,
   dp.out = out;
   dp.residual = residual;
   dp.T = (int)p.T; dp.E = p.E; dp.k = p.k; dp.H = p.H; dp.I = p.I; dp.Is = p.Is; dp.rc = p.rc;
+  dp.logits = wsp<float>(ws, p.o_logits);
+  dp.rm = route_mode(d);
+  dp.ro = SmallRouteOut{wsp<int32_t>(ws, p.o_ids), wsp<float>(ws, p.o_wts),
+                        wsp<float>(ws, p.o_sgate), wsp<int32_t>(ws, p.o_counts),
+                        wsp<int32_t>(ws, p.o_offsets), wsp<int32_t>(ws, p.o_active),
+                        wsp<int32_t>(ws, p.o_nactive), wsp<int32_t>(ws, p.o_perm),
+                        wsp<int32_t>(ws, p.o_pos), user_ids, user_w, nullptr, nullptr, nullptr};
 
   if (wf == MOE_WEIGHTS_U4_G32) return run_experts_u4(d, p, dp, out, residual, ws, s);
 
@@ -612,14 +629,14 @@ moe_status run_experts_small(const moe_desc* d, const Plan& p, const void* x,
   MOE_TRY(launch("gemv_gateup", s, [&] {
     const bool silu = d->activation == MOE_ACT_SILU;
     if (wf == MOE_WEIGHTS_F32) {
-      if (silu) launch_gu3<WF_F32, ACT_SILU>(direct, u1, g1, lds, s, dp);
-      else launch_gu3<WF_F32, ACT_GELU_TANH>(direct, u1, g1, lds, s, dp);
+      if (silu) launch_gu3<WF_F32, ACT_SILU>(direct, route, u1, g1, lds, s, dp);
+      else launch_gu3<WF_F32, ACT_GELU_TANH>(direct, route, u1, g1, lds, s, dp);
     } else if (wf == MOE_WEIGHTS_BF16) {
-      if (silu) launch_gu3<WF_BF16, ACT_SILU>(direct, u1, g1, lds, s, dp);
-      else launch_gu3<WF_BF16, ACT_GELU_TANH>(direct, u1, g1, lds, s, dp);
+      if (silu) launch_gu3<WF_BF16, ACT_SILU>(direct, route, u1, g1, lds, s, dp);
+      else launch_gu3<WF_BF16, ACT_GELU_TANH>(direct, route, u1, g1, lds, s, dp);
     } else {
-      if (silu) launch_gu3<WF_U4, ACT_SILU>(direct, u1, g1, lds, s, dp);
-      else launch_gu3<WF_U4, ACT_GELU_TANH>(direct, u1, g1, lds, s, dp);
+      if (silu) launch_gu3<WF_U4, ACT_SILU>(direct, false, u1, g1, lds, s, dp);
+      else launch_gu3<WF_U4, ACT_GELU_TANH>(direct, false, u1, g1, lds, s, dp);
     }
   }));
   const int maxK = std::max(p.I, p.Is);
@@ -860,6 +877,13 @@ moe_status moe_ffn_forward(const moe_desc* desc, int64_t num_tokens, const void*
   hipStream_t s = static_cast<hipStream_t>(stream);
   MOE_TRY(layer_input(desc, p, x, weights, ws, s, &x));
   if (p.small) {
+    if (num_tokens == 1 && desc->weight_format != MOE_WEIGHTS_U4_G32) {
+      // one token: the router kernel writes only the logits; the gate/up
+      // kernel ranks them itself and writes the routing (no routing tail)
+      MOE_TRY(run_router(desc, p, x, weights, ws, s));
+      return run_experts_small(desc, p, x, weights, out, residual, ws, s, true, topk_ids_out,
+                               topk_w_out);
+    }
     MOE_TRY(run_route_small(desc, p, x, weights, ws, topk_ids_out, topk_w_out, nullptr, nullptr,
                             nullptr, s));
     return run_experts_small(desc, p, x, weights, out, residual, ws, s);
