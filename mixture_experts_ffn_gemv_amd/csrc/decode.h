@@ -1,7 +1,9 @@
 // Decode path (few tokens, T <= 32): three launches per layer.
 //
-//   k_router_route -> k_dec_gateup3 -> k_dec_down3
+//   T = 1, f32 or bf16 weights:  k_router_gemv  -> k_dec_gateup3<ROUTE> -> k_dec_down3
+//   otherwise:                   k_router_route -> k_dec_gateup3        -> k_dec_down3
 //
+// k_router_gemv   router logits only (one workgroup per router row).
 // k_router_route  router logits (one workgroup per router row); the last
 //                 workgroup to finish then does softmax/top-k/renormalise
 //                 for every token and the stable expert grouping (counts,
@@ -11,7 +13,13 @@
 //                 wave owns 1 feature (its gate and up rows); its 64 lanes
 //                 split K into 16-byte chunks and issue every weight load of
 //                 those rows before touching the activations.  Only the
-//                 touched experts' weights are read, each byte once.
+//                 touched experts' weights are read, each byte once.  With
+//                 ROUTE (one token) every wave ranks the token's logits
+//                 itself (route_one_token, the same keys, order and weights
+//                 as the routing workgroup) to find its expert, and
+//                 workgroup (0,0) writes the routing for k_dec_down3 and
+//                 the caller: one token's top-k costs a wave less than a
+//                 grid-wide handoff inside the router launch does.
 // k_dec_down3     work item = block of output features; the 4 waves split
 //                 the touched experts, each loading the expert's down rows
 //                 once and applying them to all of the expert's routes, and

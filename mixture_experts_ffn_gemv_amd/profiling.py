@@ -32,6 +32,7 @@ KERNEL_SOURCES = {
     "gemv_down_combine": ["common.h", "gemv.h", "route.h", "decode.h", "moe_ffn.hip"],
     "gemv_down": ["common.h", "gemv.h", "route.h", "decode.h", "decode_u4.h", "moe_ffn.hip"],
     "router_route": ["common.h", "route.h", "decode.h", "moe_ffn.hip"],
+    "router_gemv": ["common.h", "route.h", "moe_ffn.hip"],
     "gemm_gateup": ["common.h", "gemm.h", "gemm_big.h", "gemm_dma.h", "moe_ffn.hip"],
     "gemm_down": ["common.h", "gemm.h", "gemm_big.h", "gemm_dma.h", "moe_ffn.hip"],
     "wsum_backward": ["common.h", "backward.h", "moe_ffn.hip"],
