@@ -53,7 +53,15 @@ struct SmallRouteOut {
   int32_t* user_counts;
   int32_t* user_offsets;
   int32_t* user_perm;
+  // one token routed in the gate/up kernel: the slot table (null otherwise)
+  int4* slots;
 };
+
+// Slot table of one-token decode: entry 0 = {slots in use, 0, 0, 0}; entry
+// 1 + s = {expert, route, routing weight (f32 bits), 0} of slot s, the
+// selected experts in ascending order, then the shared expert (route 0,
+// weight its sigmoid gate).  The down kernel reads it with one load a lane.
+constexpr int kSlotTab = MOE_MAX_TOP_K_DEV + 2;
 
 // Exclusive prefix sums of two per-thread values over the 256 threads of a
 // workgroup (thread order), and their totals.
@@ -106,16 +114,17 @@ __device__ __forceinline__ bool rank_route_ok(int T, int E) {
   return pairs <= kRankMaxPairs && ((pairs + 255) / 256) * E <= 256;
 }
 
-__device__ __forceinline__ uint64_t route_key(float l, int e) {
-  const uint32_t u = __float_as_uint(l == 0.0f ? 0.0f : l);  // -0 and +0 tie
-  const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return ((uint64_t)ord << 32) | (uint32_t)~(uint32_t)e;
+// Order-preserving 32-bit image of a logit (-0 and +0 tie) and its inverse.
+__device__ __forceinline__ uint32_t route_ord(float l) {
+  const uint32_t u = __float_as_uint(l == 0.0f ? 0.0f : l);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
-
-// The logit a key was made from (inverse of route_key's ordering map).
-__device__ __forceinline__ float key_logit(uint64_t key) {
-  const uint32_t ord = (uint32_t)(key >> 32);
+__device__ __forceinline__ float ord_logit(uint32_t ord) {
   return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord);
+}
+// Rank key of (logit, expert): larger logit first, then the lower expert.
+__device__ __forceinline__ uint64_t route_key(float l, int e) {
+  return ((uint64_t)route_ord(l) << 32) | (uint32_t)~(uint32_t)e;
 }
 
 typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
@@ -168,48 +177,82 @@ __device__ __forceinline__ void row_select(const float* __restrict__ s_l, int T,
   }
 }
 
-// v of lane `src` (wave-uniform src) through the scalar unit: no LDS trip,
-// unlike a shuffle
-__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int src) {
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, src);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), src);
-  return ((uint64_t)hi << 32) | lo;
+constexpr int kDppRowBcast15 = 0x142;  // lane 15 of each row to the next row
+constexpr int kDppRowBcast31 = 0x143;  // lane 31 to rows 2 and 3
+
+// Maximum of v over the wave, wave-uniform: the row maximum by four DPP
+// steps, then two row broadcasts carry it to lane 63.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)dpp_i<kDppXor1>((int)v));
+  v = max(v, (uint32_t)dpp_i<kDppXor2>((int)v));
+  v = max(v, (uint32_t)dpp_i<kDppHalfMirror>((int)v));
+  v = max(v, (uint32_t)dpp_i<kDppMirror>((int)v));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, kDppRowBcast15, 0xA, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, kDppRowBcast31, 0xC, 0xF, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
-// One token's routing in one wave (E <= 256): the rank keys, selection
-// order and weights of route_small_impl at T = 1 (k rounds of a wave-wide
-// key maximum: a 16-lane row maximum by DPP, then the four rows' results
-// read through the scalar unit; the winner's lane clears it).  Lane j < k
-// returns slot j's expert and routing weight; every lane must take part.
+// One token's routing in one wave (E <= 64*C): the selection order and
+// weights of route_small_impl at T = 1.  Lane l holds experts l, l+64, ...;
+// each of k rounds takes the wave maximum M of the order images, then the
+// lowest still-live expert whose image is M (ballots over the lanes, the
+// live set a wave-uniform bit mask, since taken and absent experts both read
+// as image 0), which is exactly the maximum of the rank keys.  Lane j < k
+// returns slot j's expert and routing weight; `sel` returns the selected
+// experts as bit masks (expert 64c + b at bit b of sel[c]).  Every lane must
+// take part.
+template <int C>
 __device__ __forceinline__ void route_one_token(const float* __restrict__ l, int E, int k,
-                                                RouteMode rm, int& id, float& w) {
+                                                RouteMode rm, int& id, float& w,
+                                                uint64_t (&sel)[C]) {
   const int lane = threadIdx.x & 63;
-  float lv[4];
-  uint64_t key[4];
+  float lv[C];
+  uint32_t ord[C];
+  uint64_t live[C];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
+  for (int c = 0; c < C; ++c) {
     const int e = lane + 64 * c;
-    lv[c] = e < E ? l[e] : 0.f;
-    key[c] = e < E ? route_key(lv[c], e) : 0;
+    const bool ok = e < E;
+    lv[c] = ok ? l[e] : 0.f;
+    ord[c] = ok ? route_ord(lv[c]) : 0u;
+    live[c] = __ballot(ok);
+    sel[c] = 0;
   }
-  uint64_t mine = 0;
+  int my_e = 0;
+  uint32_t my_ord = 0, top = 0;
   for (int j = 0; j < k; ++j) {
-    uint64_t b = max_u64(max_u64(key[0], key[1]), max_u64(key[2], key[3]));
-    b = max_u64(b, dpp_u64<kDppXor1>(b));
-    b = max_u64(b, dpp_u64<kDppXor2>(b));
-    b = max_u64(b, dpp_u64<kDppHalfMirror>(b));
-    b = max_u64(b, dpp_u64<kDppMirror>(b));
-    b = max_u64(max_u64(readlane_u64(b, 0), readlane_u64(b, 16)),
-                max_u64(readlane_u64(b, 32), readlane_u64(b, 48)));
+    uint32_t m = ord[0];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) key[c] = key[c] == b ? 0 : key[c];
-    if (lane == j) mine = b;
+    for (int c = 1; c < C; ++c) m = max(m, ord[c]);
+    const uint32_t M = wave_max_u32(m);
+    int e = 0;
+    bool found = false;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const uint64_t hit = __ballot(ord[c] == M) & live[c];
+      if (!found && hit != 0) {
+        e = 64 * c + __ffsll((unsigned long long)hit) - 1;
+        found = true;
+      }
+    }
+    const int ce = e >> 6, le = e & 63;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      if (c == ce) {
+        live[c] &= ~(1ull << le);
+        sel[c] |= 1ull << le;
+      }
+      ord[c] = (c == ce && lane == le) ? 0u : ord[c];
+    }
+    if (j == 0) top = M;
+    if (lane == j) {
+      my_e = e;
+      my_ord = M;
+    }
   }
-  id = lane < k ? (int)~(uint32_t)mine : 0;
-  // the selected logits come back out of their keys (the same value, -0
-  // read as +0), so nothing is read from memory again
-  const float li = key_logit(mine);
-  const float lmax = key_logit(readlane_u64(mine, 0));  // the top logit
+  id = lane < k ? my_e : 0;
+  const float li = ord_logit(my_ord);
+  const float lmax = ord_logit(top);  // the top logit
   const float ex = lane < k ? (rm.sigmoid ? sigmoid_f(li) : __expf(li - lmax)) : 0.f;
   float denom;
   if (rm.normalize) {
@@ -219,7 +262,7 @@ __device__ __forceinline__ void route_one_token(const float* __restrict__ l, int
   } else {
     float sum = 0.f;
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
+    for (int c = 0; c < C; ++c)
       if (lane + 64 * c < E) sum += __expf(lv[c] - lmax);
     denom = wave_sum(sum);
   }
@@ -481,6 +524,7 @@ struct Dec2Params {
   const float* logits;
   RouteMode rm;
   SmallRouteOut ro;
+  const int4* slots;  // slot table for the down kernel (one token), or null
 };
 
 template <int WF>
@@ -576,6 +620,101 @@ __device__ __forceinline__ void load_act(const void* x, int bf16, size_t off, fl
 constexpr int kRCMax = 4;    // routes per LDS pass (gate/up with several routes per expert)
 constexpr int kGUWaves = 4;  // features per gate/up workgroup (one per wave)
 
+// One token, routed in the gate/up kernel: every wave ranks the router
+// logits itself (route_one_token: the same result in each), so the weight
+// stream waits for no routing launch.  Slot s is the s-th smallest selected
+// expert, its route the expert's top-k position; slot k is the shared
+// expert.
+struct OneRoute {
+  int id;           // lane j < k: slot j's expert
+  float w;          // and its routing weight
+  uint64_t sel[4];  // selected experts, expert 64c + b at bit b of sel[c]
+};
+template <int C>
+__device__ __forceinline__ void route_slot(const Dec2Params& p, int s, int& na, int& slot_g,
+                                           int& route_r, OneRoute& rt) {
+  const int lane = threadIdx.x & 63;
+  uint64_t sel[C];
+  route_one_token<C>(p.logits, p.E, p.k, p.rm, rt.id, rt.w, sel);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) rt.sel[c] = c < C ? sel[c] : 0ull;
+  na = p.k + (p.Is > 0 ? 1 : 0);
+  slot_g = p.E;
+  route_r = 0;
+  if (s < p.k) {  // the s-th set bit of sel, on the scalar unit
+    int rem = s;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      uint64_t m = sel[c];
+      const int n = __popcll(m);
+      if (rem >= 0 && rem < n) {
+        for (int i = 0; i < rem; ++i) m &= m - 1;
+        slot_g = 64 * c + __ffsll((unsigned long long)m) - 1;
+      }
+      rem -= n;
+    }
+    const uint64_t at = __ballot(lane < p.k && rt.id == slot_g);
+    route_r = __builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)at) - 1);
+  }
+}
+
+// The routing of one token for the down kernel (slot table) and the caller,
+// written by one wave of the grid once its own weight loads are in flight.
+__device__ __forceinline__ void route_write(const Dec2Params& p, const OneRoute& rt) {
+  const int lane = threadIdx.x & 63;
+  const SmallRouteOut& o = p.ro;
+  const bool sh = p.Is > 0;
+  const int na = p.k + (sh ? 1 : 0);
+  const int id = rt.id;
+  if (lane < p.k) {
+    int asc = 0;  // selected experts below this lane's
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int d = id - 64 * c;
+      asc += __popcll(d >= 64 ? rt.sel[c] : d <= 0 ? 0ull : rt.sel[c] & (~0ull >> (64 - d)));
+    }
+    o.ids[lane] = id;
+    o.wts[lane] = rt.w;
+    if (o.user_ids) o.user_ids[lane] = id;
+    if (o.user_w) o.user_w[lane] = rt.w;
+    o.active[asc] = id;
+    o.perm[asc] = lane;  // route r = slot (token 0)
+    o.pos_of_route[lane] = asc;
+    if (o.user_perm) o.user_perm[asc] = lane;
+    if (o.slots) o.slots[1 + asc] = make_int4(id, lane, __float_as_int(rt.w), 0);
+  }
+  const uint64_t below_lane = lanemask_lt();
+  int prefix = 0;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int e = 64 * c + lane;
+    if (e < p.E) {
+      const int cnt = (int)((rt.sel[c] >> lane) & 1ull);
+      const int below = prefix + __popcll(rt.sel[c] & below_lane);
+      o.counts[e] = cnt;
+      o.offsets[e] = below;
+      if (o.user_counts) o.user_counts[e] = cnt;
+      if (o.user_offsets) o.user_offsets[e] = below;
+    }
+    prefix += __popcll(rt.sel[c]);
+  }
+  if (lane == 0) {
+    o.offsets[p.E] = p.k;
+    if (o.user_offsets) o.user_offsets[p.E] = p.k;
+    const float sg = sh ? sigmoid_f(p.logits[p.E]) : 0.f;
+    if (sh) {
+      o.counts[p.E] = 1;
+      o.active[p.k] = p.E;
+      o.sgate[0] = sg;
+    }
+    *o.n_active = na;
+    if (o.slots) {
+      o.slots[0] = make_int4(na, 0, 0, 0);
+      if (sh) o.slots[1 + p.k] = make_int4(p.E, 0, __float_as_int(sg), 0);
+    }
+  }
+}
+
 // gate/up: each wave owns one feature f of one touched expert: its gate row
 // and its up row, full K, lane l holding chunks l, l+64, ... (U of them).
 // DIRECT (every expert has exactly one route, i.e. one token): the lane's
@@ -592,65 +731,10 @@ __global__ __launch_bounds__(256) void k_dec_gateup3(Dec2Params p) {
   // loads go out as soon as the expert is known: the route and token lookups
   // follow while they are in flight.
   int na, slot_g, route_r = 0;
+  OneRoute rt;
   if constexpr (ROUTE) {
-    // One token: every wave ranks the router logits itself (the same result
-    // in each), so the weight stream waits for no routing launch.  Slot s is
-    // the s-th smallest selected expert, its route the expert's top-k slot;
-    // slot k is the shared expert.  Workgroup (0, 0) writes the routing for
-    // the down kernel and the caller.
-    const int lane0 = threadIdx.x & 63;
-    int id;
-    float wv;
-    route_one_token(p.logits, p.E, p.k, p.rm, id, wv);
-    int asc = 0;  // selected experts below this lane's
-    for (int j = 0; j < p.k; ++j) asc += __builtin_amdgcn_readlane(id, j) < id ? 1 : 0;
-    const bool sh = p.Is > 0;
-    na = p.k + (sh ? 1 : 0);
-    if (s < p.k) {
-      const uint64_t m = __ballot(lane0 < p.k && asc == s);
-      route_r = __builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)m) - 1);
-      slot_g = __builtin_amdgcn_readlane(id, route_r);
-    } else {
-      slot_g = p.E;
-    }
-    if (blockIdx.x == 0 && blockIdx.y == 0 && (threadIdx.x >> 6) == 0) {
-      const SmallRouteOut& o = p.ro;
-      if (lane0 < p.k) {
-        o.ids[lane0] = id;
-        o.wts[lane0] = wv;
-        if (o.user_ids) o.user_ids[lane0] = id;
-        if (o.user_w) o.user_w[lane0] = wv;
-        o.active[asc] = id;
-        o.perm[asc] = lane0;  // route r = slot (token 0)
-        o.pos_of_route[lane0] = asc;
-        if (o.user_perm) o.user_perm[asc] = lane0;
-      }
-      for (int e0 = 0; e0 < p.E; e0 += 64) {  // uniform bounds: every lane shuffles
-        const int e = e0 + lane0;
-        int below = 0, cnt = 0;
-        for (int j = 0; j < p.k; ++j) {
-          const int o2 = __builtin_amdgcn_readlane(id, j);
-          below += o2 < e ? 1 : 0;
-          cnt += o2 == e ? 1 : 0;
-        }
-        if (e < p.E) {
-          o.counts[e] = cnt;
-          o.offsets[e] = below;
-          if (o.user_counts) o.user_counts[e] = cnt;
-          if (o.user_offsets) o.user_offsets[e] = below;
-        }
-      }
-      if (lane0 == 0) {
-        o.offsets[p.E] = p.k;
-        if (o.user_offsets) o.user_offsets[p.E] = p.k;
-        if (sh) {
-          o.counts[p.E] = 1;
-          o.active[p.k] = p.E;
-          o.sgate[0] = sigmoid_f(p.logits[p.E]);
-        }
-        *o.n_active = na;
-      }
-    }
+    if (p.E <= 128) route_slot<2>(p, s, na, slot_g, route_r, rt);
+    else route_slot<4>(p, s, na, slot_g, route_r, rt);
   } else {
     na = *p.n_active;
     slot_g = p.active[s];
@@ -687,6 +771,10 @@ __global__ __launch_bounds__(256) void k_dec_gateup3(Dec2Params p) {
         const bool ok = fok && c < cpr;
         load_chunk<WF, true>(Mg, row, p.H, c, ok, wg[u], sg[u], mg[u]);
         load_chunk<WF, true>(Mu, row, p.H, c, ok, wu[u], su[u], mu[u]);
+      }
+      if constexpr (ROUTE) {
+        // workgroup (0, 0) holds slot 0, a routed expert, and feature 0
+        if (kb == 0 && blockIdx.x == 0 && blockIdx.y == 0 && wave == 0) route_write(p, rt);
       }
       if (kb == 0 && !shared) {  // the expert's one route, and its token
         if constexpr (ROUTE) {
@@ -792,18 +880,33 @@ constexpr int kDownRPW = 4;  // output features per down+combine workgroup
 // expert's rows while computing with the current one, and accumulate
 // w_route * (Wd[e][n,:] . h_route) per token in LDS.  The shared expert is
 // the last group, weighted by its sigmoid gate.  The four waves' partial
-// sums are added in a fixed order and written to out: no atomics.
-template <int WF, int U>
+// sums are added in a fixed order and written to out: no atomics.  ONE (one
+// token, routed in the gate/up kernel): each slot's expert, route and weight
+// come from the slot table, read with one load a lane, instead of a chain of
+// dependent lookups (slot count, expert, its span, route, weight).
+template <int WF, int U, bool ONE = false>
 __global__ __launch_bounds__(256) void k_dec_down3(Dec2Params p) {
   constexpr int EPC = WTraits<WF>::EPC;
   constexpr int RPW = kDownRPW;
-  __shared__ float part[4][kSmallMaxTokens][RPW];
+  constexpr int TMAX = ONE ? 1 : kSmallMaxTokens;
+  __shared__ float part[4][TMAX][RPW];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n0 = blockIdx.x * RPW;
-  for (int i = tid; i < 4 * kSmallMaxTokens * RPW; i += 256) (&part[0][0][0])[i] = 0.f;
+  const int gmax = p.E + (p.Is > 0 ? 1 : 0);
+  int4 tab = make_int4(0, 0, 0, 0);
+  int na;
+  if constexpr (ONE) {
+    if (lane < kSlotTab) tab = p.slots[lane];
+    na = min(max(__builtin_amdgcn_readlane(tab.x, 0), 0), min(gmax, p.k + (p.Is > 0 ? 1 : 0)));
+  }
+  for (int i = tid; i < 4 * TMAX * RPW; i += 256) (&part[0][0][0])[i] = 0.f;
   __syncthreads();
-  const int na = min(*p.n_active, p.E + (p.Is > 0 ? 1 : 0));
+  if constexpr (!ONE) na = min(*p.n_active, gmax);
   const int R = p.T * p.k;
+  auto slot_group = [&](int s) {
+    if constexpr (ONE) return ws_group(__builtin_amdgcn_readlane(tab.x, 1 + s), p.E, p.Is > 0);
+    else return ws_group(p.active[s], p.E, p.Is > 0);
+  };
 
   u32x4 wc[RPW][U], wn[RPW][U];
   float sc[RPW][U], mc[RPW][U], sn[RPW][U], mnx[RPW][U];
@@ -825,23 +928,31 @@ __global__ __launch_bounds__(256) void k_dec_down3(Dec2Params p) {
     }
   };
   int s = wave;
-  int g = s < na ? ws_group(p.active[s], p.E, p.Is > 0) : 0;
+  int g = s < na ? slot_group(s) : 0;
   if (s < na) load_group(g, wc, sc, mc);
   while (s < na) {
     const int sn_ = s + 4;
-    const int gn = sn_ < na ? ws_group(p.active[sn_], p.E, p.Is > 0) : 0;
+    const int gn = sn_ < na ? slot_group(sn_) : 0;
     if (sn_ < na) load_group(gn, wn, sn, mnx);
     const bool shared = (g == p.E);
     const int K = shared ? p.Is : p.I;
     const int cpr = K / EPC;
-    int count = shared ? p.T : p.counts[g];
-    int base = shared ? 0 : p.offsets[g];
-    if (!shared) ws_span(base, count, R);
+    int count = 1, base = 0;
+    if constexpr (!ONE) {
+      count = shared ? p.T : p.counts[g];
+      base = shared ? 0 : p.offsets[g];
+      if (!shared) ws_span(base, count, R);
+    }
     for (int i = 0; i < count; ++i) {
       int t;
       float wgt;
       const float* hrow;
-      if (shared) {
+      if constexpr (ONE) {
+        const int r = ws_route(__builtin_amdgcn_readlane(tab.y, 1 + s), R);
+        t = 0;
+        wgt = __int_as_float(__builtin_amdgcn_readlane(tab.z, 1 + s));
+        hrow = shared ? p.hs : p.h + (size_t)r * K;
+      } else if (shared) {
         t = i; wgt = p.sgate_val[t]; hrow = p.hs + (size_t)t * K;
       } else {
         const int r = ws_route(p.perm[base + i], R);

@@ -62,7 +62,7 @@ struct Plan {
   int max_groups = 0;      // active groups (upper bound)
   // workspace offsets
   size_t o_sync, o_xn, o_logits, o_ids, o_wts, o_sgate, o_bhist, o_boff, o_counts, o_offsets, o_active,
-      o_nactive, o_ntiles, o_perm, o_pos, o_rowtok, o_tgroup, o_tm0, o_h, o_hs, o_y, o_ys;
+      o_nactive, o_ntiles, o_perm, o_pos, o_rowtok, o_tgroup, o_tm0, o_h, o_hs, o_y, o_ys, o_slots;
   size_t total = 0;
 };
 
@@ -180,6 +180,7 @@ Plan make_plan(const moe_desc* d, int64_t T) {
   p.o_hs = take((size_t)T * p.Is * es);
   p.o_y = take((size_t)p.R * p.H * es);
   p.o_ys = take((size_t)(p.shared ? T : 0) * p.H * es);
+  p.o_slots = take((size_t)kSlotTab * 16);
   p.total = o;
   return p;
 }
@@ -285,7 +286,7 @@ moe_status run_route_small(const moe_desc* d, const Plan& p, const void* x, cons
                            void* ws, int32_t* user_ids, float* user_w, int32_t* user_counts,
                            int32_t* user_offsets, int32_t* user_perm, hipStream_t s) {
   const int T = (int)p.T;
-  SmallRouteOut o;
+  SmallRouteOut o{};
   o.ids = wsp<int32_t>(ws, p.o_ids);
   o.wts = wsp<float>(ws, p.o_wts);
   o.sgate = wsp<float>(ws, p.o_sgate);
@@ -502,16 +503,24 @@ void launch_gu3(bool direct, bool route, int u, dim3 grid, size_t lds, hipStream
   if (direct) launch_gu3_u<WF, ACT, true, false>(u, grid, 0, s, dp);
   else launch_gu3_u<WF, ACT, false, false>(u, grid, lds, s, dp);
 }
-template <int WF>
-void launch_dn3(int u, dim3 grid, hipStream_t s, const Dec2Params& dp) {
+template <int WF, bool ONE>
+void launch_dn3_u(int u, dim3 grid, hipStream_t s, const Dec2Params& dp) {
   switch (u) {
-    case 1: k_dec_down3<WF, 1><<<grid, 256, 0, s>>>(dp); break;
-    case 2: k_dec_down3<WF, 2><<<grid, 256, 0, s>>>(dp); break;
-    case 3: k_dec_down3<WF, 3><<<grid, 256, 0, s>>>(dp); break;
-    case 4: k_dec_down3<WF, 4><<<grid, 256, 0, s>>>(dp); break;
-    case 6: k_dec_down3<WF, 6><<<grid, 256, 0, s>>>(dp); break;
-    default: k_dec_down3<WF, 8><<<grid, 256, 0, s>>>(dp); break;
+    case 1: k_dec_down3<WF, 1, ONE><<<grid, 256, 0, s>>>(dp); break;
+    case 2: k_dec_down3<WF, 2, ONE><<<grid, 256, 0, s>>>(dp); break;
+    case 3: k_dec_down3<WF, 3, ONE><<<grid, 256, 0, s>>>(dp); break;
+    case 4: k_dec_down3<WF, 4, ONE><<<grid, 256, 0, s>>>(dp); break;
+    case 6: k_dec_down3<WF, 6, ONE><<<grid, 256, 0, s>>>(dp); break;
+    default: k_dec_down3<WF, 8, ONE><<<grid, 256, 0, s>>>(dp); break;
   }
+}
+// one: one token whose routing the gate/up kernel wrote as a slot table
+template <int WF>
+void launch_dn3(bool one, int u, dim3 grid, hipStream_t s, const Dec2Params& dp) {
+  if constexpr (WF != WF_U4) {
+    if (one) return launch_dn3_u<WF, true>(u, grid, s, dp);
+  }
+  launch_dn3_u<WF, false>(u, grid, s, dp);
 }
 
 // Lanes per row of the 4-bit kernels for rows of G groups: the whole wave,
@@ -617,7 +626,9 @@ moe_status run_experts_small(const moe_desc* d, const Plan& p, const void* x,
                         wsp<float>(ws, p.o_sgate), wsp<int32_t>(ws, p.o_counts),
                         wsp<int32_t>(ws, p.o_offsets), wsp<int32_t>(ws, p.o_active),
                         wsp<int32_t>(ws, p.o_nactive), wsp<int32_t>(ws, p.o_perm),
-                        wsp<int32_t>(ws, p.o_pos), user_ids, user_w, nullptr, nullptr, nullptr};
+                        wsp<int32_t>(ws, p.o_pos), user_ids, user_w, nullptr, nullptr, nullptr,
+                        route ? wsp<int4>(ws, p.o_slots) : nullptr};
+  dp.slots = dp.ro.slots;
 
   if (wf == MOE_WEIGHTS_U4_G32) return run_experts_u4(d, p, dp, out, residual, ws, s);
 
@@ -643,9 +654,9 @@ moe_status run_experts_small(const moe_desc* d, const Plan& p, const void* x,
   const int u2 = pick_u(maxK / epc);
   dim3 g2((p.H + kDownRPW - 1) / kDownRPW);
   return launch("gemv_down_combine", s, [&] {
-    if (wf == MOE_WEIGHTS_F32) launch_dn3<WF_F32>(u2, g2, s, dp);
-    else if (wf == MOE_WEIGHTS_BF16) launch_dn3<WF_BF16>(u2, g2, s, dp);
-    else launch_dn3<WF_U4>(u2, g2, s, dp);
+    if (wf == MOE_WEIGHTS_F32) launch_dn3<WF_F32>(route, u2, g2, s, dp);
+    else if (wf == MOE_WEIGHTS_BF16) launch_dn3<WF_BF16>(route, u2, g2, s, dp);
+    else launch_dn3<WF_U4>(false, u2, g2, s, dp);
   });
 }
 

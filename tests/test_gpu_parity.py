@@ -93,6 +93,14 @@ SMALL = [
               router_dtype=DT_BF16, shared=True, Is=192, seed_index=35),
     MoeConfig(name="gemv_bf16x_gelu_t1", T=1, H=512, I=256, E=64, k=8, act=ACT_GELU_TANH,
               weight_format=WF_BF16, act_dtype=DT_BF16, router_dtype=DT_BF16, seed_index=36),
+    # one token ranked inside the gate/up kernel: experts past 128 (four
+    # logits a lane, the last 64-expert block ragged), f32 weights, and 1, 2
+    # or 4 features a wave
+    MoeConfig(name="gemv_f32_t1_e256", T=1, H=192, I=96, E=256, k=8, seed_index=69),
+    MoeConfig(name="gemv_bf16_t1_e129", T=1, H=2304, I=96, E=129, k=6, weight_format=WF_BF16,
+              router_dtype=DT_BF16, shared=True, Is=32, seed_index=70),
+    MoeConfig(name="gemv_bf16_t1_h4096", T=1, H=4096, I=32, E=8, k=2, act=ACT_GELU_TANH,
+              weight_format=WF_BF16, seed_index=71),
     MoeConfig(name="gemv_f32_dense_e1", T=3, H=64, I=32, E=1, k=1, seed_index=20),
     MoeConfig(name="gemv_f32_k32", T=2, H=64, I=32, E=256, k=32, seed_index=21),
     MoeConfig(name="gemv_bf16_f32x_t32", T=32, H=2816, I=704, E=128, k=8, act=ACT_GELU_TANH,
