@@ -228,6 +228,10 @@ moe_status moe_route(const moe_desc* desc, int64_t num_tokens, const void* x,
  *   ws, ws_bytes workspace, at least moe_workspace_size(desc, T) bytes
  *
  * `out` must not alias x, the weights or the workspace.  T = 0 is a no-op.
+ * MOE_UNSUPPORTED when hidden > 16384 unless the call takes the bf16 MFMA
+ * path (bf16 weights and activations, T > 32, hidden, intermediate and
+ * shared_intermediate multiples of 64): the decode kernels keep a route's
+ * activation row in LDS.
  */
 moe_status moe_ffn_forward(const moe_desc* desc, int64_t num_tokens,
                            const void* x, const moe_weights* weights,

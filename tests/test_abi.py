@@ -103,6 +103,25 @@ def test_forward_rejects_null_and_small_workspace_on_host(lib):
     assert st == M.MOE_UNSUPPORTED            # misaligned x
 
 
+def test_wide_rows_need_the_bf16_prefill_path(lib):
+    """Rows longer than 16384 are supported only on the bf16 MFMA path
+    (bf16 weights and activations, more than 32 tokens); elsewhere the call
+    is refused before anything is enqueued."""
+    fake = 1 << 20
+    w = M.make_weights(router=None)
+    w.router, w.gate, w.up, w.down = fake, fake, fake, fake
+    for name, T in (("decode_geglu_t1", 1), ("decode_geglu_t1", 8), ("decode_u4_t32", 32)):
+        d = _desc(name, hidden=16416)
+        if name == "decode_u4_t32":
+            w.gate_u4 = w.up_u4 = w.down_u4 = M.U4Matrix(fake, fake, fake)
+        st = lib.moe_ffn_forward(ctypes.byref(d), T, fake, ctypes.byref(w), fake, None, None, None,
+                                 fake, 1 << 40, None)
+        assert st == M.MOE_UNSUPPORTED, name
+        assert "16384" in lib.moe_last_error().decode()
+    d = _desc("prefill_shared_t4096", hidden=16448)
+    assert M.workspace_size(d, 4096) > 0     # the bf16 prefill path plans it
+
+
 def test_zero_tokens_is_a_noop(lib):
     d = _desc()
     w = M.Weights()
