@@ -275,8 +275,12 @@ moe_status run_router(const moe_desc* d, const Plan& p, const void* x, const moe
     auto go = [&](auto xtag, auto rtag, auto nctag) {
       using XT = decltype(xtag);
       constexpr int RDT = decltype(rtag)::value, NC = decltype(nctag)::value;
-      k_router_gemv<XT, RDT, NC><<<grid, 256, 0, s>>>(static_cast<const XT*>(x), w->router,
-          w->router_bias, w->shared_gate_inp, logits, T, p.H, p.E, p.ncols);
+      if (T == 1)
+        k_router_gemv<XT, RDT, NC, 1><<<grid, 256, 0, s>>>(static_cast<const XT*>(x), w->router,
+            w->router_bias, w->shared_gate_inp, logits, T, p.H, p.E, p.ncols);
+      else
+        k_router_gemv<XT, RDT, NC><<<grid, 256, 0, s>>>(static_cast<const XT*>(x), w->router,
+            w->router_bias, w->shared_gate_inp, logits, T, p.H, p.E, p.ncols);
     };
     dispatch_router(xb, rb, nc, go);
   });

@@ -16,10 +16,11 @@ namespace moe {
 // RDT: 0 = f32 router, 1 = bf16 router.  COHERENT: logits are stored at
 // device scope (written through to the point of coherence of all XCDs), so
 // that another workgroup may read them within the same launch.  NC: chunks
-// per thread per block of the row; all loads of a (4-token, block) step are
-// issued before the first is used, with clamped indices so that none sits
-// behind a branch.
-template <typename XT, int RDT, bool COHERENT = false, int NC = 1>
+// per thread per block of the row; TB: tokens per step (1 for one token, so
+// the activation row is read once, else 4); all loads of a (TB-token, block)
+// step are issued before the first is used, with clamped indices so that
+// none sits behind a branch.
+template <typename XT, int RDT, bool COHERENT = false, int NC = 1, int TB = 4>
 __device__ __forceinline__ void router_row(const XT* __restrict__ x, const void* __restrict__ router,
                                            const float* __restrict__ bias,
                                            const void* __restrict__ shared_gate_inp,
@@ -31,18 +32,20 @@ __device__ __forceinline__ void router_row(const XT* __restrict__ x, const void*
       ? reinterpret_cast<const uint8_t*>(router) + (size_t)e * H * (RDT ? 2 : 4)
       : reinterpret_cast<const uint8_t*>(shared_gate_inp);
   const int cpr = H / EPC;
-  __shared__ float red[4][4];
-  for (int t0 = 0; t0 < T; t0 += 4) {
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  __shared__ float red[4][TB];
+  for (int t0 = 0; t0 < T; t0 += TB) {
+    float acc[TB];
+#pragma unroll
+    for (int r = 0; r < TB; ++r) acc[r] = 0.f;
     for (int cb = 0; cb < cpr; cb += 256 * NC) {
       u32x4 wv[NC];
-      float xv[NC][4][EPC];
+      float xv[NC][TB][EPC];
 #pragma unroll
       for (int j = 0; j < NC; ++j) {
         const int c = min(cb + tid + 256 * j, cpr - 1);
         wv[j] = ld16(row + (size_t)c * 16);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
+        for (int r = 0; r < TB; ++r) {
           const XT* xr = x + (size_t)min(t0 + r, T - 1) * H + (size_t)c * EPC;
 #pragma unroll
           for (int q = 0; q < EPC; ++q) {
@@ -63,7 +66,7 @@ __device__ __forceinline__ void router_row(const XT* __restrict__ x, const void*
             for (int q = 0; q < 4; ++q) w[q] = __uint_as_float(wv[j][q]);
           }
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
+          for (int r = 0; r < TB; ++r) {
             float sdot = 0.f;
 #pragma unroll
             for (int q = 0; q < EPC; ++q) sdot = fmaf(w[q], xv[j][r][q], sdot);
@@ -74,12 +77,12 @@ __device__ __forceinline__ void router_row(const XT* __restrict__ x, const void*
     }
     const int wv2 = tid >> 6, ln = tid & 63;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
+    for (int r = 0; r < TB; ++r) {
       float sm = wave_sum(acc[r]);
       if (ln == 0) red[wv2][r] = sm;
     }
     __syncthreads();
-    if (tid < 4 && t0 + tid < T) {
+    if (tid < TB && t0 + tid < T) {
       float sm = red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];
       if (e < E && bias) sm += bias[e];
       float* dst = logits + (size_t)(t0 + tid) * ncols + e;
@@ -93,12 +96,12 @@ __device__ __forceinline__ void router_row(const XT* __restrict__ x, const void*
 // chunks per thread for a row of `cpr` 16-byte chunks (one block when it fits in 4)
 inline int router_nc(int cpr) { return cpr <= 256 ? 1 : cpr <= 512 ? 2 : 4; }
 
-template <typename XT, int RDT, int NC>
+template <typename XT, int RDT, int NC, int TB = 4>
 __global__ __launch_bounds__(256) void k_router_gemv(
     const XT* __restrict__ x, const void* __restrict__ router,
     const float* __restrict__ bias, const void* __restrict__ shared_gate_inp,
     float* __restrict__ logits, int T, int H, int E, int ncols) {
-  router_row<XT, RDT, false, NC>(x, router, bias, shared_gate_inp, logits, T, H, E, ncols,
+  router_row<XT, RDT, false, NC, TB>(x, router, bias, shared_gate_inp, logits, T, H, E, ncols,
                                  blockIdx.x);
 }
 
