@@ -238,10 +238,9 @@ __device__ __forceinline__ void route_one_token(const float* __restrict__ l, int
     const int ce = e >> 6, le = e & 63;
 #pragma unroll
     for (int c = 0; c < C; ++c) {
-      if (c == ce) {
-        live[c] &= ~(1ull << le);
-        sel[c] |= 1ull << le;
-      }
+      const uint64_t bit = c == ce ? 1ull << le : 0ull;  // selects, no branch
+      live[c] &= ~bit;
+      sel[c] |= bit;
       ord[c] = (c == ce && lane == le) ? 0u : ord[c];
     }
     if (j == 0) top = M;
@@ -899,9 +898,16 @@ __global__ __launch_bounds__(256) void k_dec_down3(Dec2Params p) {
     if (lane < kSlotTab) tab = p.slots[lane];
     na = min(max(__builtin_amdgcn_readlane(tab.x, 0), 0), min(gmax, p.k + (p.Is > 0 ? 1 : 0)));
   }
-  for (int i = tid; i < 4 * TMAX * RPW; i += 256) (&part[0][0][0])[i] = 0.f;
-  __syncthreads();
-  if constexpr (!ONE) na = min(*p.n_active, gmax);
+  // ONE: each wave sums its slots in registers and stores its partials once
+  // at the end, so no zeroing (and no barrier) comes first
+  float osum[RPW];
+#pragma unroll
+  for (int q = 0; q < RPW; ++q) osum[q] = 0.f;
+  if constexpr (!ONE) {
+    for (int i = tid; i < 4 * TMAX * RPW; i += 256) (&part[0][0][0])[i] = 0.f;
+    __syncthreads();
+    na = min(*p.n_active, gmax);
+  }
   const int R = p.T * p.k;
   auto slot_group = [&](int s) {
     if constexpr (ONE) return ws_group(__builtin_amdgcn_readlane(tab.x, 1 + s), p.E, p.Is > 0);
@@ -974,7 +980,8 @@ __global__ __launch_bounds__(256) void k_dec_down3(Dec2Params p) {
 #pragma unroll
       for (int q = 0; q < RPW; ++q) {
         const float v = wave_sum(acc[q]);
-        if (lane == 0) part[wave][t][q] += wgt * v;
+        if constexpr (ONE) osum[q] += wgt * v;
+        else if (lane == 0) part[wave][t][q] += wgt * v;
       }
     }
 #pragma unroll
@@ -983,6 +990,12 @@ __global__ __launch_bounds__(256) void k_dec_down3(Dec2Params p) {
       for (int q = 0; q < RPW; ++q) { wc[q][u] = wn[q][u]; sc[q][u] = sn[q][u]; mc[q][u] = mnx[q][u]; }
     s = sn_;
     g = gn;
+  }
+  if constexpr (ONE) {
+    if (lane == 0) {
+#pragma unroll
+      for (int q = 0; q < RPW; ++q) part[wave][0][q] = osum[q];
+    }
   }
   __syncthreads();
   for (int i = tid; i < p.T * RPW; i += 256) {
