@@ -7,4 +7,4 @@ from .generator import (MoeInputs, U4Weights, generate, x_rows,
                         router_bias_values, norm_weight_values, residual_values, grad_inputs,
                         f32_to_bf16_bits, f32_to_f16_bits,
                         normal_np, normal_torch, codes_np, codes_torch,
-                        stream_key)
+                        stream_key, tied_router_inputs)

@@ -62,6 +62,8 @@ TID_GRAD_GU = 15
 TID_U4_CODES = 16      # + matrix index (0 gate, 1 up, 2 down)
 TID_GRAD_DH = 24
 TID_U4_SCALES = 32     # + matrix index
+TID_TIES_ROUTER = 40   # integer router rows with exact ties
+TID_TIES_X = 41
 ATTEMPT_SHIFT = 20     # resampled x rows use TID_X + (attempt << 20)
 
 
@@ -305,6 +307,32 @@ def grad_inputs(cfg: MoeConfig) -> dict:
             "dout": nrm(TID_GRAD_DOUT, (T, H), 1.0),
             "gate_up": nrm(TID_GRAD_GU, (T * k, 2 * I), 2.0),
             "dh": nrm(TID_GRAD_DH, (T * k, I), 1.0)}
+
+
+def tied_router_inputs(cfg: MoeConfig, zero_top: bool = False):
+    """Router rows [E, H] and token rows [T, H] (float32) of small integers,
+    so that every logit is an exact integer in f32, bf16 inputs and f64
+    alike, and equal logits are exact ties.  Default: rows repeat with
+    period max(E // 4, 1) (experts e and e + E//4 tie), entries in -2..2,
+    x in -3..3.  zero_top: every third expert (e % 3 == 1) has an all-zero
+    row, so the largest logit is 0 (reached as +0 or -0 by the sums) for
+    E/3 experts, the others -1 or below (entries in -2..0 with a -1 first,
+    x in 1..3)."""
+    E, H, T = cfg.E, cfg.H, cfg.T
+    def ints(tid, n, lo, hi):
+        u = uniform_np(stream_key(cfg.seed, tid), np.arange(n, dtype=np.uint64))
+        return (lo + np.floor(u * (hi - lo + 1))).astype(np.float32)
+    if zero_top:
+        r = ints(TID_TIES_ROUTER, E * H, -2, 0).reshape(E, H)
+        r[:, 0] = -1.0
+        r[np.arange(E) % 3 == 1] = 0.0
+        x = ints(TID_TIES_X, T * H, 1, 3).reshape(T, H)
+    else:
+        D = max(E // 4, 1)
+        base = ints(TID_TIES_ROUTER, D * H, -2, 2).reshape(D, H)
+        r = base[np.arange(E) % D]
+        x = ints(TID_TIES_X, T * H, -3, 3).reshape(T, H)
+    return r, x
 
 
 def generate(cfg: MoeConfig, backend: str = "numpy", device=None) -> MoeInputs:

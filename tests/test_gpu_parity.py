@@ -336,3 +336,41 @@ def test_max_hidden_decode():
     cfg = MoeConfig(name="decode_h16384", T=2, H=16384, I=256, E=8, k=2, weight_format=WF_BF16,
                     router_dtype=DT_BF16, seed_index=55)
     check_case(Case(cfg))
+
+
+# Exact ties in the router logits: integer router rows that repeat (or are
+# all zero) and integer activations make equal logits bit-identical on both
+# sides, so the lower expert index must win every tie, on every routing
+# kernel: one token ranked in the gate/up kernel (up to 128 and past 128
+# experts), the wave-per-token decode routing (T <= 4), rank counting (T*E
+# <= 1024), row selection, and the prefill top-k after the MFMA router.
+TIE_CASES = [
+    (MoeConfig(name="ties_t1_e128", T=1, H=256, I=64, E=128, k=8, act=ACT_GELU_TANH,
+               weight_format=WF_BF16, seed_index=74), False),
+    (MoeConfig(name="ties_t1_e200", T=1, H=192, I=64, E=200, k=6, seed_index=75), False),
+    (MoeConfig(name="ties_t1_zero", T=1, H=128, I=64, E=48, k=8, weight_format=WF_BF16,
+               router_dtype=DT_BF16, seed_index=76), True),
+    (MoeConfig(name="ties_t3", T=3, H=128, I=64, E=16, k=4, seed_index=77), False),
+    (MoeConfig(name="ties_t8_rank", T=8, H=128, I=64, E=64, k=6, weight_format=WF_BF16,
+               router_dtype=DT_BF16, seed_index=78), False),
+    (MoeConfig(name="ties_t20_rows_zero", T=20, H=64, I=32, E=96, k=5, seed_index=79), True),
+    (MoeConfig(name="ties_prefill", T=300, H=128, I=64, E=16, k=4, weight_format=WF_BF16,
+               act_dtype=DT_BF16, router_dtype=DT_BF16, seed_index=80), False),
+]
+
+
+@pytest.mark.parametrize("cfg,zero_top", TIE_CASES, ids=[c.name for c, _ in TIE_CASES])
+def test_tied_logits_lowest_index_wins(cfg, zero_top):
+    from moe_synth import tied_router_inputs
+    from oracle import moe_oracle as O
+    case = Case(cfg)
+    r, x = tied_router_inputs(cfg, zero_top)
+    case.dev.router.copy_(torch.from_numpy(r).to(case.dev.router.dtype))
+    case.dev.x.copy_(torch.from_numpy(x).to(case.dev.x.dtype))
+    torch.cuda.synchronize()
+    # the inputs do tie inside every token's top k + 1 (and the logits are integers)
+    L = O.router_logits(x.astype(np.float64), r.astype(np.float64), None)
+    assert (L == np.round(L)).all()
+    top = -np.sort(-L, axis=1)[:, :cfg.k + 1]
+    assert (np.diff(top, axis=1) == 0).any(axis=1).all()
+    check_case(case)
