@@ -473,8 +473,12 @@ __global__ __launch_bounds__(256) void k_router_route(const XT* __restrict__ x,
                                                       int E, int k, int ncols, RouteMode rm,
                                                       int has_shared, int* __restrict__ ticket,
                                                       SmallRouteOut o) {
-  router_row<XT, RDT, true, NC>(x, router, bias, shared_gate_inp, logits, T, H, E, ncols,
-                                blockIdx.x);
+  if (H / (RDT ? 8 : 4) <= 256 * NC && T <= kRowTokens)
+    router_row_few<XT, RDT, true, NC>(x, router, bias, shared_gate_inp, logits, T, H, E, ncols,
+                                      blockIdx.x);
+  else
+    router_row<XT, RDT, true, NC>(x, router, bias, shared_gate_inp, logits, T, H, E, ncols,
+                                  blockIdx.x);
   __shared__ int s_last;
   __builtin_amdgcn_s_waitcnt(0);  // this wave's logit stores have completed
   __syncthreads();

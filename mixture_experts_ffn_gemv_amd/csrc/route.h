@@ -93,6 +93,92 @@ __device__ __forceinline__ void router_row(const XT* __restrict__ x, const void*
   }
 }
 
+// Router row e for at most kRowTokens tokens when the row fits one block of
+// NC chunks a thread: the weight chunks are loaded once, every token's
+// partial dot product stays in a register, and one reduction at the end
+// (one barrier) gives all the token's logits; tokens are walked in steps of
+// 4 with all activation loads of a step issued together.  COHERENT as in
+// router_row.
+constexpr int kRowTokens = 32;
+template <typename XT, int RDT, bool COHERENT, int NC>
+__device__ __forceinline__ void router_row_few(const XT* __restrict__ x, const void* __restrict__ router,
+                                               const float* __restrict__ bias,
+                                               const void* __restrict__ shared_gate_inp,
+                                               float* __restrict__ logits, int T, int H, int E,
+                                               int ncols, int e) {
+  constexpr int EPC = RDT ? 8 : 4;  // router elements per 16-byte chunk
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint8_t* row = (e < E)
+      ? reinterpret_cast<const uint8_t*>(router) + (size_t)e * H * (RDT ? 2 : 4)
+      : reinterpret_cast<const uint8_t*>(shared_gate_inp);
+  const int cpr = H / EPC;
+  __shared__ float red[4][kRowTokens];
+  float w[NC][EPC];
+#pragma unroll
+  for (int j = 0; j < NC; ++j) {
+    const int c = min(tid + 256 * j, cpr - 1);
+    const u32x4 v = ld16(row + (size_t)c * 16);
+    const bool ok = tid + 256 * j < cpr;
+    if constexpr (RDT) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        w[j][2 * q] = ok ? bf16lo(v[q]) : 0.f;
+        w[j][2 * q + 1] = ok ? bf16hi(v[q]) : 0.f;
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) w[j][q] = ok ? __uint_as_float(v[q]) : 0.f;
+    }
+  }
+  float acc[kRowTokens];
+#pragma unroll
+  for (int t0 = 0; t0 < kRowTokens; t0 += 4) {
+    if (t0 < T) {
+      float xv[4][NC][EPC];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const XT* xr = x + (size_t)min(t0 + r, T - 1) * H;
+#pragma unroll
+        for (int j = 0; j < NC; ++j) {
+          const int c = min(tid + 256 * j, cpr - 1);
+#pragma unroll
+          for (int q = 0; q < EPC; ++q) {
+            if constexpr (sizeof(XT) == 4) xv[r][j][q] = xr[(size_t)c * EPC + q];
+            else xv[r][j][q] = bf16_to_f32(xr[(size_t)c * EPC + q]);
+          }
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float sdot = 0.f;
+#pragma unroll
+        for (int j = 0; j < NC; ++j)
+#pragma unroll
+          for (int q = 0; q < EPC; ++q) sdot = fmaf(w[j][q], xv[r][j][q], sdot);
+        acc[t0 + r] = sdot;
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[t0 + r] = 0.f;
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < kRowTokens; ++t) {
+    if (t < T) {
+      const float sm = wave_sum(acc[t]);
+      if (lane == 0) red[wave][t] = sm;
+    }
+  }
+  __syncthreads();
+  if (tid < T) {
+    float sm = red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];
+    if (e < E && bias) sm += bias[e];
+    float* dst = logits + (size_t)tid * ncols + e;
+    if constexpr (COHERENT) __hip_atomic_store(dst, sm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else *dst = sm;
+  }
+}
+
 // chunks per thread for a row of `cpr` 16-byte chunks (one block when it fits in 4)
 inline int router_nc(int cpr) { return cpr <= 256 ? 1 : cpr <= 512 ? 2 : 4; }
 
