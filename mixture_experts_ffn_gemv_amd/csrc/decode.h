@@ -1,6 +1,6 @@
 // Decode path (few tokens, T <= 32): three launches per layer.
 //
-//   T = 1, f32 or bf16 weights:  k_router_gemv  -> k_dec_gateup3<ROUTE> -> k_dec_down3
+//   T = 1, f32 or bf16 weights:  k_router_gemv  -> k_dec_gateup3<ONE> -> k_dec_down3<ONE>
 //   otherwise:                   k_router_route -> k_dec_gateup3        -> k_dec_down3
 //
 // k_router_gemv   router logits only (one workgroup per router row).
@@ -14,11 +14,12 @@
 //                 split K into 16-byte chunks and issue every weight load of
 //                 those rows before touching the activations.  Only the
 //                 touched experts' weights are read, each byte once.  With
-//                 ROUTE (one token) every wave ranks the token's logits
-//                 itself (route_one_token, the same keys, order and weights
-//                 as the routing workgroup) to find its expert, and
-//                 workgroup (0,0) writes the routing for k_dec_down3 and
-//                 the caller: one token's top-k costs a wave less than a
+//                 ONE (one token) every wave ranks the token's logits
+//                 itself (route_one_token: the selection order and weights
+//                 of the routing workgroup) to find its expert, and one
+//                 wave of workgroup (0,0) writes the routing (and the slot
+//                 table k_dec_down3<ONE> reads) for the down kernel and the
+//                 caller: one token's top-k costs a wave less than a
 //                 grid-wide handoff inside the router launch does.
 // k_dec_down3     work item = block of output features; the 4 waves split
 //                 the touched experts, each loading the expert's down rows
@@ -720,12 +721,12 @@ __device__ __forceinline__ void route_write(const Dec2Params& p, const OneRoute&
 
 // gate/up: each wave owns one feature f of one touched expert: its gate row
 // and its up row, full K, lane l holding chunks l, l+64, ... (U of them).
-// DIRECT (every expert has exactly one route, i.e. one token): the lane's
-// activation chunks are loaded straight into registers.  Otherwise the
-// activations of up to rc routes are staged in LDS as f32 per pass.
-template <int WF, int ACT, int U, bool DIRECT, bool ROUTE = false>
+// ONE (one token, routed in this kernel: every expert has exactly one
+// route): the lane's activation chunks are loaded straight into registers.
+// Otherwise the activations of up to rc routes are staged in LDS as f32 per
+// pass.
+template <int WF, int ACT, int U, bool ONE>
 __global__ __launch_bounds__(256) void k_dec_gateup3(Dec2Params p) {
-  static_assert(!ROUTE || DIRECT, "routing in the kernel is for one token");
   constexpr int EPC = WTraits<WF>::EPC;
   extern __shared__ float xs[];  // [rc][H] (staged path only)
   const int s = blockIdx.x;
@@ -735,7 +736,7 @@ __global__ __launch_bounds__(256) void k_dec_gateup3(Dec2Params p) {
   // follow while they are in flight.
   int na, slot_g, route_r = 0;
   OneRoute rt;
-  if constexpr (ROUTE) {
+  if constexpr (ONE) {
     if (p.E <= 128) route_slot<2>(p, s, na, slot_g, route_r, rt);
     else route_slot<4>(p, s, na, slot_g, route_r, rt);
   } else {
@@ -761,7 +762,7 @@ __global__ __launch_bounds__(256) void k_dec_gateup3(Dec2Params p) {
   const int fc = min(f, N - 1);  // waves past the last feature read a valid row, unused
   const size_t row = shared ? (size_t)fc : (size_t)g * N + fc;
 
-  if constexpr (DIRECT) {
+  if constexpr (ONE) {
     int r = 0, t = 0;
     float ag = 0.f, au = 0.f;
     for (int kb = 0; kb < cpr; kb += 64 * U) {
@@ -775,18 +776,10 @@ __global__ __launch_bounds__(256) void k_dec_gateup3(Dec2Params p) {
         load_chunk<WF, true>(Mg, row, p.H, c, ok, wg[u], sg[u], mg[u]);
         load_chunk<WF, true>(Mu, row, p.H, c, ok, wu[u], su[u], mu[u]);
       }
-      if constexpr (ROUTE) {
-        // workgroup (0, 0) holds slot 0, a routed expert, and feature 0
-        if (kb == 0 && blockIdx.x == 0 && blockIdx.y == 0 && wave == 0) route_write(p, rt);
-      }
+      // workgroup (0, 0) holds slot 0, a routed expert, and feature 0
+      if (kb == 0 && blockIdx.x == 0 && blockIdx.y == 0 && wave == 0) route_write(p, rt);
       if (kb == 0 && !shared) {  // the expert's one route, and its token
-        if constexpr (ROUTE) {
-          r = route_r;
-        } else {
-          int count = p.counts[g], base = p.offsets[g];
-          ws_span(base, count, R);
-          r = ws_route(p.perm[base], R);
-        }
+        r = route_r;
         t = r / p.k;
       }
 #pragma unroll

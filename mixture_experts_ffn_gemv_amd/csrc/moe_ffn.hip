@@ -485,27 +485,22 @@ int pick_u(int cpr) {
   return 8;
 }
 
-template <int WF, int ACT, bool DIRECT, bool ROUTE>
+template <int WF, int ACT, bool ONE>
 void launch_gu3_u(int u, dim3 grid, size_t lds, hipStream_t s, const Dec2Params& dp) {
   switch (u) {
-    case 1: k_dec_gateup3<WF, ACT, 1, DIRECT, ROUTE><<<grid, 256, lds, s>>>(dp); break;
-    case 2: k_dec_gateup3<WF, ACT, 2, DIRECT, ROUTE><<<grid, 256, lds, s>>>(dp); break;
-    case 3: k_dec_gateup3<WF, ACT, 3, DIRECT, ROUTE><<<grid, 256, lds, s>>>(dp); break;
-    case 4: k_dec_gateup3<WF, ACT, 4, DIRECT, ROUTE><<<grid, 256, lds, s>>>(dp); break;
-    case 6: k_dec_gateup3<WF, ACT, 6, DIRECT, ROUTE><<<grid, 256, lds, s>>>(dp); break;
-    default: k_dec_gateup3<WF, ACT, 8, DIRECT, ROUTE><<<grid, 256, lds, s>>>(dp); break;
+    case 1: k_dec_gateup3<WF, ACT, 1, ONE><<<grid, 256, lds, s>>>(dp); break;
+    case 2: k_dec_gateup3<WF, ACT, 2, ONE><<<grid, 256, lds, s>>>(dp); break;
+    case 3: k_dec_gateup3<WF, ACT, 3, ONE><<<grid, 256, lds, s>>>(dp); break;
+    case 4: k_dec_gateup3<WF, ACT, 4, ONE><<<grid, 256, lds, s>>>(dp); break;
+    case 6: k_dec_gateup3<WF, ACT, 6, ONE><<<grid, 256, lds, s>>>(dp); break;
+    default: k_dec_gateup3<WF, ACT, 8, ONE><<<grid, 256, lds, s>>>(dp); break;
   }
 }
-// direct: one token (its route read in place); route: also rank its router
-// logits in the kernel (one token, f32 or bf16 weights)
+// one: one token, ranked in the kernel (no LDS); else the routes' activations staged
 template <int WF, int ACT>
-void launch_gu3(bool direct, bool route, int u, dim3 grid, size_t lds, hipStream_t s,
-                const Dec2Params& dp) {
-  if constexpr (WF != WF_U4) {
-    if (route) return launch_gu3_u<WF, ACT, true, true>(u, grid, 0, s, dp);
-  }
-  if (direct) launch_gu3_u<WF, ACT, true, false>(u, grid, 0, s, dp);
-  else launch_gu3_u<WF, ACT, false, false>(u, grid, lds, s, dp);
+void launch_gu3(bool one, int u, dim3 grid, size_t lds, hipStream_t s, const Dec2Params& dp) {
+  if (one) launch_gu3_u<WF, ACT, true>(u, grid, 0, s, dp);
+  else launch_gu3_u<WF, ACT, false>(u, grid, lds, s, dp);
 }
 template <int WF, bool ONE>
 void launch_dn3_u(int u, dim3 grid, hipStream_t s, const Dec2Params& dp) {
@@ -521,10 +516,8 @@ void launch_dn3_u(int u, dim3 grid, hipStream_t s, const Dec2Params& dp) {
 // one: one token whose routing the gate/up kernel wrote as a slot table
 template <int WF>
 void launch_dn3(bool one, int u, dim3 grid, hipStream_t s, const Dec2Params& dp) {
-  if constexpr (WF != WF_U4) {
-    if (one) return launch_dn3_u<WF, true>(u, grid, s, dp);
-  }
-  launch_dn3_u<WF, false>(u, grid, s, dp);
+  if (one) launch_dn3_u<WF, true>(u, grid, s, dp);
+  else launch_dn3_u<WF, false>(u, grid, s, dp);
 }
 
 // Lanes per row of the 4-bit kernels for rows of G groups: the whole wave,
@@ -637,21 +630,17 @@ moe_status run_experts_small(const moe_desc* d, const Plan& p, const void* x,
   if (wf == MOE_WEIGHTS_U4_G32) return run_experts_u4(d, p, dp, out, residual, ws, s);
 
   const int u1 = pick_u(p.H / epc);
-  const bool direct = p.T == 1;
   const int maxN = std::max(p.I, p.Is);
   dim3 g1(p.max_groups, (maxN + kGUWaves - 1) / kGUWaves);
   const size_t lds = (size_t)p.rc * p.H * 4;
   MOE_TRY(launch("gemv_gateup", s, [&] {
     const bool silu = d->activation == MOE_ACT_SILU;
     if (wf == MOE_WEIGHTS_F32) {
-      if (silu) launch_gu3<WF_F32, ACT_SILU>(direct, route, u1, g1, lds, s, dp);
-      else launch_gu3<WF_F32, ACT_GELU_TANH>(direct, route, u1, g1, lds, s, dp);
-    } else if (wf == MOE_WEIGHTS_BF16) {
-      if (silu) launch_gu3<WF_BF16, ACT_SILU>(direct, route, u1, g1, lds, s, dp);
-      else launch_gu3<WF_BF16, ACT_GELU_TANH>(direct, route, u1, g1, lds, s, dp);
+      if (silu) launch_gu3<WF_F32, ACT_SILU>(route, u1, g1, lds, s, dp);
+      else launch_gu3<WF_F32, ACT_GELU_TANH>(route, u1, g1, lds, s, dp);
     } else {
-      if (silu) launch_gu3<WF_U4, ACT_SILU>(direct, false, u1, g1, lds, s, dp);
-      else launch_gu3<WF_U4, ACT_GELU_TANH>(direct, false, u1, g1, lds, s, dp);
+      if (silu) launch_gu3<WF_BF16, ACT_SILU>(route, u1, g1, lds, s, dp);
+      else launch_gu3<WF_BF16, ACT_GELU_TANH>(route, u1, g1, lds, s, dp);
     }
   }));
   const int maxK = std::max(p.I, p.Is);
@@ -659,8 +648,7 @@ moe_status run_experts_small(const moe_desc* d, const Plan& p, const void* x,
   dim3 g2((p.H + kDownRPW - 1) / kDownRPW);
   return launch("gemv_down_combine", s, [&] {
     if (wf == MOE_WEIGHTS_F32) launch_dn3<WF_F32>(route, u2, g2, s, dp);
-    else if (wf == MOE_WEIGHTS_BF16) launch_dn3<WF_BF16>(route, u2, g2, s, dp);
-    else launch_dn3<WF_U4>(false, u2, g2, s, dp);
+    else launch_dn3<WF_BF16>(route, u2, g2, s, dp);
   });
 }
 
