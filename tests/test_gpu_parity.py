@@ -101,6 +101,12 @@ SMALL = [
               router_dtype=DT_BF16, shared=True, Is=32, seed_index=70),
     MoeConfig(name="gemv_bf16_t1_h4096", T=1, H=4096, I=32, E=8, k=2, act=ACT_GELU_TANH,
               weight_format=WF_BF16, seed_index=71),
+    # one token: every expert selected (k = E), a single expert, and one
+    # expert alone in the second 64-lane block of the ranking
+    MoeConfig(name="gemv_f32_t1_k_eq_e", T=1, H=128, I=64, E=8, k=8, seed_index=81),
+    MoeConfig(name="gemv_bf16_t1_dense_e1", T=1, H=128, I=64, E=1, k=1, weight_format=WF_BF16,
+              router_dtype=DT_BF16, shared=True, Is=64, seed_index=82),
+    MoeConfig(name="gemv_f32_t1_e65", T=1, H=96, I=32, E=65, k=3, seed_index=83),
     MoeConfig(name="gemv_f32_dense_e1", T=3, H=64, I=32, E=1, k=1, seed_index=20),
     MoeConfig(name="gemv_f32_k32", T=2, H=64, I=32, E=256, k=32, seed_index=21),
     MoeConfig(name="gemv_bf16_f32x_t32", T=32, H=2816, I=704, E=128, k=8, act=ACT_GELU_TANH,
