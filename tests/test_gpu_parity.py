@@ -336,11 +336,13 @@ def test_graph_replay_matches_eager(name):
     assert int(ws[:M.WORKSPACE_ZERO_BYTES].count_nonzero()) == 0
 
 
-def test_max_hidden_decode():
+@pytest.mark.parametrize("T", [2, 1])
+def test_max_hidden_decode(T):
     """hidden = 16384, the largest the decode kernels take (several K passes
-    per lane), bf16 weights, two tokens."""
-    cfg = MoeConfig(name="decode_h16384", T=2, H=16384, I=256, E=8, k=2, weight_format=WF_BF16,
-                    router_dtype=DT_BF16, seed_index=55)
+    per lane), bf16 weights; two tokens (routes staged in LDS) and one token
+    (ranked in the gate/up kernel, four K blocks a lane)."""
+    cfg = MoeConfig(name=f"decode_h16384_t{T}", T=T, H=16384, I=256, E=8, k=2,
+                    weight_format=WF_BF16, router_dtype=DT_BF16, seed_index=55)
     check_case(Case(cfg))
 
 
