@@ -382,3 +382,35 @@ def test_tied_logits_lowest_index_wins(cfg, zero_top):
     top = -np.sort(-L, axis=1)[:, :cfg.k + 1]
     assert (np.diff(top, axis=1) == 0).any(axis=1).all()
     check_case(case)
+
+
+def _one_token_sweep(n=16, seed=0x1E7):
+    """A fixed, seeded list of one-token layers for the in-kernel ranking:
+    expert counts 1..256, k up to min(E, 32), row lengths and dtypes mixed,
+    with or without a shared expert, softmax or sigmoid gating, with or
+    without renormalisation, and a weight scale."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        E = int(rng.choice([1, 2, 7, 31, 64, 65, 100, 128, 129, 191, 256]))
+        k = int(rng.integers(1, min(E, 32) + 1))
+        wf = int(rng.choice([WF_F32, WF_BF16]))
+        shared = bool(rng.integers(0, 2))
+        cfg = MoeConfig(name=f"sweep_t1_{i}_e{E}_k{k}", T=1, H=32 * int(rng.integers(2, 33)),
+                        I=32 * int(rng.integers(1, 9)), E=E, k=k,
+                        act=int(rng.choice([ACT_SILU, ACT_GELU_TANH])), weight_format=wf,
+                        act_dtype=int(rng.choice([DT_F32, DT_BF16])),
+                        router_dtype=int(rng.choice([DT_F32, DT_BF16])), shared=shared,
+                        Is=32 * int(rng.integers(1, 5)) if shared else 0, seed_index=100 + i)
+        route = dict(gating=int(rng.integers(0, 2)), normalize=bool(rng.integers(0, 2)),
+                     scale=float(rng.choice([1.0, 2.5])))
+        out.append((cfg, route))
+    return out
+
+
+SWEEP = _one_token_sweep()
+
+
+@pytest.mark.parametrize("cfg,route", SWEEP, ids=[c.name for c, _ in SWEEP])
+def test_one_token_sweep(cfg, route):
+    check_case(Case(cfg, **route))
