@@ -414,3 +414,34 @@ SWEEP = _one_token_sweep()
 @pytest.mark.parametrize("cfg,route", SWEEP, ids=[c.name for c, _ in SWEEP])
 def test_one_token_sweep(cfg, route):
     check_case(Case(cfg, **route))
+
+
+def _few_token_sweep(n=10, seed=0x5E7):
+    """A fixed, seeded list of 2..32-token decode layers: the router rows
+    with one to four chunks a thread (or longer rows, walked in blocks), and
+    the routing workgroup's three strategies (a wave per token at T <= 4,
+    rank counting, row selection), f32, bf16 and 4-bit weights."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        T = int(rng.choice([2, 3, 4, 5, 9, 17, 32]))
+        E = int(rng.choice([4, 16, 40, 64, 128, 200]))
+        k = int(rng.integers(1, min(E, 8) + 1))
+        wf = int(rng.choice([WF_F32, WF_BF16, WF_U4]))
+        shared = wf != WF_U4 and bool(rng.integers(0, 2))
+        cfg = MoeConfig(name=f"sweep_t{T}_{i}_e{E}_k{k}", T=T, H=32 * int(rng.integers(2, 161)),
+                        I=32 * int(rng.integers(1, 7)), E=E, k=k,
+                        act=int(rng.choice([ACT_SILU, ACT_GELU_TANH])), weight_format=wf,
+                        act_dtype=int(rng.choice([DT_F32, DT_BF16])),
+                        router_dtype=int(rng.choice([DT_F32, DT_BF16])), shared=shared,
+                        Is=32 * int(rng.integers(1, 5)) if shared else 0, seed_index=200 + i)
+        out.append(cfg)
+    return out
+
+
+FEW = _few_token_sweep()
+
+
+@pytest.mark.parametrize("cfg", FEW, ids=[c.name for c in FEW])
+def test_few_token_sweep(cfg):
+    check_case(Case(cfg))
