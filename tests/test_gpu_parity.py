@@ -445,3 +445,33 @@ FEW = _few_token_sweep()
 @pytest.mark.parametrize("cfg", FEW, ids=[c.name for c in FEW])
 def test_few_token_sweep(cfg):
     check_case(Case(cfg))
+
+
+def _prefill_sweep(n=8, seed=0x9F1):
+    """A fixed, seeded list of bf16 prefill layers (33..1200 tokens) whose
+    experts average fewer or more than the 96 routes a tile needs for the
+    direct-to-LDS GEMM, ragged in every tile dimension, with or without a
+    shared expert and a router bias."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        E = int(rng.choice([2, 4, 8, 16, 32]))
+        k = int(rng.integers(1, min(E, 4) + 1))
+        T = int(rng.integers(33, 1201))
+        shared = bool(rng.integers(0, 2))
+        cfg = MoeConfig(name=f"sweep_prefill_{i}_t{T}_e{E}_k{k}", T=T,
+                        H=64 * int(rng.integers(1, 9)), I=64 * int(rng.integers(1, 7)), E=E, k=k,
+                        act=int(rng.choice([ACT_SILU, ACT_GELU_TANH])), weight_format=WF_BF16,
+                        act_dtype=DT_BF16, router_dtype=DT_BF16, shared=shared,
+                        Is=64 * int(rng.integers(1, 4)) if shared else 0,
+                        bias=int(rng.choice([0, BIAS_ZIPF])), seed_index=300 + i)
+        out.append(cfg)
+    return out
+
+
+PREFILL_SWEEP = _prefill_sweep()
+
+
+@pytest.mark.parametrize("cfg", PREFILL_SWEEP, ids=[c.name for c in PREFILL_SWEEP])
+def test_prefill_sweep(cfg):
+    check_case(Case(cfg))
