@@ -199,9 +199,9 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 // lowest still-live expert whose image is M (ballots over the lanes, the
 // live set a wave-uniform bit mask, since taken and absent experts both read
 // as image 0), which is exactly the maximum of the rank keys.  Lane j < k
-// returns slot j's expert and routing weight; `sel` returns the selected
-// experts as bit masks (expert 64c + b at bit b of sel[c]).  Every lane must
-// take part.
+// returns the expert and routing weight of top-k position j; `sel` returns
+// the selected experts as bit masks (expert 64c + b at bit b of sel[c]).
+// Every lane must take part.
 template <int C>
 __device__ __forceinline__ void route_one_token(const float* __restrict__ l, int E, int k,
                                                 RouteMode rm, int& id, float& w,
@@ -630,7 +630,7 @@ constexpr int kGUWaves = 4;  // features per gate/up workgroup (one per wave)
 // expert, its route the expert's top-k position; slot k is the shared
 // expert.
 struct OneRoute {
-  int id;           // lane j < k: slot j's expert
+  int id;           // lane j < k: the expert of top-k position j
   float w;          // and its routing weight
   uint64_t sel[4];  // selected experts, expert 64c + b at bit b of sel[c]
 };
