@@ -202,6 +202,7 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 // returns the expert and routing weight of top-k position j; `sel` returns
 // the selected experts as bit masks (expert 64c + b at bit b of sel[c]).
 // Every lane must take part.
+static_assert(MOE_MAX_EXPERTS_DEV <= 4 * 64, "one-token ranking holds at most 4 logits a lane");
 template <int C>
 __device__ __forceinline__ void route_one_token(const float* __restrict__ l, int E, int k,
                                                 RouteMode rm, int& id, float& w,
