@@ -64,6 +64,7 @@ TID_GRAD_DH = 24
 TID_U4_SCALES = 32     # + matrix index
 TID_TIES_ROUTER = 40   # integer router rows with exact ties
 TID_TIES_X = 41
+TID_EXPERT_SCALE = 42  # per-expert routing scale [E]
 ATTEMPT_SHIFT = 20     # resampled x rows use TID_X + (attempt << 20)
 
 
@@ -285,6 +286,13 @@ def norm_weight_values(cfg: MoeConfig) -> np.ndarray:
     """Pre-FFN RMSNorm weight [H] (float32), uniform in [0.5, 1.5)."""
     key = stream_key(cfg.seed, TID_NORM)
     u = uniform_np(key, np.arange(cfg.H, dtype=np.uint64))
+    return (0.5 + u).astype(np.float32)
+
+
+def expert_scale_values(cfg: MoeConfig) -> np.ndarray:
+    """Per-expert routing scale [E] (float32), uniform in [0.5, 1.5)."""
+    key = stream_key(cfg.seed, TID_EXPERT_SCALE)
+    u = uniform_np(key, np.arange(cfg.E, dtype=np.uint64))
     return (0.5 + u).astype(np.float32)
 
 

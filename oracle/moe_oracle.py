@@ -12,9 +12,10 @@ order"):
 1. router logits  l = x . Wr^T  (+ per-expert bias, as ferrox-models
    decoder.rs adds in gpt_oss_ffn before selection)
 2. softmax over all experts (or a sigmoid per expert), top-k by score
-   (stable sort, so the lower expert index wins a tie), renormalise the k
-   selected scores to sum to one (hf2q softmax_topk_renorm_cpu), times a
-   weight scale
+   (stable sort, so the lower expert index wins a tie), optionally times a
+   per-expert scale (mlx-native moe_gather_topk_weights_encode),
+   renormalise the k selected scores to sum to one (hf2q
+   softmax_topk_renorm_cpu), times a weight scale
 3. for each selected expert e: g = Wg[e] x, u = Wu[e] x,
    h = act(g) * u, y = Wd[e] h; out += w * y, in slot order
 4. shared expert (when present): s = sigmoid(x . w_sg),
@@ -188,25 +189,33 @@ def gating_scores(l, gating: int = GATING_SOFTMAX) -> np.ndarray:
 
 
 def route(logits, k: int, normalize: bool = True, gating: int = GATING_SOFTMAX,
-          scale: float = 1.0):
-    """Scores -> top-k -> renormalise -> scale, per token.
+          scale: float = 1.0, expert_scale=None):
+    """Scores -> top-k -> per-expert scale -> renormalise -> scale, per token.
 
     Returns (ids [T, k] int64, weights [T, k] float64); slot j holds the
-    j-th largest score.  Without ``normalize`` the raw scores of the winners
-    are returned.  Every weight is then multiplied by ``scale`` (llama.cpp's
-    w_scale, which ferrox-models names in gpt_oss_ffn; the pages give only
-    the name and the value 1, so a plain factor on the weights is the
-    reading taken).
+    j-th largest score.  Selection looks at the scores only.  With
+    ``expert_scale`` ([E]) each selected score is first multiplied by its
+    expert's entry, and the renormalisation then runs over those scaled
+    scores: the order of mlx-native moe_dispatch.rs
+    moe_gather_topk_weights_encode (gather the top-k ids and weights, apply
+    per_expert_scale, renormalise).  Without ``normalize`` the (scaled) raw
+    scores of the winners are returned.  Every weight is then multiplied by
+    ``scale`` (llama.cpp's w_scale, which ferrox-models names in
+    gpt_oss_ffn; the pages give only the name and the value 1, so a plain
+    factor on the weights is the reading taken).
     """
     logits = np.atleast_2d(np.asarray(logits, dtype=np.float64))
     T = logits.shape[0]
     ids = np.zeros((T, k), dtype=np.int64)
     w = np.zeros((T, k), dtype=np.float64)
+    es = None if expert_scale is None else np.asarray(expert_scale, dtype=np.float64)
     for t in range(T):
         p = gating_scores(logits[t], gating)
         sel = topk_stable_desc(p, k)
         ids[t] = sel
         ps = p[sel]
+        if es is not None:
+            ps = ps * es[sel]
         w[t] = (ps / ps.sum() if normalize else ps) * scale
     return ids, w
 
@@ -367,14 +376,16 @@ def shared_expert(xt, w_sg, Wsg, Wsu, Wsd):
 
 
 def moe_ffn(inputs, tokens=None, normalize: bool = True, src: WeightSource = None,
-            gating: int = GATING_SOFTMAX, scale: float = 1.0, pre_norm=None, residual=None):
+            gating: int = GATING_SOFTMAX, scale: float = 1.0, pre_norm=None, residual=None,
+            expert_scale=None):
     """The whole layer for the given token ids (all tokens by default).
 
     Returns dict with out [n, H] float64, ids [n, k], w [n, k] float64,
     logits [n, E] float64 and (when present) shared gate values [n].
     ``pre_norm`` = (norm_weight [H], eps) runs the layer on the RMSNorm of
     x, stored in the activation type; ``residual`` [T, H] is added to out
-    (hf2q's residual folded into the final reduce).
+    (hf2q's residual folded into the final reduce); ``expert_scale`` [E] is
+    the per-expert routing scale of ``route``.
     """
     cfg = inputs.cfg
     src = src or WeightSource(inputs)
@@ -384,7 +395,7 @@ def moe_ffn(inputs, tokens=None, normalize: bool = True, src: WeightSource = Non
         nw, eps = pre_norm
         X = round_to_act(rms_norm(X, nw, eps), cfg.act_dtype == 1)
     logits = router_logits(X, src.router(), src.router_bias())
-    ids, w = route(logits, cfg.k, normalize, gating, scale)
+    ids, w = route(logits, cfg.k, normalize, gating, scale, expert_scale)
     out = np.zeros((len(toks), cfg.H), dtype=np.float64)
     sgate = np.zeros(len(toks), dtype=np.float64)
     for n in range(len(toks)):

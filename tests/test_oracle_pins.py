@@ -176,14 +176,102 @@ def test_sigmoid_unnormalised_is_library_expit():
     assert np.abs(w2 - w).max() > 1e-3
 
 
-def test_weight_scale_multiplies_the_routed_sum_only():
+def test_weight_scale_worked_values_and_routed_sum_only():
+    # logits (ln 3, 0): softmax 3/4, 1/4; a scale of 2.5 gives 1.875, 0.625
+    l = np.array([[math.log(3.0), 0.0]])
+    _, w = O.route(l, 2, scale=2.5)
+    np.testing.assert_allclose(w[0], [1.875, 0.625], rtol=1e-15)
+    # sigmoid scores 3/4, 1/2, raw, times 2.5
+    _, w = O.route(l, 2, normalize=False, gating=O.GATING_SIGMOID, scale=2.5)
+    np.testing.assert_allclose(w[0], [1.875, 1.25], rtol=1e-15)
+    # renormalised weights then sum to the scale, whatever the logits
+    rng = np.random.default_rng(44)
+    _, w = O.route(rng.normal(size=(32, 16)) * 3, 4, scale=2.5)
+    np.testing.assert_allclose(w.sum(axis=1), 2.5, rtol=0, atol=1e-13)
     for g in (O.GATING_SOFTMAX, O.GATING_SIGMOID):
         base = O.moe_ffn(_tiny_inputs(seed=43, shared=True, T=4), gating=g)
         sc = O.moe_ffn(_tiny_inputs(seed=43, shared=True, T=4), gating=g, scale=2.5)
-        np.testing.assert_allclose(sc["w"], 2.5 * base["w"], rtol=1e-15)
         routed = O.moe_ffn(_tiny_inputs(seed=43, shared=False, T=4), gating=g)["out"]
         # the shared expert's contribution is untouched by the scale
         np.testing.assert_allclose(sc["out"] - base["out"], 1.5 * routed, rtol=1e-10, atol=1e-13)
+
+
+@pytest.mark.parametrize("act", [ACT_SILU, ACT_GELU_TANH])
+def test_weight_scale_single_expert_is_scaled_dense_ffn(act):
+    # one expert, top-1: the routed part is the dense gated FFN, computed
+    # here with torch's linear layers, times the scale
+    inp = _tiny_inputs(E=1, k=1, act=act, seed=45)
+    r = O.moe_ffn(inp, scale=-0.75)
+    x = torch.from_numpy(inp.x).double()
+    g = F.linear(x, torch.from_numpy(inp.gate[0]).double())
+    u = F.linear(x, torch.from_numpy(inp.up[0]).double())
+    a = F.silu(g) if act == ACT_SILU else F.gelu(g, approximate="tanh")
+    ref = -0.75 * F.linear(a * u, torch.from_numpy(inp.down[0]).double()).numpy()
+    np.testing.assert_allclose(r["out"], ref, rtol=1e-9, atol=1e-12)
+
+
+# ------------------------------------------------------ per-expert scale
+def test_expert_scale_worked_values():
+    # logits (ln 3, 0): softmax 3/4, 1/4.  Scales (2, 1): scaled scores
+    # 3/2, 1/4, renormalised 6/7, 1/7; raw 3/2, 1/4; times a weight scale of
+    # 2: 12/7, 2/7
+    l = np.array([[math.log(3.0), 0.0]])
+    es = np.array([2.0, 1.0])
+    ids, w = O.route(l, 2, expert_scale=es)
+    assert ids[0].tolist() == [0, 1]
+    np.testing.assert_allclose(w[0], [6 / 7, 1 / 7], rtol=1e-15)
+    _, w = O.route(l, 2, normalize=False, expert_scale=es)
+    np.testing.assert_allclose(w[0], [1.5, 0.25], rtol=1e-15)
+    _, w = O.route(l, 2, expert_scale=es, scale=2.0)
+    np.testing.assert_allclose(w[0], [12 / 7, 2 / 7], rtol=1e-15)
+    # sigmoid scores 3/4, 1/2 with scales (1, 3): 3/4, 3/2 -> 1/3, 2/3
+    _, w = O.route(l, 2, gating=O.GATING_SIGMOID, expert_scale=np.array([1.0, 3.0]))
+    np.testing.assert_allclose(w[0], [1 / 3, 2 / 3], rtol=1e-15)
+
+
+def test_expert_scale_ones_is_plain_routing_and_k1_weight_is_one():
+    rng = np.random.default_rng(46)
+    L = rng.normal(size=(24, 32)) * 2
+    for g in (O.GATING_SOFTMAX, O.GATING_SIGMOID):
+        for nrm in (True, False):
+            a = O.route(L, 5, nrm, g)
+            b = O.route(L, 5, nrm, g, expert_scale=np.ones(32))
+            assert (a[0] == b[0]).all()
+            np.testing.assert_array_equal(a[1], b[1])
+    # renormalising one selected expert's scaled score gives exactly 1
+    es = rng.uniform(0.5, 1.5, size=32)
+    for g in (O.GATING_SOFTMAX, O.GATING_SIGMOID):
+        _, w = O.route(L, 1, gating=g, expert_scale=es)
+        assert (w == 1.0).all()
+
+
+def test_expert_scale_does_not_change_selection():
+    # the scale applies to the gathered winners: a large scale on an
+    # expert with a small logit does not select it
+    rng = np.random.default_rng(47)
+    L = rng.normal(size=(40, 16))
+    es = np.ones(16)
+    es[int(np.argmin(L[0]))] = 1e6
+    a, _ = O.route(L, 4)
+    b, wb = O.route(L, 4, expert_scale=es)
+    assert (a == b).all()
+    # renormalised weights are proportional to p_e * s_e over the winners
+    P = scipy.special.softmax(L, axis=1)
+    for t in range(40):
+        ref = P[t, b[t]] * es[b[t]]
+        np.testing.assert_allclose(wb[t], ref / ref.sum(), rtol=1e-13)
+
+
+def test_expert_scale_equals_scaled_down_weights_without_renormalisation():
+    # unnormalised weights enter the output linearly: scaling expert e's
+    # weight by 2^m equals scaling its down matrix by 2^m (exact in f32)
+    es = np.array([2.0, 0.5, 4.0, 0.25], dtype=np.float32)
+    a = O.moe_ffn(_tiny_inputs(seed=48, T=6), normalize=False, expert_scale=es)
+    inp = _tiny_inputs(seed=48, T=6)
+    inp.down = inp.down * es[:, None, None]
+    b = O.moe_ffn(inp, normalize=False)
+    assert (a["ids"] == b["ids"]).all()
+    np.testing.assert_allclose(a["out"], b["out"], rtol=1e-13, atol=1e-15)
 
 
 # ------------------------------------------------- pre-FFN RMSNorm, residual
@@ -464,6 +552,66 @@ def test_shared_gate_sigmoid_controls_contribution():
                                atol=1e-14)
 
 
+def _shared_only_inputs(act, seed):
+    """Routed experts that contribute nothing (zero down weights), and a
+    shared-gate vector whose logit is 1000 for every token (x[:, 0] = 1,
+    w_sg = 1000 e_0), so the sigmoid gate is exactly 1 in float64."""
+    inp = _tiny_inputs(seed=seed, shared=True, T=3, act=act, Is=12)
+    inp.down = np.zeros_like(inp.down)
+    inp.x[:, 0] = 1.0
+    inp.shared_gate_inp = np.zeros_like(inp.shared_gate_inp)
+    inp.shared_gate_inp[0] = 1000.0
+    return inp
+
+
+def _torch_swiglu(inp):
+    x = torch.from_numpy(inp.x).double()
+    g = F.linear(x, torch.from_numpy(inp.shared_gate).double())
+    u = F.linear(x, torch.from_numpy(inp.shared_up).double())
+    return F.linear(F.silu(g) * u, torch.from_numpy(inp.shared_down).double()).numpy()
+
+
+def _shared_pin_holds(act, seed=28):
+    inp = _shared_only_inputs(act, seed)
+    r = O.moe_ffn(inp)
+    if not (r["shared_gate"] == 1.0).all():
+        return False
+    return np.allclose(r["out"], _torch_swiglu(inp), rtol=1e-10, atol=1e-13)
+
+
+@pytest.mark.parametrize("act", [ACT_SILU, ACT_GELU_TANH])
+def test_shared_expert_is_a_swiglu_of_its_own_weights(act):
+    # the shared expert is SiLU(Wsg x) * (Wsu x) through Wsd, whatever the
+    # routed experts' activation (an independent torch computation)
+    assert _shared_pin_holds(act)
+
+
+def test_shared_expert_pin_catches_planted_mistakes(monkeypatch):
+    # plant plausible mistakes in the oracle's shared expert: each must make
+    # the pin above fail
+    def swapped(xt, w_sg, Wsg, Wsu, Wsd):
+        s = O.sigmoid(float(xt @ w_sg))
+        return s * (Wsd @ (O.silu(Wsu @ xt) * (Wsg @ xt))), s
+
+    def gelu_shared(xt, w_sg, Wsg, Wsu, Wsd):
+        s = O.sigmoid(float(xt @ w_sg))
+        return s * (Wsd @ (O.gelu_tanh(Wsg @ xt) * (Wsu @ xt))), s
+
+    def transposed_down(xt, w_sg, Wsg, Wsu, Wsd):
+        s = O.sigmoid(float(xt @ w_sg))
+        h = O.silu(Wsg @ xt) * (Wsu @ xt)
+        return s * (Wsd.reshape(Wsd.shape[1], Wsd.shape[0]).T @ h), s
+
+    def ungated(xt, w_sg, Wsg, Wsu, Wsd):
+        return 0.5 * (Wsd @ (O.silu(Wsg @ xt) * (Wsu @ xt))), 0.5
+
+    for bad in (swapped, gelu_shared, transposed_down, ungated):
+        monkeypatch.setattr(O, "shared_expert", bad)
+        assert not _shared_pin_holds(ACT_SILU), bad.__name__
+    monkeypatch.undo()
+    assert _shared_pin_holds(ACT_SILU)
+
+
 def test_down_scaling_and_token_permutation():
     inp = _tiny_inputs(seed=27, T=6)
     out = O.moe_ffn(inp)["out"]
@@ -522,3 +670,39 @@ def test_margin_check_detects_close_logits():
     L = np.array([[3.0, 2.0, 2.0 + 0.5 * MARGIN, -1.0], [3.0, 2.0, 1.0, 0.0]])
     assert margin_violations(L, 2) == [0]
     assert margin_violations(L, 1) == []
+
+
+# ------------------------------------------- the test-side oracle driver
+def test_layer_by_expert_is_bit_identical_to_oracle():
+    from oracle_driver import layer_by_expert
+    from moe_synth import expert_scale_values, residual_values, norm_weight_values
+    cfg = MoeConfig(name="drv", T=9, H=64, I=32, E=8, k=3, act=ACT_GELU_TANH,
+                    weight_format=WF_BF16, act_dtype=DT_BF16, router_dtype=DT_BF16, shared=True,
+                    Is=32, seed_index=90)
+    inp = make_inputs(cfg)
+    es = expert_scale_values(cfg)
+    res = residual_values(cfg)
+    pn = (norm_weight_values(cfg), 1e-5)
+    toks = [8, 0, 3, 5]
+    for kw in (dict(), dict(expert_scale=es, gating=1, scale=2.0), dict(residual=res),
+               dict(pre_norm=pn, normalize=False)):
+        a = O.moe_ffn(inp, tokens=toks, **kw)["out"]
+        b = layer_by_expert(inp, toks, **kw)
+        np.testing.assert_array_equal(a, b)
+
+
+def test_tile_covering_tokens_spread_and_special_tiles():
+    from oracle_driver import tile_covering_tokens
+    rng = np.random.default_rng(91)
+    T, E, k = 3000, 16, 2
+    # skewed expert choice: expert 0 far more often, so it has a ragged last tile
+    ids = np.stack([rng.choice(E, size=k, replace=False, p=np.r_[0.4, np.full(E - 1, 0.6 / 15)])
+                    for _ in range(T)])
+    toks = tile_covering_tokens(ids, E, k, T, shared=True, tile=256, spread=12)
+    assert len(toks) >= 12 and all(0 <= t < T for t in toks)
+    cnt, off, perm, _ = O.permutation(ids, E)
+    # the last grouped route of the whole list and the shared expert's last token
+    assert int(perm[-1]) // k in toks or T - 1 in toks
+    assert T - 1 in toks
+    # the hot expert's last route
+    assert int(perm[int(off[0]) + int(cnt[0]) - 1]) // k in toks
