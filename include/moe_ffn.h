@@ -8,10 +8,10 @@
  *   1. router logits      l[t,e] = x[t,:] . router[e,:] (+ router_bias[e])
  *   2. routing            softmax over the E logits (or a sigmoid per
  *                         logit, moe_gating), the top_k experts by score
- *                         (ties: lower expert index first), weights
- *                         renormalised over the selected experts
- *                         (hf2q softmax_topk_renorm_cpu), times
- *                         routed_scale
+ *                         (ties: lower expert index first), optionally
+ *                         times a per-expert scale, weights renormalised
+ *                         over the selected experts (hf2q
+ *                         softmax_topk_renorm_cpu), times routed_scale
  *   3. routed experts     for each selected expert e of token t:
  *                         h = act(gate[e] x) * (up[e] x),  y = down[e] h
  *                         (act = SiLU, or the tanh form of GELU used by
@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define MOE_FFN_ABI_VERSION 6
+#define MOE_FFN_ABI_VERSION 7
 
 /* Leading workspace bytes that must be zero before a workspace's first use. */
 #define MOE_WORKSPACE_ZERO_BYTES 256
@@ -169,6 +169,16 @@ typedef struct moe_weights {
   const void* down_packed;
   const void* shared_gate_up_packed;
   const void* shared_down_packed;
+  /* [E] f32, 4-byte aligned, or NULL: a learned per-expert scale on the
+   * routing weights (mlx-native moe_dispatch.rs, moe_gather_topk_weights_
+   * encode: gather the top-k experts and their scores, apply
+   * per_expert_scale, renormalise).  Selection looks at the scores alone;
+   * then selected expert e's score p is replaced by p * expert_scale[e],
+   * and the renormalisation (normalize_topk) divides by the sum of the
+   * scaled scores.  routed_scale applies after that.  With
+   * renormalisation, scales whose scaled sum is zero for a token give
+   * non-finite weights; positive scales never do.  NULL: all ones. */
+  const float* expert_scale;
 } moe_weights;
 
 /* ABI version (MOE_FFN_ABI_VERSION of the built library). */
@@ -204,8 +214,9 @@ moe_status moe_workspace_size(const moe_desc* desc, int64_t num_tokens,
  *                  in increasing r, that chose expert e.
  *   ws, ws_bytes   workspace, at least moe_workspace_size(desc, T) bytes
  *
- * Only weights->router, weights->router_bias and (with a shared expert)
- * weights->shared_gate_inp are read.  T = 0 is a no-op.
+ * Only weights->router, weights->router_bias, weights->expert_scale and
+ * (with a shared expert) weights->shared_gate_inp are read.  T = 0 is a
+ * no-op.
  */
 moe_status moe_route(const moe_desc* desc, int64_t num_tokens, const void* x,
                      const moe_weights* weights, int32_t* topk_ids,

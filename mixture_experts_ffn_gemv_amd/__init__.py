@@ -67,7 +67,7 @@ class Weights(ctypes.Structure):
                 ("norm_weight", ctypes.c_void_p),
                 ("gate_up_packed", ctypes.c_void_p), ("down_packed", ctypes.c_void_p),
                 ("shared_gate_up_packed", ctypes.c_void_p),
-                ("shared_down_packed", ctypes.c_void_p)]
+                ("shared_down_packed", ctypes.c_void_p), ("expert_scale", ctypes.c_void_p)]
 
 
 _lib = None
@@ -137,8 +137,9 @@ def _ptr(t) -> Optional[int]:
 
 def make_weights(router, gate=None, up=None, down=None, router_bias=None, shared_gate_inp=None,
                  shared_gate=None, shared_up=None, shared_down=None, u4=None,
-                 norm_weight=None) -> Weights:
-    """Device tensors -> moe_weights.  ``u4`` = dict(gate=(codes, scales, mins), up=..., down=...)."""
+                 norm_weight=None, expert_scale=None) -> Weights:
+    """Device tensors -> moe_weights.  ``u4`` = dict(gate=(codes, scales, mins), up=..., down=...);
+    ``expert_scale``: [E] float32 per-expert routing scale, or None."""
     w = Weights()
     w.router, w.router_bias = _ptr(router), _ptr(router_bias)
     w.gate, w.up, w.down = _ptr(gate), _ptr(up), _ptr(down)
@@ -149,6 +150,7 @@ def make_weights(router, gate=None, up=None, down=None, router_bias=None, shared
     w.shared_gate_inp, w.shared_gate = _ptr(shared_gate_inp), _ptr(shared_gate)
     w.shared_up, w.shared_down = _ptr(shared_up), _ptr(shared_down)
     w.norm_weight = _ptr(norm_weight)
+    w.expert_scale = _ptr(expert_scale)
     return w
 
 

@@ -254,7 +254,8 @@ __device__ __forceinline__ void route_one_token(const float* __restrict__ l, int
   id = lane < k ? my_e : 0;
   const float li = ord_logit(my_ord);
   const float lmax = ord_logit(top);  // the top logit
-  const float ex = lane < k ? (rm.sigmoid ? sigmoid_f(li) : __expf(li - lmax)) : 0.f;
+  const float ex =
+      lane < k ? (rm.sigmoid ? sigmoid_f(li) : __expf(li - lmax)) * expert_scale_of(rm, id) : 0.f;
   float denom;
   if (rm.normalize) {
     denom = wave_sum(ex);
@@ -346,7 +347,9 @@ __device__ __forceinline__ void route_small_impl(const float* __restrict__ logit
       const float* lt = s_l + t * E;
       const int id = lane < k ? s_rid[t * k + lane] : 0;
       const float lmax = lt[s_rid[t * k]];
-      const float ex = lane < k ? (rm.sigmoid ? sigmoid_f(lt[id]) : __expf(lt[id] - lmax)) : 0.f;
+      const float ex = lane < k ? (rm.sigmoid ? sigmoid_f(lt[id]) : __expf(lt[id] - lmax)) *
+                                      expert_scale_of(rm, id)
+                                : 0.f;
       float denom;
       if (rm.normalize) {
         denom = wave_sum(ex);
@@ -380,9 +383,11 @@ __device__ __forceinline__ void route_small_impl(const float* __restrict__ logit
         for (int e = l16; e < E; e += 16) {
           const bool sel = s_sel[t * E + e] >= 0;
           if (rm.sigmoid) {
-            if (sel) sum += sigmoid_f(lt[e]);
-          } else if (!rm.normalize || sel) {
+            if (sel) sum += sigmoid_f(lt[e]) * expert_scale_of(rm, e);
+          } else if (!rm.normalize) {
             sum += __expf(lt[e] - lmax);
+          } else if (sel) {
+            sum += __expf(lt[e] - lmax) * expert_scale_of(rm, e);
           }
         }
       }
@@ -398,7 +403,8 @@ __device__ __forceinline__ void route_small_impl(const float* __restrict__ logit
       const int t = r / k;
       const float* lt = s_l + t * E;
       const int id = s_rid[r];
-      const float sc = rm.sigmoid ? sigmoid_f(lt[id]) : __expf(lt[id] - lt[s_rid[t * k]]);
+      const float sc = (rm.sigmoid ? sigmoid_f(lt[id]) : __expf(lt[id] - lt[s_rid[t * k]])) *
+                       expert_scale_of(rm, id);
       const float w = sc / s_den[t] * rm.scale;
       o.ids[r] = id;
       o.wts[r] = w;

@@ -66,8 +66,9 @@ struct Plan {
   size_t total = 0;
 };
 
-RouteMode route_mode(const moe_desc* d) {
-  return RouteMode{d->normalize_topk, d->gating == MOE_GATING_SIGMOID ? 1 : 0, d->routed_scale};
+RouteMode route_mode(const moe_desc* d, const moe_weights* w) {
+  return RouteMode{d->normalize_topk, d->gating == MOE_GATING_SIGMOID ? 1 : 0, d->routed_scale,
+                   w->expert_scale};
 }
 
 int epc_of(int wf) { return wf == MOE_WEIGHTS_F32 ? 4 : (wf == MOE_WEIGHTS_BF16 ? 8 : 32); }
@@ -309,7 +310,7 @@ moe_status run_route_small(const moe_desc* d, const Plan& p, const void* x, cons
   int* ticket = wsp<int>(ws, p.o_sync);
   const bool xb = d->act_dtype == MOE_BF16, rb = d->router_dtype == MOE_BF16;
   const int sh = p.shared ? 1 : 0;
-  const RouteMode rm = route_mode(d);
+  const RouteMode rm = route_mode(d, w);
   dim3 grid(p.ncols);
   const int nc = router_nc(p.H / (rb ? 8 : 4));
   return launch("router_route", s, [&] {
@@ -323,13 +324,14 @@ moe_status run_route_small(const moe_desc* d, const Plan& p, const void* x, cons
   });
 }
 
-moe_status run_route_and_group(const moe_desc* d, const Plan& p, void* ws, int32_t* user_ids,
+moe_status run_route_and_group(const moe_desc* d, const Plan& p, const moe_weights* w, void* ws,
+                               int32_t* user_ids,
                                float* user_w, int32_t* user_counts, int32_t* user_offsets,
                                int32_t* user_perm, hipStream_t s) {
   const int T = (int)p.T, R = (int)p.R;
   MOE_TRY(launch("topk", s, [&] {
     k_topk<<<(T + 3) / 4, 256, 0, s>>>(wsp<float>(ws, p.o_logits), T, p.E, p.k, p.ncols,
-                                       route_mode(d), p.shared ? 1 : 0, wsp<int32_t>(ws, p.o_ids),
+                                       route_mode(d, w), p.shared ? 1 : 0, wsp<int32_t>(ws, p.o_ids),
                                        wsp<float>(ws, p.o_wts), user_ids, user_w,
                                        wsp<float>(ws, p.o_sgate));
   }));
@@ -618,7 +620,7 @@ moe_status run_experts_small(const moe_desc* d, const Plan& p, const void* x,
   dp.residual = residual;
   dp.T = (int)p.T; dp.E = p.E; dp.k = p.k; dp.H = p.H; dp.I = p.I; dp.Is = p.Is; dp.rc = p.rc;
   dp.logits = wsp<float>(ws, p.o_logits);
-  dp.rm = route_mode(d);
+  dp.rm = route_mode(d, w);
   dp.ro = SmallRouteOut{wsp<int32_t>(ws, p.o_ids), wsp<float>(ws, p.o_wts),
                         wsp<float>(ws, p.o_sgate), wsp<int32_t>(ws, p.o_counts),
                         wsp<int32_t>(ws, p.o_offsets), wsp<int32_t>(ws, p.o_active),
@@ -817,6 +819,8 @@ moe_status check_common(const moe_desc* d, int64_t T, const void* x, const moe_w
   if (d->pre_norm && (!w->norm_weight || !aligned16(w->norm_weight)))
     return fail(w->norm_weight ? MOE_UNSUPPORTED : MOE_INVALID_ARGUMENT,
                 "pre_norm needs weights->norm_weight, 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(w->expert_scale) & 3u)
+    return fail(MOE_UNSUPPORTED, "expert_scale must be 4-byte aligned");
   if (!aligned16(x) || !aligned16(w->router) ||
       (d->has_shared_expert && !aligned16(w->shared_gate_inp)))
     return fail(MOE_UNSUPPORTED, "x, router and shared_gate_inp must be 16-byte aligned");
@@ -862,8 +866,8 @@ moe_status moe_route(const moe_desc* desc, int64_t num_tokens, const void* x,
     return run_route_small(desc, p, x, weights, ws, topk_ids, topk_w, expert_counts,
                            expert_offsets, route_perm, s);
   MOE_TRY(run_router(desc, p, x, weights, ws, s));
-  return run_route_and_group(desc, p, ws, topk_ids, topk_w, expert_counts, expert_offsets,
-                             route_perm, s);
+  return run_route_and_group(desc, p, weights, ws, topk_ids, topk_w, expert_counts,
+                             expert_offsets, route_perm, s);
 }
 
 moe_status moe_ffn_forward(const moe_desc* desc, int64_t num_tokens, const void* x,
@@ -892,7 +896,8 @@ moe_status moe_ffn_forward(const moe_desc* desc, int64_t num_tokens, const void*
     return run_experts_small(desc, p, x, weights, out, residual, ws, s);
   }
   MOE_TRY(run_router(desc, p, x, weights, ws, s));
-  MOE_TRY(run_route_and_group(desc, p, ws, topk_ids_out, topk_w_out, nullptr, nullptr, nullptr, s));
+  MOE_TRY(run_route_and_group(desc, p, weights, ws, topk_ids_out, topk_w_out, nullptr, nullptr,
+                              nullptr, s));
   if (p.mfma) return run_experts_mfma(desc, p, x, weights, out, residual, ws, s);
   return run_experts_gemv(desc, p, x, weights, out, residual, ws, s);
 }

@@ -194,13 +194,19 @@ __global__ __launch_bounds__(256) void k_router_gemv(
 // How the selected experts' weights follow from their logits:
 //   softmax gating: p = softmax(l) over all E experts;
 //   sigmoid gating: p_e = sigmoid(l_e), each expert on its own;
+//   escale:         [E] or null: a selected expert's score p_j becomes
+//                   p_j * escale[e_j] (selection looks at p alone);
 //   normalize:      w_j = p_j / (sum of the k selected p), else w_j = p_j;
 //   scale:          every w_j is multiplied by it.
 struct RouteMode {
   int normalize;
   int sigmoid;
   float scale;
+  const float* escale;
 };
+__device__ __forceinline__ float expert_scale_of(const RouteMode& rm, int e) {
+  return rm.escale ? rm.escale[e] : 1.f;
+}
 
 // --------------------------------------------------------------------------
 // Softmax (or sigmoid) -> top-k -> renormalise, one wave per token.
@@ -210,7 +216,9 @@ struct RouteMode {
 // exp(l - l_max), which equals p_j / sum(p_selected).  Without
 // renormalisation the denominator runs over all E experts.  Sigmoid scores
 // are increasing in the logit too, so selection is the same; their weights
-// are sigmoid(l_j) over the selected sum, or sigmoid(l_j) alone.
+// are sigmoid(l_j) over the selected sum, or sigmoid(l_j) alone.  A
+// per-expert scale multiplies the selected numerators (and so the
+// renormalising sum) only.
 // --------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_topk(
     const float* __restrict__ logits, int T, int E, int k, int ncols,
@@ -243,7 +251,9 @@ __global__ __launch_bounds__(256) void k_topk(
     if (lane == j) { my_id = bi; my_val = bv; }
   }
   const float lmax = __shfl(my_val, 0, 64);
-  const float ex = (lane < k) ? (rm.sigmoid ? sigmoid_f(my_val) : __expf(my_val - lmax)) : 0.f;
+  const float ex = (lane < k) ? (rm.sigmoid ? sigmoid_f(my_val) : __expf(my_val - lmax)) *
+                                    expert_scale_of(rm, my_id)
+                              : 0.f;
   float denom;
   if (rm.normalize) {
     denom = wave_sum(ex);

@@ -186,9 +186,12 @@ def _normal_tensor(seed, tid, shape, std, dtype, backend, device=None,
     n = int(np.prod(shape))
     key = stream_key(seed, tid)
     if backend == "numpy":
-        v = (normal_np(key, 0, n) * std).astype(np.float32)
-        v = v.reshape(shape)
-        return f32_to_bf16_bits(v) if dtype == DT_BF16 else v
+        out = np.empty(n, dtype=np.uint16 if dtype == DT_BF16 else np.float32)
+        for s in range(0, n, 1 << 24):      # bounded temporaries
+            c = min(1 << 24, n - s)
+            v = (normal_np(key, s, c) * std).astype(np.float32)
+            out[s:s + c] = f32_to_bf16_bits(v) if dtype == DT_BF16 else v
+        return out.reshape(shape)
     torch = _torch()
     tdt = torch.bfloat16 if dtype == DT_BF16 else torch.float32
     out = torch.empty(n, dtype=tdt, device=device)
@@ -222,8 +225,10 @@ def _u4_tensor(seed, mat, E, N, K, group, backend, device=None, chunk=1 << 26):
     kc = stream_key(seed, TID_U4_CODES + mat)
     ks = stream_key(seed, TID_U4_SCALES + mat)
     if backend == "numpy":
-        c = codes_np(kc, 0, n_codes).reshape(E, N, K)
-        packed = (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
+        packed = np.empty((E, N, K // 2), dtype=np.uint8)
+        for e in range(E):                  # one expert at a time: bounded temporaries
+            c = codes_np(kc, e * N * K, N * K).reshape(N, K)
+            packed[e] = c[:, 0::2] | (c[:, 1::2] << 4)
         u = uniform_np(ks, np.arange(n_groups, dtype=np.uint64))
         sc = (0.005 + 0.015 * u).astype(np.float32).astype(np.float16)
         mn = (sc * np.float16(-8.0)).astype(np.float16)

@@ -57,10 +57,11 @@ def tile_covering_tokens(ids, E, k, T, shared, tile=256, spread=24):
     The tile list holds, expert by expert, ceil(count / tile) tiles of
     consecutive grouped routes, then (with a shared expert) ceil(T / tile)
     tiles of all tokens in order; the GEMMs deal it to the XCDs in equal
-    consecutive ranges.  Picked: the last route of `spread` tiles evenly
-    spaced over the list (first and last included), the first and last
-    route of the most loaded expert's last tile, and the last token of the
-    shared expert's first and last tiles."""
+    consecutive ranges.  Picked: the last route of tiles evenly spaced over
+    the list (first and last included) until `spread` distinct tokens are
+    in (or every tile is), the first and last route of the most loaded
+    expert's last tile, and the last token of the shared expert's first and
+    last tiles."""
     cnt, off, perm, _ = O.permutation(ids, E)
     tiles = []   # (start position, length) in the grouped route order; shared: token ranges
     for e in range(E):
@@ -71,9 +72,16 @@ def tile_covering_tokens(ids, E, k, T, shared, tile=256, spread=24):
         for i in range((T + tile - 1) // tile):
             tiles.append(("s", i * tile, min(tile, T - i * tile)))
     toks = set()
-    for q in np.linspace(0, len(tiles) - 1, min(spread, len(tiles))).round().astype(int):
-        kind, s, n = tiles[q]
-        toks.add(int(perm[s + n - 1]) // k if kind == "r" else s + n - 1)
+    # tiles of one token can coincide: widen the spread until `spread`
+    # distinct tokens are in (or every tile is)
+    m = min(spread, len(tiles))
+    while True:
+        for q in np.linspace(0, len(tiles) - 1, m).round().astype(int):
+            kind, s, n = tiles[q]
+            toks.add(int(perm[s + n - 1]) // k if kind == "r" else s + n - 1)
+        if len(toks) >= spread or m >= len(tiles):
+            break
+        m = min(len(tiles), m + (spread - len(toks)) + 1)
     hot = int(np.argmax(cnt))
     last = (int(cnt[hot]) - 1) // tile
     s = int(off[hot]) + last * tile

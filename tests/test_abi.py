@@ -35,7 +35,7 @@ def test_header_declares_the_bound_functions():
 def test_library_exports_every_declared_symbol(lib):
     for name in _declared_functions():
         assert hasattr(lib, name), name
-    assert lib.moe_abi_version() == 6
+    assert lib.moe_abi_version() == 7
 
 
 def _desc(name="decode_geglu_t1", **over):

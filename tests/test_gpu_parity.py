@@ -26,19 +26,32 @@ def _gpu():
 from parity_util import Case, check_case, log, rel_err, TOL as TOL_BY_WF  # noqa: E402
 
 # ----------------------------------------------------------- full workloads
-FULL_SAMPLES = {
+# Every token at the decode shapes.  At the prefill shapes, the tokens of
+# route tiles spread over the grouped GEMMs' whole tile list (every XCD's
+# share), the most loaded expert's ragged last tile and the shared
+# expert's last tile: at least 32 tokens at 4096, 16 at 16384.
+FULL_SPREAD = {
     "tiny_f32": None,
     "decode_geglu_t1": None,
-    "decode_u4_t32": [0, 7, 13, 31],
-    "prefill_shared_t4096": [0, 1, 127, 128, 2049, 4095],
-    "prefill_skew_t16384": [0, 5000, 16383],
+    "decode_u4_t32": None,
+    "prefill_shared_t4096": 32,
+    "prefill_skew_t16384": 16,
 }
 
 
-@pytest.mark.parametrize("name", list(FULL_SAMPLES))
+@pytest.mark.parametrize("name", list(FULL_SPREAD))
 def test_full_workload_parity(name):
-    case = Case(CONFIGS[name])
-    check_case(case, FULL_SAMPLES[name])
+    from oracle_driver import tile_covering_tokens
+    cfg = CONFIGS[name]
+    case = Case(cfg)
+    spread = FULL_SPREAD[name]
+    pick = None
+    if spread:
+        def pick(ids):
+            return tile_covering_tokens(ids, cfg.E, cfg.k, cfg.T, cfg.shared, spread=spread)
+    res = check_case(case, tokens_from_ids=pick)
+    if spread:
+        assert len(res["tokens"]) >= spread
 
 
 # ----------------------------------------------- small shapes, every token
@@ -161,6 +174,47 @@ ROUTING_VARIANTS = [
 @pytest.mark.parametrize("cfg,opts", ROUTING_VARIANTS, ids=[c.name for c, _ in ROUTING_VARIANTS])
 def test_routing_variant_parity(cfg, opts):
     check_case(Case(cfg, **opts))
+
+
+# per-expert routing scale (U(0.5, 1.5) per expert) on every routing
+# kernel: one token ranked in the gate/up kernel (f32 and bf16 weights,
+# past 128 experts), the wave-per-token decode routing, rank counting, row
+# selection, the 4-bit decode path, the prefill top-k (MFMA path) and the
+# GEMV fallback; softmax and sigmoid, with and without renormalisation
+EXPERT_SCALE = [
+    (MoeConfig(name="escale_t1_f32", T=1, H=192, I=96, E=200, k=8, seed_index=400),
+     dict(gating=0, normalize=True)),
+    (MoeConfig(name="escale_t1_bf16_shared_raw", T=1, H=1024, I=320, E=64, k=6,
+               weight_format=WF_BF16, router_dtype=DT_BF16, shared=True, Is=128,
+               seed_index=401), dict(gating=0, normalize=False, scale=1.5)),
+    (MoeConfig(name="escale_t1_sigmoid", T=1, H=512, I=128, E=128, k=8, act=ACT_GELU_TANH,
+               weight_format=WF_BF16, router_dtype=DT_BF16, seed_index=402),
+     dict(gating=1, normalize=True)),
+    (MoeConfig(name="escale_t3", T=3, H=128, I=64, E=16, k=4, seed_index=403),
+     dict(gating=0, normalize=True)),
+    (MoeConfig(name="escale_t8_rank_sigmoid", T=8, H=128, I=64, E=64, k=6, weight_format=WF_BF16,
+               router_dtype=DT_BF16, seed_index=404), dict(gating=1, normalize=True)),
+    (MoeConfig(name="escale_t20_rows", T=20, H=128, I=64, E=96, k=5, seed_index=405),
+     dict(gating=0, normalize=True, scale=0.5)),
+    (MoeConfig(name="escale_t20_rows_raw", T=20, H=128, I=64, E=96, k=5, seed_index=406),
+     dict(gating=0, normalize=False)),
+    (MoeConfig(name="escale_u4", T=6, H=256, I=128, E=16, k=4, weight_format=WF_U4,
+               seed_index=407), dict(gating=0, normalize=True)),
+    (MoeConfig(name="escale_prefill_shared", T=300, H=256, I=128, E=16, k=4,
+               weight_format=WF_BF16, act_dtype=DT_BF16, router_dtype=DT_BF16, shared=True,
+               Is=64, seed_index=408), dict(gating=0, normalize=True)),
+    (MoeConfig(name="escale_prefill_sigmoid_raw", T=200, H=128, I=64, E=8, k=3,
+               weight_format=WF_BF16, act_dtype=DT_BF16, router_dtype=DT_BF16, seed_index=409),
+     dict(gating=1, normalize=False, scale=2.0)),
+    (MoeConfig(name="escale_gemv_fallback", T=100, H=96, I=64, E=8, k=2, weight_format=WF_BF16,
+               act_dtype=DT_BF16, router_dtype=DT_BF16, seed_index=410),
+     dict(gating=0, normalize=True)),
+]
+
+
+@pytest.mark.parametrize("cfg,opts", EXPERT_SCALE, ids=[c.name for c, _ in EXPERT_SCALE])
+def test_expert_scale_parity(cfg, opts):
+    check_case(Case(cfg, expert_scale=True, **opts))
 
 
 # pre-FFN RMSNorm on every path: decode (wave-per-token and one-token
