@@ -679,7 +679,12 @@ moe_status run_experts_mfma(const moe_desc* d, const Plan& p, const void* x,
     gu.spk = static_cast<const uint8_t*>(w->shared_gate_up_packed);
   }
   const int maxN = std::max(p.I, p.Is);
-  dim3 g1(p.max_tiles, (maxN + kBW / 2 - 1) / (kBW / 2));
+  // The kernels deal the existing tiles to the XCDs in 8 equal ranges of
+  // ceil(n / 8) workgroup slots each, so the grid needs a whole multiple of
+  // 8 columns: max_tiles columns alone leave the last ranges short whenever
+  // max_tiles * rows < 8 * ceil(n / 8), and those tiles would never run.
+  const int gx = (p.max_tiles + 7) / 8 * 8;
+  dim3 g1(gx, (maxN + kBW / 2 - 1) / (kBW / 2));
   MOE_TRY(launch("gemm_gateup", s, [&] {
     const bool silu = d->activation == MOE_ACT_SILU;
     if (p.bt == kDmaBT && p.ra == 3) {
@@ -705,7 +710,7 @@ moe_status run_experts_mfma(const moe_desc* d, const Plan& p, const void* x,
     gd.pk = static_cast<const uint8_t*>(w->down_packed);
     gd.spk = static_cast<const uint8_t*>(w->shared_down_packed);
   }
-  dim3 g2(p.max_tiles, (p.H + kBW - 1) / kBW);
+  dim3 g2(gx, (p.H + kBW - 1) / kBW);
   MOE_TRY(launch("gemm_down", s, [&] {
     if (p.bt == kDmaBT && p.ra == 3) k_gemm_dma<GM_DOWN, 0, kDmaBK, 3><<<g2, kDmaThreads, 0, s>>>(gd);
     else if (p.bt == kDmaBT) k_gemm_dma<GM_DOWN, 0, kDmaBK, 2><<<g2, kDmaThreads, 0, s>>>(gd);

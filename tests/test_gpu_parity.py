@@ -83,6 +83,11 @@ SMALL = [
               seed_index=64),
     MoeConfig(name="mfma_t33", T=33, H=128, I=64, E=8, k=2, weight_format=WF_BF16,
               act_dtype=DT_BF16, router_dtype=DT_BF16, seed_index=14),
+    # 17 route tiles (16 experts + the shared one) in a grid sized for 19:
+    # every XCD's share of tiles must still run (the grid is padded to a
+    # multiple of 8 columns)
+    MoeConfig(name="mfma_grid_tail", T=40, H=256, I=128, E=16, k=4, weight_format=WF_BF16,
+              act_dtype=DT_BF16, router_dtype=DT_BF16, shared=True, Is=64, seed_index=502),
     MoeConfig(name="mfma_dense_e1", T=40, H=128, I=64, E=1, k=1, weight_format=WF_BF16,
               act_dtype=DT_BF16, router_dtype=DT_BF16, seed_index=15),
     # GEMV path
