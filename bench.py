@@ -6,9 +6,13 @@ inputs are already resident in HBM.  The default workload is single-token
 decode with GELU-GLU experts (T=1, H=2816, I=704, E=128, top-8, bf16
 weights, f32 activations); --workload selects another.
 
-Decode steps rotate over a pool of distinct token vectors, so consecutive
-steps select different experts and the weights stream from HBM rather than
-from the 256 MB Infinity Cache (the full expert set is 1.5 GB).
+Decode steps rotate over a pool of token vectors chosen so that no expert
+is used twice within 3 consecutive steps (at the one-token shape that is
+285 MB of other weights in between, more than the 256 MB Infinity Cache
+holds), so each step's weights stream from HBM.  The timed steps run as
+HIP-graph replays (a graph of min(steps, pool) steps, plus one graph for
+the remainder), captured before the timed region; config.launch says what
+ran.
 
 Prints one JSON line.  Fields beyond the common contract:
   roofline      dominant kernel: algorithmic bytes (decode) or flops or
@@ -16,11 +20,20 @@ Prints one JSON line.  Fields beyond the common contract:
                 binding against the MI355X ridge point, both fractions
                 reported) per launch over its average launch time, measured
                 with hipEvents recorded on the launch stream around every
-                launch, in a second (eager) pass over the same K steps;
+                launch, in a second (eager) pass over the same steps; the
+                *_cold figures come from a third eager pass with a 512 MiB
+                copy between steps (outside the brackets), which leaves
+                nothing of the step's own data in L2 or the Infinity Cache;
                 traffic = HBM bytes per launch (FETCH_SIZE + WRITE_SIZE,
                 scaled by a plain copy of known size) from the committed
                 counter record, null when the kernel sources have changed
                 since the counters were taken
+  cold_mall     that cold pass: event-bracketed step and kernel times
+  prefill_t4096, prefill_t16384
+                the prefill workloads (T=4096 shared-expert, T=16384
+                skewed) timed in the same run: ms per step over graph
+                replays, the gate/up GEMM's TFLOP/s and the fractions of
+                the bf16 MFMA and HBM peaks, for the GEMM and the step
   cpu_baseline  the float64 CPU oracle timed on a bounded sample of tokens
 """
 from __future__ import annotations
@@ -63,6 +76,18 @@ def parse():
                     help="packed: prepare the bf16 expert weights in the prefill GEMMs' packed "
                          "layout once, before timing (auto: for bf16 prefill workloads whose "
                          "routes fill whole 256-route tiles, where it measured faster)")
+    ap.add_argument("--expert-scale", action="store_true",
+                    help="apply the generator's per-expert routing scale")
+    ap.add_argument("--host-inputs", action="store_true",
+                    help="generate inputs on the host (numpy) and copy them: no generator "
+                         "kernels run on the GPU (for profiled runs)")
+    ap.add_argument("--cold-mib", type=int, default=512,
+                    help="MiB copied between the steps of the cold-cache kernel pass "
+                         "(0: no such pass)")
+    ap.add_argument("--prefill", default="prefill_shared_t4096,prefill_skew_t16384",
+                    help="prefill workloads timed after the main one, reported under "
+                         "prefill_t<T> keys ('none': skip)")
+    ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="first run one plain device copy of this many MiB (a kernel of known "
                          "traffic, to scale hardware byte counters)")
@@ -71,6 +96,243 @@ def parse():
 
 def bytes_per_weight(wf):
     return {0: 4.0, 1: 2.0, 2: 0.5 + 4.0 / 32}[wf]
+
+
+def _nproc():
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count()
+
+
+def _blas_threads():
+    from threadpoolctl import threadpool_info
+    return max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+
+
+def make_inputs_on_device(cfg, dev, host_inputs):
+    """The workload's inputs resident in HBM.  host_inputs: generated with
+    the numpy generator and copied (no generator kernels run on the GPU)."""
+    from moe_synth import generate
+    from moe_synth.device import to_device
+    if host_inputs:
+        return to_device(generate(cfg, backend="numpy"), dev)
+    return generate(cfg, backend="torch", device=dev)
+
+
+def token_pool(M, cfg, desc, w, inp, P, dev, host_inputs, window=3):
+    """P token batches to rotate through.  pool[0] is the generated x.  For
+    decode batches whose experts can be kept apart (T*k*(window+1) <= E),
+    the others are drawn so that no expert is used by two batches within
+    `window` steps of each other (cyclically): each step's weights then
+    come from HBM, not from what earlier steps left in the 256 MB Infinity
+    Cache (window 3: at least 3 steps of weights, 285 MB at the one-token
+    decode shape, between two uses of an expert)."""
+    import numpy as np
+    import torch
+    from moe_synth.generator import x_rows
+    from moe_synth.device import _t
+    T = cfg.T
+    if P == 1:
+        return [inp.x], None
+
+    def rows(rr, attempt):
+        if host_inputs:
+            return _t(x_rows(cfg, rr, attempt, backend="numpy"), dev,
+                      bf16=cfg.act_dtype == 1)
+        return x_rows(cfg, rr, attempt, backend="torch", device=dev)
+
+    if T * cfg.k * (window + 1) > cfg.E:
+        # every batch touches most experts: plain distinct draws
+        return [inp.x] + [rows(range(T), 1000 + a) for a in range(1, P)], None
+    # candidates: one batch of C*T rows, routed once by the library
+    C = 64 * P
+    cand = rows(range(C * T), 1000)
+    ws = M.alloc_workspace(desc, C * T, dev)
+    r = M.moe_route(desc, cand, w, workspace=ws)
+    torch.cuda.synchronize()
+    ids = r.ids.cpu().numpy().reshape(C, T * cfg.k)
+    r0 = M.moe_route(desc, inp.x, w)
+    torch.cuda.synchronize()
+    sets = [set(r0.ids.cpu().numpy().ravel().tolist())]
+    chosen = [None]
+    used = np.zeros(C, dtype=bool)
+    for a in range(1, P):
+        near = [sets[i] for i in range(max(0, a - window), a)]
+        # the last batches also come within `window` of the first ones
+        near += [sets[i] for i in range(0, max(0, a + window - P + 1))]
+        avoid = set().union(*near)
+        pick = next((c for c in range(C) if not used[c] and avoid.isdisjoint(ids[c])), None)
+        if pick is None:
+            raise RuntimeError("no candidate token batch keeps the experts apart")
+        used[pick] = True
+        chosen.append(pick)
+        sets.append(set(ids[pick].tolist()))
+    pool = [inp.x] + [cand[c * T:(c + 1) * T].clone() for c in chosen[1:]]
+    return pool, window
+
+
+class Stepper:
+    """K consecutive steps as HIP-graph replays: a graph of G = min(K, pool)
+    steps replayed K // G times, then a graph of the K % G remaining steps.
+    prepare(K) captures those graphs (outside any timed region); warm(W)
+    replays the G-step graph until at least W steps have run.  Records what
+    ran for the JSON line."""
+
+    def __init__(self, step, P, eager):
+        self.step, self.P, self.eager = step, P, eager
+        self.graphs = {}
+        self.ran = []
+
+    def prepare(self, n):
+        if self.eager or n == 0:
+            return
+        G = min(n, self.P)
+        self._graph(G)
+        if n % G:
+            self._graph(n % G)
+
+    def warm(self, n, steps):
+        """At least n warm-up steps, as replays of the timed run's main graph."""
+        if self.eager or steps == 0:
+            for i in range(n):
+                self.step(i)
+            return
+        g = self._graph(min(steps, self.P))
+        for _ in range((n + min(steps, self.P) - 1) // min(steps, self.P)):
+            g.replay()
+
+    def _graph(self, n):
+        import torch
+        if n not in self.graphs:
+            stream = torch.cuda.current_stream()
+            s = torch.cuda.Stream()
+            s.wait_stream(stream)
+            with torch.cuda.stream(s):
+                for i in range(min(n, 3)):
+                    self.step(i)
+            stream.wait_stream(s)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(n):
+                    self.step(i)
+            torch.cuda.synchronize()
+            self.graphs[n] = g
+        return self.graphs[n]
+
+    def run(self, n):
+        if self.eager or n == 0:
+            for i in range(n):
+                self.step(i)
+            self.ran = [("eager", n, 1)]
+            return
+        G = min(n, self.P)
+        full, rem = divmod(n, G)
+        g = self._graph(G)
+        rg = self._graph(rem) if rem else None
+        for _ in range(full):
+            g.replay()
+        if rg is not None:
+            rg.replay()
+        self.ran = [("graph", G, full)] + ([("graph", rem, 1)] if rem else [])
+
+    def label(self):
+        parts = []
+        for kind, size, reps in self.ran:
+            parts.append(f"{kind} {size} steps" if kind == "eager"
+                         else f"hipgraph of {size} steps x{reps}")
+        return " + ".join(parts)
+
+
+def kernel_times(M, step, n, scrub=None):
+    """Average event-bracketed duration per kernel (ms) over n eager steps;
+    with `scrub`, a 512 MiB copy runs before every step, outside the
+    brackets, so the step starts with nothing of its own in the caches.
+    Also returns the average event-bracketed step (ms)."""
+    import torch
+    M.timing_reset()
+    M.timing_enable(True)
+    ev = []
+    for i in range(n):
+        if scrub is not None:
+            scrub[1].copy_(scrub[0])
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        step(i)
+        b.record()
+        ev.append((a, b))
+    torch.cuda.synchronize()
+    st = sum(a.elapsed_time(b) for a, b in ev)
+    kt = M.timing_read()
+    M.timing_enable(False)
+    return {k: v[1] / v[0] for k, v in kt.items()}, st / max(n, 1)
+
+
+def prefill_figures(cfg, touched, sec_gateup, sec_step):
+    """Flops and bytes the prefill path must do at least, and the fractions
+    of the MI355X peaks they reach in the given times."""
+    T, k, H, I, E = cfg.T, cfg.k, cfg.H, cfg.I, cfg.E
+    R = T * k
+    Is = cfg.Is if cfg.shared else 0
+    fl = 2.0 * (R * 2 * I * H + T * 2 * Is * H)
+    by = (touched * 2 * I * H + 2 * Is * H) * 2 + T * H * 2 + (R * I + T * Is) * 2
+    tot = 2.0 * T * (k * 3 * I * H + 3 * Is * H + (E + 1) * H)
+    tot_by = (touched * 3 * I * H + 3 * Is * H + (E + 1) * H) * 2 + T * H * 2 + T * H * 4
+    tf, gbs = fl / sec_gateup / 1e12, by / sec_gateup / 1e9
+    return {
+        "gateup_flops": fl, "gateup_bytes": by, "gateup_tflops": round(tf, 1),
+        "gateup_frac_mfma": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+        "gateup_frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+        "path_flops": tot, "path_bytes": tot_by,
+        "path_tflops": round(tot / sec_step / 1e12, 1),
+        "frac_mfma": round(tot / sec_step / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        "frac_hbm": round(tot_by / sec_step / 1e9 / HBM_PEAK_GBS, 4),
+    }
+
+
+def bench_prefill(M, name, steps, warmup, dev):
+    """One prefill workload (inputs resident in HBM): ms per step over
+    graph replays, the gate/up GEMM's event-bracketed time, and the
+    fractions of the bf16 MFMA and HBM peaks."""
+    import torch
+    from moe_synth import CONFIGS
+    from moe_synth.device import desc_kwargs, weights_kwargs
+    cfg = CONFIGS[name]
+    inp = make_inputs_on_device(cfg, dev, False)
+    desc = M.make_desc(**desc_kwargs(cfg))
+    w = M.make_weights(**weights_kwargs(inp))
+    packed = None
+    if cfg.T * cfg.k >= 256 * cfg.E:
+        packed = M.pack_weights(desc, w, device=dev)
+    ws = M.alloc_workspace(desc, cfg.T, dev)
+    out = torch.empty((cfg.T, cfg.H), dtype=torch.float32, device=dev)
+    r = M.moe_route(desc, inp.x, w, workspace=ws)
+    torch.cuda.synchronize()
+    touched = int((r.counts.cpu().numpy() > 0).sum())
+
+    def step(i):
+        M.moe_ffn_forward(desc, inp.x, w, out=out, workspace=ws)
+
+    st = Stepper(step, steps, False)
+    st.prepare(steps)
+    st.warm(warmup, steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    st.run(steps)
+    torch.cuda.synchronize()
+    sec = (time.perf_counter() - t0) / steps
+    km, _ = kernel_times(M, step, max(3, min(steps, 10)))
+    fig = prefill_figures(cfg, touched, km["gemm_gateup"] * 1e-3, sec)
+    res = {"workload": name, "T": cfg.T, "ms_per_step": round(sec * 1e3, 4),
+           "tokens_per_s": round(cfg.T / sec, 1), "launch": st.label(),
+           "weight_layout": "packed" if packed else "rowmajor", "touched_experts": touched,
+           "gateup_us": round(km["gemm_gateup"] * 1e3, 1),
+           "kernels_us": {k2: round(v * 1e3, 1) for k2, v in km.items()}, **fig}
+    del inp, w, ws, out, packed
+    torch.cuda.empty_cache()
+    return res
 
 
 def main():
@@ -86,8 +348,7 @@ def main():
 
     import mixture_experts_ffn_gemv_amd as M
     from mixture_experts_ffn_gemv_amd.profiling import recorded_traffic
-    from moe_synth import CONFIGS, generate, WF_U4
-    from moe_synth.generator import x_rows
+    from moe_synth import CONFIGS, expert_scale_values
     from moe_synth.device import desc_kwargs, weights_kwargs
 
     cfg = CONFIGS[args.workload]
@@ -101,7 +362,7 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    inp = generate(cfg, backend="torch", device=dev)
+    inp = make_inputs_on_device(cfg, dev, args.host_inputs)
     gating = {"softmax": M.GATING_SOFTMAX, "sigmoid": M.GATING_SIGMOID}[args.gating]
     desc = M.make_desc(**desc_kwargs(cfg, gating=gating, routed_scale=args.routed_scale),
                        norm_eps=args.pre_norm)
@@ -109,6 +370,9 @@ def main():
     if args.pre_norm is not None:
         from moe_synth import norm_weight_values
         wkw["norm_weight"] = torch.from_numpy(norm_weight_values(cfg)).to(dev)
+    escale = expert_scale_values(cfg) if args.expert_scale else None
+    if escale is not None:
+        wkw["expert_scale"] = torch.from_numpy(escale).to(dev)
     w = M.make_weights(**wkw)
     layout = args.weight_layout
     if layout == "auto":
@@ -122,13 +386,9 @@ def main():
     T = cfg.T
     decode = T <= 32
     P = args.pool if decode else 1
-    # token pool: pool[0] is the generated x, the rest are fresh draws
-    xs = [inp.x]
-    for a in range(1, P):
-        xs.append(x_rows(cfg, range(T), 1000 + a, backend="torch", device=dev))
+    xs, window = token_pool(M, cfg, desc, w, inp, P, dev, args.host_inputs)
     ws = M.alloc_workspace(desc, T, dev)
     out = torch.empty((T, cfg.H), dtype=torch.float32, device=dev)
-    stream = torch.cuda.current_stream()
 
     def step(i):
         M.moe_ffn_forward(desc, xs[i % P], w, out=out, workspace=ws, residual=res)
@@ -139,52 +399,26 @@ def main():
     counts = r.counts.cpu().numpy()
     touched = int((counts > 0).sum())
 
-    # HIP graph of the whole pool rotation (P consecutive steps): one replay
-    # runs P steps back to back, so the per-replay launch cost is amortised
-    graph = None
-    if not args.eager:
-        s = torch.cuda.Stream()
-        s.wait_stream(stream)
-        with torch.cuda.stream(s):
-            for i in range(3):
-                step(i)
-        stream.wait_stream(s)
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            for i in range(P):
-                step(i)
-        torch.cuda.synchronize()
-
-    def run_steps(n):
-        """n consecutive steps: whole-pool graph replays, then single eager steps."""
-        i = 0
-        if graph is not None:
-            while n - i >= P:
-                graph.replay()
-                i += P
-        while i < n:
-            step(i)
-            i += 1
-
-    run_steps(args.warmup)
+    stepper = Stepper(step, P, args.eager)
+    stepper.prepare(args.steps)        # graph capture stays outside the timed region
+    stepper.warm(args.warmup, args.steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    run_steps(args.steps)
+    stepper.run(args.steps)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / args.steps
     tokens_per_s = T * args.steps / elapsed
 
-    # ---- per-kernel durations: hipEvents around each launch, eager pass ------
-    M.timing_reset()
-    M.timing_enable(True)
-    for i in range(args.steps):
-        step(i)
-    torch.cuda.synchronize()
-    kt = M.timing_read()
-    M.timing_enable(False)
-    kernel_ms = {k: v[1] / v[0] for k, v in kt.items()}
+    # ---- per-kernel durations: hipEvents around each launch, eager passes ---
+    nk = max(1, min(args.steps, 400))
+    kernel_ms, _ = kernel_times(M, step, nk)
+    cold_ms = cold_step_ms = None
+    if args.cold_mib:
+        n = args.cold_mib << 18   # float32 elements
+        scrub = (torch.ones(n, device=dev), torch.empty(n, device=dev))
+        cold_ms, cold_step_ms = kernel_times(M, step, nk, scrub)
+        del scrub
 
     H, I, E, k = cfg.H, cfg.I, cfg.E, cfg.k
     bpw = bytes_per_weight(cfg.weight_format)
@@ -192,40 +426,45 @@ def main():
         # selected-expert gate+up weight bytes streamed by one gate/up launch
         dom = "gemv_gateup"
         alg = touched * 2 * I * H * bpw + (2 * cfg.Is * H * bpw if cfg.shared else 0)
-    if decode:
         achieved = alg / (kernel_ms[dom] * 1e-3) / 1e9
         roof = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": recorded_traffic(cfg.name, dom), "algorithmic_bytes_per_launch": alg,
                 "avg_launch_us": round(kernel_ms[dom] * 1e3, 2)}
+        if cold_ms:
+            ac = alg / (cold_ms[dom] * 1e-3) / 1e9
+            roof.update({"achieved_cold": round(ac, 1), "frac_cold": round(ac / HBM_PEAK_GBS, 4),
+                         "avg_launch_us_cold": round(cold_ms[dom] * 1e3, 2)})
         step_bytes = touched * 3 * I * H * bpw + (3 * cfg.Is * H * bpw if cfg.shared else 0)
         extra = {"path_weight_bytes": step_bytes,
-                 "path_gbs": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1)}
+                 "path_gbs": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+                 "path_frac_hbm": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     else:
         # gate/up grouped GEMM: flops, and the bytes it must move at least
         # (touched experts' gate+up weights, x, h written; shared expert alike)
         dom = "gemm_gateup"
-        R = T * k
-        Is = cfg.Is if cfg.shared else 0
-        fl = 2.0 * (R * 2 * I * H + T * 2 * Is * H)
-        by = (touched * 2 * I * H + 2 * Is * H) * bpw + T * H * 2 + (R * I + T * Is) * 2
-        sec = kernel_ms[dom] * 1e-3
-        tflops, gbs = fl / sec / 1e12, by / sec / 1e9
+        fig = prefill_figures(cfg, touched, kernel_ms[dom] * 1e-3, ms_per_step * 1e-3)
         ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
-        f_mfma, f_hbm = tflops / MFMA_BF16_PEAK_TFLOPS, gbs / HBM_PEAK_GBS
+        fl, by = fig["gateup_flops"], fig["gateup_bytes"]
         if fl / by >= ridge:   # arithmetic intensity above the ridge: bound by MFMA
-            roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(f_mfma, 4)}
+            roof = {"bound": "mfma", "achieved": fig["gateup_tflops"],
+                    "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": fig["gateup_frac_mfma"]}
         else:
-            roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-                    "unit": "GB/s", "frac": round(f_hbm, 4)}
+            roof = {"bound": "hbm", "achieved": round(by / (kernel_ms[dom] * 1e-3) / 1e9, 1),
+                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": fig["gateup_frac_hbm"]}
         roof.update({"kernel": dom, "traffic": recorded_traffic(cfg.name, dom),
                      "algorithmic_flops_per_launch": fl, "algorithmic_bytes_per_launch": by,
                      "arithmetic_intensity": round(fl / by, 1), "ridge": round(ridge, 1),
-                     "frac_mfma": round(f_mfma, 4), "frac_hbm": round(f_hbm, 4),
+                     "frac_mfma": fig["gateup_frac_mfma"], "frac_hbm": fig["gateup_frac_hbm"],
                      "avg_launch_us": round(kernel_ms[dom] * 1e3, 2)})
-        tot = 2.0 * T * (k * 3 * I * H + (3 * cfg.Is * H if cfg.shared else 0) + (E + 1) * H)
-        extra = {"path_flops": tot, "path_tflops": round(tot / (ms_per_step * 1e-3) / 1e12, 1)}
+        extra = {"path_flops": fig["path_flops"], "path_tflops": fig["path_tflops"],
+                 "path_frac_mfma": fig["frac_mfma"]}
+    if cold_ms:
+        extra["cold_mall"] = {
+            "scrub_mib": args.cold_mib, "steps": nk,
+            "step_us": round(cold_step_ms * 1e3, 2),
+            "kernels_us": {k2: round(v * 1e3, 2) for k2, v in cold_ms.items()}}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -234,7 +473,7 @@ def main():
             from moe_synth import norm_weight_values
             pn = (norm_weight_values(cfg), args.pre_norm)
         cpu = cpu_baseline(cfg, inp, xs, args.cpu_seconds, gating, args.routed_scale, pn,
-                           None if res is None else res.cpu().numpy())
+                           None if res is None else res.cpu().numpy(), escale)
 
     line = {
         "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -249,15 +488,25 @@ def main():
                    "activations": ["f32", "bf16"][cfg.act_dtype],
                    "shared_expert": cfg.Is if cfg.shared else 0,
                    "gating": args.gating, "routed_scale": args.routed_scale,
+                   "expert_scale": bool(args.expert_scale),
                    "pre_norm_eps": args.pre_norm, "residual": args.residual,
                    "touched_experts": touched, "token_pool": P,
-                   "launch": "eager" if graph is None else f"hipgraph x{P} steps",
+                   "expert_reuse_window": window,
+                   "launch": stepper.label(),
                    "parallelism": "single-gpu"},
         "roofline": roof,
         "kernels_us": {k2: round(v * 1e3, 2) for k2, v in kernel_ms.items()},
         **extra,
         "cpu_baseline": cpu,
     }
+    del packed_bufs
+    # the T=4096 (and T=16384) half of the metric: prefill workloads, same run
+    if args.prefill and args.prefill != "none":
+        del inp, w, ws, xs, out
+        torch.cuda.empty_cache()
+        for name in args.prefill.split(","):
+            pf = bench_prefill(M, name, args.prefill_steps, 2, dev)
+            line[f"prefill_t{CONFIGS[name].T}"] = pf
     print(json.dumps(line), flush=True)
 
 
@@ -340,7 +589,6 @@ def bench_backward(args):
                                                    / 1e9, 1)}}
     cpu = None
     if not args.no_cpu_baseline:
-        from threadpoolctl import threadpool_info
         from oracle import weighted_sum_backward, glu_backward
         n, tcpu, t = 0, 0.0, 0
         while tcpu < args.cpu_seconds:
@@ -350,8 +598,8 @@ def bench_backward(args):
             tcpu += time.perf_counter() - t0c
             n += 1
             t = (t + 1) % T
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-        cpu = {"value": round(n / tcpu, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+        cpu = {"value": round(n / tcpu, 3), "unit": "tokens/s", "cores": _blas_threads(),
+               "host_cores": _nproc(), "kind": "oracle",
                "sample": f"{n} tokens of {cfg.name}: both float64 backward steps per token"}
     ms = elapsed * 1e3 / args.steps
     print(json.dumps({
@@ -366,9 +614,9 @@ def bench_backward(args):
         "cpu_baseline": cpu}), flush=True)
 
 
-def cpu_baseline(cfg, inp, xs, seconds, gating=0, scale=1.0, pre_norm=None, residual=None):
+def cpu_baseline(cfg, inp, xs, seconds, gating=0, scale=1.0, pre_norm=None, residual=None,
+                 expert_scale=None):
     """The float64 CPU oracle, as it stands, on a bounded sample of tokens."""
-    from threadpoolctl import threadpool_info
     from moe_synth.device import HostView
     from oracle import moe_ffn, WeightSource
 
@@ -385,18 +633,19 @@ def cpu_baseline(cfg, inp, xs, seconds, gating=0, scale=1.0, pre_norm=None, resi
             src = WeightSource(host, cache=False)
             t0 = time.perf_counter()
             moe_ffn(host, tokens=[tok], src=src, gating=gating, scale=scale, pre_norm=pre_norm,
-                    residual=residual)
+                    residual=residual, expert_scale=expert_scale)
             t_total += time.perf_counter() - t0
             n_done += 1
             if t_total >= seconds:
                 break
         j += 1
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    return {"value": round(n_done / t_total, 3), "unit": "tokens/s", "cores": threads,
-            "kind": "oracle",
+    return {"value": round(n_done / t_total, 3), "unit": "tokens/s", "cores": _blas_threads(),
+            "host_cores": _nproc(), "kind": "oracle",
             "sample": f"{n_done} tokens of {cfg.name} (drawn from the benchmark's token pool), "
                       f"one float64 oracle call per token with its experts decoded per call; "
-                      f"inputs copied to host memory before timing"}
+                      f"inputs copied to host memory before timing; cores = the BLAS threads "
+                      f"of its matrix products (the per-token loop is one Python thread), "
+                      f"host_cores = the cores this process may use"}
 
 
 if __name__ == "__main__":
