@@ -251,6 +251,27 @@ moe_status moe_ffn_forward(const moe_desc* desc, int64_t num_tokens,
                            void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * moe_ffn_forward_noalloc: moe_ffn_forward without a workspace argument,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).  The
+ * scratch comes from a static device array of MOE_NOALLOC_SCRATCH_BYTES
+ * inside the library, one per GPU, held until the process ends; the call
+ * itself allocates nothing.  Arguments, results and errors are those of
+ * moe_ffn_forward, plus MOE_UNSUPPORTED when the call needs more scratch
+ * than the array holds (moe_workspace_size(desc, num_tokens) >
+ * MOE_NOALLOC_SCRATCH_BYTES: decode shapes and small prefill batches fit).
+ * All calls on one GPU share its array: calls that overlap in time on one
+ * GPU (different streams not ordered by events, or different threads)
+ * race and give undefined results.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (32u << 20)
+moe_status moe_ffn_forward_noalloc(const moe_desc* desc, int64_t num_tokens,
+                                   const void* x, const moe_weights* weights,
+                                   float* out, const float* residual,
+                                   int32_t* topk_ids_out, float* topk_w_out,
+                                   void* stream);
+
+/*
  * Backward of the routing-weighted combine (mlx-native moe_dispatch.rs,
  * moe_weighted_sum_seq and its two backward kernels).  Forward:
  * out[t,d] = sum_j w[t,j] * y[t,j,d].  Gradients, given dout = dL/dout:

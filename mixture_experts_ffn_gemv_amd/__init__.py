@@ -34,7 +34,8 @@ GATING_SOFTMAX, GATING_SIGMOID = 0, 1
 DT_F32, DT_BF16 = 0, 1
 
 EXPORTED_SYMBOLS = ("moe_abi_version", "moe_last_error", "moe_workspace_size", "moe_route",
-                    "moe_ffn_forward", "moe_weighted_sum_backward", "moe_glu_backward",
+                    "moe_ffn_forward", "moe_ffn_forward_noalloc", "moe_weighted_sum_backward",
+                    "moe_glu_backward",
                     "moe_packed_weight_bytes", "moe_pack_weights",
                     "moe_timing_enable", "moe_timing_read", "moe_timing_reset")
 
@@ -94,6 +95,9 @@ def load(path: Optional[str] = None):
     lib.moe_ffn_forward.argtypes = [ctypes.POINTER(Desc), i64, vp, ctypes.POINTER(Weights), vp, vp,
                                     vp, vp, vp, ctypes.c_size_t, vp]
     lib.moe_ffn_forward.restype = i32
+    lib.moe_ffn_forward_noalloc.argtypes = [ctypes.POINTER(Desc), i64, vp, ctypes.POINTER(Weights),
+                                            vp, vp, vp, vp, vp]
+    lib.moe_ffn_forward_noalloc.restype = i32
     lib.moe_weighted_sum_backward.argtypes = [i64, i32, i32, vp, vp, vp, vp, vp, vp]
     lib.moe_weighted_sum_backward.restype = i32
     lib.moe_glu_backward.argtypes = [i64, i32, i32, vp, vp, vp, vp]
@@ -241,6 +245,27 @@ def moe_ffn_forward(desc: Desc, x, weights: Weights, out=None, workspace=None, s
     _check(load().moe_ffn_forward(ctypes.byref(desc), T, x.data_ptr(), ctypes.byref(weights),
                                   out.data_ptr(), _ptr(residual), _ptr(ids), _ptr(w),
                                   ws.data_ptr(), ws.numel(), _stream(stream)))
+    return (out, ids, w) if return_routing else out
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20   # MOE_NOALLOC_SCRATCH_BYTES
+
+
+def moe_ffn_forward_noalloc(desc: Desc, x, weights: Weights, out=None, stream=None,
+                            return_routing: bool = False, residual=None):
+    """moe_ffn_forward on the library's static scratch (no workspace)."""
+    import torch
+    T = x.shape[0]
+    dev = x.device
+    if out is None:
+        out = torch.empty((T, desc.hidden), dtype=torch.float32, device=dev)
+    ids = w = None
+    if return_routing:
+        ids = torch.empty((T, desc.top_k), dtype=torch.int32, device=dev)
+        w = torch.empty((T, desc.top_k), dtype=torch.float32, device=dev)
+    _check(load().moe_ffn_forward_noalloc(ctypes.byref(desc), T, x.data_ptr(),
+                                          ctypes.byref(weights), out.data_ptr(), _ptr(residual),
+                                          _ptr(ids), _ptr(w), _stream(stream)))
     return (out, ids, w) if return_routing else out
 
 

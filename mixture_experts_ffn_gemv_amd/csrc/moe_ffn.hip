@@ -45,6 +45,7 @@ moe_status fail(moe_status s, const char* fmt, ...) {
 // path is available.
 constexpr int64_t kDecodeMaxTokens = 32;
 constexpr size_t kSyncBytes = MOE_WORKSPACE_ZERO_BYTES;
+constexpr size_t kScratchBytes = MOE_NOALLOC_SCRATCH_BYTES;
 
 size_t align_up(size_t v, size_t a = 256) { return (v + a - 1) / a * a; }
 
@@ -786,8 +787,11 @@ moe_status check_packed(const moe_desc* d, const moe_weights* w) {
   return MOE_OK;
 }
 
+// own_scratch: the call runs on the library's static scratch (ws is not
+// checked; the plan must fit kScratchBytes instead).
 moe_status check_common(const moe_desc* d, int64_t T, const void* x, const moe_weights* w,
-                        void* ws, size_t ws_bytes, bool full, Plan* plan) {
+                        void* ws, size_t ws_bytes, bool full, Plan* plan,
+                        bool own_scratch = false) {
   MOE_TRY(check_desc(d));
   if (T < 0) return fail(MOE_INVALID_ARGUMENT, "num_tokens %lld is negative", (long long)T);
   if (T * d->top_k > INT32_MAX || T > INT32_MAX / 4)
@@ -832,10 +836,97 @@ moe_status check_common(const moe_desc* d, int64_t T, const void* x, const moe_w
   if (!plan->mfma && d->hidden > 16384)
     return fail(MOE_UNSUPPORTED, "hidden %d > 16384 needs bf16 weights and activations and more "
                 "than %d tokens", d->hidden, (int)kDecodeMaxTokens);
+  if (own_scratch) {
+    if (plan->total > kScratchBytes)
+      return fail(MOE_UNSUPPORTED, "%lld tokens need %zu bytes of scratch; the library's static "
+                  "scratch holds %zu (call moe_ffn_forward with a workspace instead)",
+                  (long long)T, plan->total, kScratchBytes);
+    return MOE_OK;
+  }
   if (!ws) return fail(MOE_INVALID_ARGUMENT, "workspace is NULL");
   if (!aligned16(ws)) return fail(MOE_UNSUPPORTED, "workspace must be 16-byte aligned");
   if (ws_bytes < plan->total)
     return fail(MOE_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", ws_bytes, plan->total);
+  return MOE_OK;
+}
+
+// The whole layer once the arguments have passed check_common.
+moe_status forward_body(const moe_desc* desc, const Plan& p, int64_t num_tokens, const void* x,
+                        const moe_weights* weights, float* out, const float* residual,
+                        int32_t* topk_ids_out, float* topk_w_out, void* ws, hipStream_t s) {
+  MOE_TRY(layer_input(desc, p, x, weights, ws, s, &x));
+  if (p.small) {
+    if (num_tokens == 1 && desc->weight_format != MOE_WEIGHTS_U4_G32) {
+      // one token: the router kernel writes only the logits; the gate/up
+      // kernel ranks them itself and writes the routing (no routing tail)
+      MOE_TRY(run_router(desc, p, x, weights, ws, s));
+      return run_experts_small(desc, p, x, weights, out, residual, ws, s, true, topk_ids_out,
+                               topk_w_out);
+    }
+    MOE_TRY(run_route_small(desc, p, x, weights, ws, topk_ids_out, topk_w_out, nullptr, nullptr,
+                            nullptr, s));
+    return run_experts_small(desc, p, x, weights, out, residual, ws, s);
+  }
+  MOE_TRY(run_router(desc, p, x, weights, ws, s));
+  MOE_TRY(run_route_and_group(desc, p, weights, ws, topk_ids_out, topk_w_out, nullptr, nullptr,
+                              nullptr, s));
+  if (p.mfma) return run_experts_mfma(desc, p, x, weights, out, residual, ws, s);
+  return run_experts_gemv(desc, p, x, weights, out, residual, ws, s);
+}
+
+// ------------------------------------------------- library-owned scratch
+// moe_ffn_forward_noalloc runs on this array instead of a caller workspace.
+// Host code never uses its name as an address: each device's copy is found
+// with hipGetSymbolAddress once, with that device current, and that
+// pointer is what kernels and fills receive.
+__global__ void k_zero_words(uint32_t* p, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0u;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+bool g_scratch_zeroed[kMaxDevices] = {};
+
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+// The current device's scratch.  Its leading MOE_WORKSPACE_ZERO_BYTES (the
+// routing ticket) must be zero before its first use: until a call made
+// outside graph capture has zeroed them, each call first enqueues a small
+// fill kernel on its stream (under capture that kernel becomes part of the
+// graph, so every replay starts from zero too).
+moe_status scratch_for_device(hipStream_t s, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MOE_HIP_ERROR, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MOE_UNSUPPORTED, "device %d: at most %d devices have library scratch", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* q = nullptr;
+    e = hipGetSymbolAddress(&q, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !q)
+      return fail(MOE_HIP_ERROR, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = q;
+  }
+  if (!g_scratch_zeroed[dev]) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    e = hipStreamIsCapturing(s, &cs);
+    if (e != hipSuccess)
+      return fail(MOE_HIP_ERROR, "hipStreamIsCapturing failed: %s", hipGetErrorString(e));
+    MOE_TRY(launch("zero_scratch_counters", s, [&] {
+      k_zero_words<<<1, 64, 0, s>>>(static_cast<uint32_t*>(g_scratch_ptr[dev]),
+                                    MOE_WORKSPACE_ZERO_BYTES / 4);
+    }));
+    if (cs == hipStreamCaptureStatusNone) g_scratch_zeroed[dev] = true;
+  }
+  *out = g_scratch_ptr[dev];
   return MOE_OK;
 }
 
@@ -886,25 +977,25 @@ moe_status moe_ffn_forward(const moe_desc* desc, int64_t num_tokens, const void*
   if (!out) return fail(MOE_INVALID_ARGUMENT, "out is NULL");
   if (!aligned16(out) || !aligned16(residual))
     return fail(MOE_UNSUPPORTED, "out and residual must be 16-byte aligned");
+  return forward_body(desc, p, num_tokens, x, weights, out, residual, topk_ids_out, topk_w_out,
+                      ws, static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_ffn_forward_noalloc(const moe_desc* desc, int64_t num_tokens, const void* x,
+                                   const moe_weights* weights, float* out, const float* residual,
+                                   int32_t* topk_ids_out, float* topk_w_out, void* stream) {
+  g_err.clear();
+  Plan p;
+  MOE_TRY(check_common(desc, num_tokens, x, weights, nullptr, 0, true, &p, true));
+  if (num_tokens == 0) return MOE_OK;
+  if (!out) return fail(MOE_INVALID_ARGUMENT, "out is NULL");
+  if (!aligned16(out) || !aligned16(residual))
+    return fail(MOE_UNSUPPORTED, "out and residual must be 16-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  MOE_TRY(layer_input(desc, p, x, weights, ws, s, &x));
-  if (p.small) {
-    if (num_tokens == 1 && desc->weight_format != MOE_WEIGHTS_U4_G32) {
-      // one token: the router kernel writes only the logits; the gate/up
-      // kernel ranks them itself and writes the routing (no routing tail)
-      MOE_TRY(run_router(desc, p, x, weights, ws, s));
-      return run_experts_small(desc, p, x, weights, out, residual, ws, s, true, topk_ids_out,
-                               topk_w_out);
-    }
-    MOE_TRY(run_route_small(desc, p, x, weights, ws, topk_ids_out, topk_w_out, nullptr, nullptr,
-                            nullptr, s));
-    return run_experts_small(desc, p, x, weights, out, residual, ws, s);
-  }
-  MOE_TRY(run_router(desc, p, x, weights, ws, s));
-  MOE_TRY(run_route_and_group(desc, p, weights, ws, topk_ids_out, topk_w_out, nullptr, nullptr,
-                              nullptr, s));
-  if (p.mfma) return run_experts_mfma(desc, p, x, weights, out, residual, ws, s);
-  return run_experts_gemv(desc, p, x, weights, out, residual, ws, s);
+  void* ws = nullptr;
+  MOE_TRY(scratch_for_device(s, &ws));
+  return forward_body(desc, p, num_tokens, x, weights, out, residual, topk_ids_out, topk_w_out,
+                      ws, s);
 }
 
 moe_status moe_packed_weight_bytes(const moe_desc* desc, size_t* gate_up_bytes,

@@ -233,3 +233,30 @@ def test_forward_rejects_unpaired_packed_weights_on_host(lib):
     st = lib.moe_ffn_forward(ctypes.byref(dd), 1, fake, ctypes.byref(w2), fake, None, None, None,
                              fake, 1 << 40, None)
     assert st == M.MOE_UNSUPPORTED
+
+
+def test_noalloc_rejects_calls_beyond_its_scratch_on_host(lib):
+    # the 4096-token prefill needs far more than the static scratch: the
+    # call is refused on the host, before any HIP call
+    d = _desc("prefill_shared_t4096")
+    assert M.workspace_size(d, 4096) > M.NOALLOC_SCRATCH_BYTES
+    fake = 1 << 20
+    w = M.make_weights(router=None)
+    w.router, w.gate, w.up, w.down = fake, fake, fake, fake
+    w.shared_gate_inp, w.shared_gate, w.shared_up, w.shared_down = fake, fake, fake, fake
+    st = lib.moe_ffn_forward_noalloc(ctypes.byref(d), 4096, fake, ctypes.byref(w), fake, None,
+                                     None, None, None)
+    assert st == M.MOE_UNSUPPORTED and "scratch" in lib.moe_last_error().decode()
+    # the bad-argument checks of moe_ffn_forward apply as well
+    st = lib.moe_ffn_forward_noalloc(ctypes.byref(d), 4, None, ctypes.byref(w), fake, None,
+                                     None, None, None)
+    assert st == M.MOE_INVALID_ARGUMENT
+    st = lib.moe_ffn_forward_noalloc(ctypes.byref(d), 0, fake, ctypes.byref(w), fake, None,
+                                     None, None, None)
+    assert st == M.MOE_OK
+
+
+def test_noalloc_scratch_bytes_matches_header():
+    src = open(os.path.join(ROOT, "include", "moe_ffn.h")).read()
+    m = re.search(r"#define MOE_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == M.NOALLOC_SCRATCH_BYTES
