@@ -81,6 +81,10 @@ def parse():
     ap.add_argument("--host-inputs", action="store_true",
                     help="generate inputs on the host (numpy) and copy them: no generator "
                          "kernels run on the GPU (for profiled runs)")
+    ap.add_argument("--inputs-dir", default=None,
+                    help="copy the inputs from .npy files in this directory when it has them, "
+                         "else generate them on the GPU and save them there (so that a "
+                         "profiled run can launch no generator kernels)")
     ap.add_argument("--cold-mib", type=int, default=512,
                     help="MiB copied between the steps of the cold-cache kernel pass "
                          "(0: no such pass)")
@@ -110,14 +114,71 @@ def _blas_threads():
     return max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
 
 
-def make_inputs_on_device(cfg, dev, host_inputs):
+_INPUT_FIELDS = ("x", "router", "router_bias", "gate", "up", "down", "shared_gate_inp",
+                 "shared_gate", "shared_up", "shared_down")
+
+
+def _save_inputs(inp, d):
+    """Storage-format copies of every input tensor, one .npy per array."""
+    import numpy as np
+    import torch
+    from moe_synth import U4Weights
+    os.makedirs(d, exist_ok=True)
+
+    def host(t):
+        if t.dtype in (torch.bfloat16, torch.float16):
+            return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        return t.contiguous().cpu().numpy()
+    for name in _INPUT_FIELDS:
+        v = getattr(inp, name)
+        if v is None:
+            continue
+        if isinstance(v, U4Weights):
+            for part in ("codes", "scales", "mins"):
+                np.save(os.path.join(d, f"{name}.{part}.npy"), host(getattr(v, part)))
+        else:
+            np.save(os.path.join(d, f"{name}.npy"), host(v))
+
+
+def _load_inputs(cfg, d):
+    """A host MoeInputs read back from _save_inputs' files (memory-mapped)."""
+    import numpy as np
+    from moe_synth import MoeInputs, U4Weights, WF_U4
+
+    def ld(name):
+        f = os.path.join(d, f"{name}.npy")
+        return np.load(f, mmap_mode="r") if os.path.exists(f) else None
+    vals = {}
+    for name in _INPUT_FIELDS:
+        if cfg.weight_format == WF_U4 and name in ("gate", "up", "down"):
+            K = cfg.I if name == "down" else cfg.H
+            vals[name] = U4Weights(ld(f"{name}.codes"), ld(f"{name}.scales"),
+                                   ld(f"{name}.mins"), K, cfg.group_size)
+        else:
+            vals[name] = ld(name)
+    inp = MoeInputs(cfg, vals["x"], vals["router"], vals["router_bias"], vals["gate"],
+                    vals["up"], vals["down"], backend="numpy")
+    for name in _INPUT_FIELDS[6:]:
+        setattr(inp, name, vals[name])
+    return inp
+
+
+def make_inputs_on_device(cfg, dev, host_inputs, inputs_dir=None):
     """The workload's inputs resident in HBM.  host_inputs: generated with
-    the numpy generator and copied (no generator kernels run on the GPU)."""
+    the numpy generator and copied (no generator kernels run on the GPU).
+    inputs_dir: when it holds this workload's arrays, they are copied from
+    there (again no generator kernels); else they are generated on the GPU
+    and saved there, for a later (profiled) run."""
     from moe_synth import generate
     from moe_synth.device import to_device
+    if inputs_dir and os.path.exists(os.path.join(inputs_dir, "x.npy")):
+        return to_device(_load_inputs(cfg, inputs_dir), dev)
     if host_inputs:
         return to_device(generate(cfg, backend="numpy"), dev)
-    return generate(cfg, backend="torch", device=dev)
+    inp = generate(cfg, backend="torch", device=dev)
+    if inputs_dir:
+        _save_inputs(inp, inputs_dir)
+    return inp
 
 
 def token_pool(M, cfg, desc, w, inp, P, dev, host_inputs, window=3):
@@ -362,7 +423,9 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    inp = make_inputs_on_device(cfg, dev, args.host_inputs)
+    loaded = bool(args.inputs_dir) and os.path.exists(os.path.join(args.inputs_dir, "x.npy"))
+    inp = make_inputs_on_device(cfg, dev, args.host_inputs, args.inputs_dir)
+    host_side = args.host_inputs or loaded    # the token pool is drawn on the host too
     gating = {"softmax": M.GATING_SOFTMAX, "sigmoid": M.GATING_SIGMOID}[args.gating]
     desc = M.make_desc(**desc_kwargs(cfg, gating=gating, routed_scale=args.routed_scale),
                        norm_eps=args.pre_norm)
@@ -386,7 +449,7 @@ def main():
     T = cfg.T
     decode = T <= 32
     P = args.pool if decode else 1
-    xs, window = token_pool(M, cfg, desc, w, inp, P, dev, args.host_inputs)
+    xs, window = token_pool(M, cfg, desc, w, inp, P, dev, host_side)
     ws = M.alloc_workspace(desc, T, dev)
     out = torch.empty((T, cfg.H), dtype=torch.float32, device=dev)
 

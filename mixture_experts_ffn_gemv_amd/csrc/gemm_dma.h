@@ -46,10 +46,7 @@ constexpr int kDmaThreads = 64 * kDmaWaves;
 constexpr int kDmaBK = 64;                     // K per stage: full 128-byte rows
 constexpr int kDmaSlotsB = 2;                  // LDS slots of the route operand (32 KB each)
 constexpr int kDmaGroupT = 8;                  // route tiles per tile-order group
-#ifndef MOE_DMA_MIN_AVG_ROUTES
-#define MOE_DMA_MIN_AVG_ROUTES 96
-#endif
-constexpr int kDmaMinAvgRoutes = MOE_DMA_MIN_AVG_ROUTES;  // mean routes per expert
+constexpr int kDmaMinAvgRoutes = 96;           // mean routes per expert to take this kernel
 constexpr int kPackRows = 256;                   // weight rows per packed block
 constexpr int kPackBlock = kPackRows * kDmaBK * 2;  // bytes per packed block (32 KB)
 

@@ -332,9 +332,9 @@ moe_status run_route_and_group(const moe_desc* d, const Plan& p, const moe_weigh
   const int T = (int)p.T, R = (int)p.R;
   MOE_TRY(launch("topk", s, [&] {
     k_topk<<<(T + 3) / 4, 256, 0, s>>>(wsp<float>(ws, p.o_logits), T, p.E, p.k, p.ncols,
-                                       route_mode(d, w), p.shared ? 1 : 0, wsp<int32_t>(ws, p.o_ids),
-                                       wsp<float>(ws, p.o_wts), user_ids, user_w,
-                                       wsp<float>(ws, p.o_sgate));
+                                       route_mode(d, w), p.shared ? 1 : 0,
+                                       wsp<int32_t>(ws, p.o_ids), wsp<float>(ws, p.o_wts),
+                                       user_ids, user_w, wsp<float>(ws, p.o_sgate));
   }));
   MOE_TRY(launch("perm_hist", s, [&] {
     k_perm_hist<<<p.nblk, 256, 0, s>>>(wsp<int32_t>(ws, p.o_ids), R, p.E, wsp<int32_t>(ws, p.o_bhist));
@@ -527,15 +527,30 @@ void launch_dn3(bool one, int u, dim3 grid, hipStream_t s, const Dec2Params& dp)
 // or 16 when G is a multiple of 16 but not of 64 (at most 8 groups a lane).
 int u4_lpr(int G) { return (G % 64 != 0 && G % 16 == 0 && G <= 16 * 8) ? 16 : 64; }
 
+// Raises a kernel's dynamic-LDS limit to the full 160 KB, once per device
+// and kernel (launches then need no attribute call).
+std::mutex g_lds_mu;
+std::map<std::pair<int, const void*>, bool> g_lds_set;
+moe_status allow_full_lds(const void* kern, const char* name) {
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  std::lock_guard<std::mutex> lk(g_lds_mu);
+  auto key = std::make_pair(dev, kern);
+  if (g_lds_set.count(key)) return MOE_OK;
+  hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     kU4LdsMax);
+  if (e != hipSuccess)
+    return fail(MOE_HIP_ERROR, "allowing %d bytes of LDS for %s failed: %s", kU4LdsMax, name,
+                hipGetErrorString(e));
+  g_lds_set[key] = true;
+  return MOE_OK;
+}
+
 template <int MODE, int ACT>
 moe_status launch_u4(const char* name, int G, dim3 grid, size_t lds, hipStream_t s,
                      const Dec2Params& dp) {
   auto go = [&](auto kern) -> moe_status {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess)
-      return fail(MOE_HIP_ERROR, "setting %zu bytes of LDS for %s failed: %s", lds, name,
-                  hipGetErrorString(e));
+    MOE_TRY(allow_full_lds(reinterpret_cast<const void*>(kern), name));
     return launch(name, s, [&] { kern<<<grid, 256, lds, s>>>(dp); });
   };
   const int lpr = u4_lpr(G);

@@ -220,15 +220,14 @@ __device__ __forceinline__ float expert_scale_of(const RouteMode& rm, int e) {
 // per-expert scale multiplies the selected numerators (and so the
 // renormalising sum) only.
 // --------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_topk(
-    const float* __restrict__ logits, int T, int E, int k, int ncols,
-    RouteMode rm, int has_shared, int32_t* __restrict__ ids,
-    float* __restrict__ wts, int32_t* __restrict__ user_ids,
-    float* __restrict__ user_w, float* __restrict__ sgate) {
+// One token's routing in one wave: l points at the token's logits (global
+// or LDS), column E holding the shared expert's gate logit when there is
+// one.  Lane j < k writes top-k position j.
+__device__ __forceinline__ void topk_token(const float* l, int t, int E, int k, RouteMode rm,
+                                           int has_shared, int32_t* __restrict__ ids,
+                                           float* __restrict__ wts, int32_t* __restrict__ user_ids,
+                                           float* __restrict__ user_w, float* __restrict__ sgate) {
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  const float* l = logits + (size_t)t * ncols;
   float v[4];
   unsigned taken = 0;  // bit q: candidate q of this lane is used up (or absent)
 #pragma unroll
@@ -274,6 +273,17 @@ __global__ __launch_bounds__(256) void k_topk(
     if (user_w) user_w[(size_t)t * k + lane] = w;
   }
   if (has_shared && lane == 0) sgate[t] = sigmoid_f(l[E]);
+}
+
+__global__ __launch_bounds__(256) void k_topk(
+    const float* __restrict__ logits, int T, int E, int k, int ncols,
+    RouteMode rm, int has_shared, int32_t* __restrict__ ids,
+    float* __restrict__ wts, int32_t* __restrict__ user_ids,
+    float* __restrict__ user_w, float* __restrict__ sgate) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  topk_token(logits + (size_t)t * ncols, t, E, k, rm, has_shared, ids, wts, user_ids, user_w,
+             sgate);
 }
 
 // --------------------------------------------------------------------------

@@ -12,6 +12,7 @@ Usage:
       --kernel gemv_gateup=k_dec_gateup3 --kernel gemv_down_combine=k_dec_down3 \
       --out profiles/traffic.json
   python -m mixture_experts_ffn_gemv_amd.profiling stats --csv FILE
+  python -m mixture_experts_ffn_gemv_amd.profiling counters --dir DIR
 """
 from __future__ import annotations
 
@@ -137,6 +138,51 @@ def cmd_stats(a) -> None:
                   f"{float(r['Percentage']):.2f} |")
 
 
+def cmd_counters(a) -> None:
+    """Markdown table of per-dispatch averages of the counters of one
+    --pmc pass, for the library's kernels (and the derived rates below)."""
+    per: dict = {}
+    with open(_counter_csv(a.dir)) as fh:
+        for r in csv.DictReader(fh):
+            if "moe::" not in r["Kernel_Name"]:
+                continue
+            name = r["Kernel_Name"].replace("moe::", "").split("(")[0]
+            per.setdefault(name, {}).setdefault(r["Counter_Name"], []).append(
+                float(r["Counter_Value"]))
+    names = sorted({c for v in per.values() for c in v})
+    print("| kernel | dispatches | " + " | ".join(names) + " |")
+    print("|---|---|" + "---|" * len(names))
+    avg = {}
+    for k, v in per.items():
+        avg[k] = {c: sum(x) / len(x) for c, x in v.items()}
+        n = len(next(iter(v.values())))
+        print(f"| `{k}` | {n} | " + " | ".join(f"{avg[k].get(c, float('nan')):.4g}"
+                                                 for c in names) + " |")
+    # derived: MFMA busy (per SIMD, over the GPU-active cycles of all SIMDs),
+    # bf16 MFMA flops (512 per MOP), LDS bank-conflict cycles per active LDS cycle
+    rows = []
+    for k, c in avg.items():
+        d = {}
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in c and "GRBM_GUI_ACTIVE" in c:
+            d["mfma_busy"] = c["SQ_VALU_MFMA_BUSY_CYCLES"] / (c["GRBM_GUI_ACTIVE"] * a.cus * 4)
+        if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in c:
+            d["mfma_bf16_tflop"] = c["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512 / 1e12
+        if "SQ_LDS_BANK_CONFLICT" in c and c.get("SQ_LDS_IDX_ACTIVE"):
+            d["lds_conflict_per_active"] = c["SQ_LDS_BANK_CONFLICT"] / c["SQ_LDS_IDX_ACTIVE"]
+        if "SQ_INSTS_VALU" in c and "GRBM_GUI_ACTIVE" in c:
+            # a wave64 VALU instruction occupies a 16-lane SIMD for 4 cycles
+            d["valu_busy"] = c["SQ_INSTS_VALU"] * 4 / (c["GRBM_GUI_ACTIVE"] * a.cus * 4)
+        if d:
+            rows.append((k, d))
+    if rows:
+        print()
+        print("| kernel | " + " | ".join(sorted({x for _, d in rows for x in d})) + " |")
+        keys = sorted({x for _, d in rows for x in d})
+        print("|---|" + "---|" * len(keys))
+        for k, d in rows:
+            print(f"| `{k}` | " + " | ".join(f"{d[x]:.4g}" if x in d else "" for x in keys) + " |")
+
+
 def main() -> None:
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -149,8 +195,11 @@ def main() -> None:
     t.add_argument("--out", default=TRAFFIC_JSON)
     s = sub.add_parser("stats")
     s.add_argument("--csv", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("--dir", required=True, help="output directory of one --pmc pass")
+    c.add_argument("--cus", type=int, default=256, help="compute units of the GPU")
     a = ap.parse_args()
-    {"traffic": cmd_traffic, "stats": cmd_stats}[a.cmd](a)
+    {"traffic": cmd_traffic, "stats": cmd_stats, "counters": cmd_counters}[a.cmd](a)
 
 
 if __name__ == "__main__":
