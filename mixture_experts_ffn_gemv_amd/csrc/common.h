@@ -84,6 +84,8 @@ constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
 constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141;
 constexpr int kDppMirror = 0x140;
+constexpr int kDppRowRor4 = 0x124;   // row_ror:4 (rotate within 16-lane rows)
+constexpr int kDppRowRor8 = 0x128;   // row_ror:8
 __device__ __forceinline__ float readlane_f(float v, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }

@@ -1,27 +1,26 @@
 // Decode path for 4-bit affine weights (codes in groups of 32 along K, one
-// f16 scale and one f16 min per group: w = code * scale + min), T <= 32.
+// f16 scale and one f16 min per group: w = code * scale + min), T <= 32 (any
+// T runs, in chunks of up to 4 routes per expert).
 //
-// One workgroup per (touched expert, block of output rows).  The activations
-// of the expert's routes (x for gate/up, h for down), up to kU4Routes per
-// pass, are staged once in LDS and shared by every row of the block, in a
-// group-contiguous layout: 16-byte piece q of 32-element group c of route r
-// sits at float4 index (r*G + c)*9 + q (G groups per row, one float4 of
-// padding per group), so a lane reads its group's 8 pieces at immediate
-// offsets from one address, and the 144-byte stride between the lanes'
-// groups keeps every 8 or 16 lanes of a ds_read_b128 on distinct banks.
-// Next to them, the sum of each group's 32 activations.
+// The dot products run on the 4x4x4 (16-block) f16 MFMA with the codes
+// exact.  Per group g of a weight row and route r:
+//   sum_i (c_i s + m) x_ri = s * sum_i c_i x_ri + m * sum_i x_ri,
+// the first sum on the MFMA, the second from a staged per-group sum.  The
+// codes enter as the f16 integers 0..15 (normal numbers, so the products are
+// exact); each activation as two f16 terms hi + lo of the route's row scaled
+// by a power of two, about 22 significant bits, and the MFMA accumulates in
+// f32.
 //
-// A group of one row is dequantised once and reused for every route:
-//   sum_i (c_i*s + m) x_i = s * sum_i c_i x_i + m * sum_i x_i,
-// the nibbles go to floats by byte-wise conversion, and the second term
-// takes the staged group sum.  Per weight element that is about 1.25
-// conversion operations plus one FMA per route.
+// Launches: k_u4_stage (each token's x row, and the expert work list), the
+// gate/up kernel, k_u4_stage again (each route's h row), the down kernel,
+// then the weighted combine.
 //
-// gate/up: each wave owns features f (gate row and up row of f); the epilogue
-//          writes h = act(gate) * up (f32).
-// down   : each wave owns output rows n; writes y[position, n] (f32, rows in
-//          the expert-grouped order), summed per token with the routing
-//          weights by k_combine.
+// Lane layout of v_mfma_f32_4x4x4f16 (16 blocks of 4x4 outputs, 4 k each):
+// lane l = 4b + j of block b holds row j of A (here: staged route slot j)
+// and column j of B (here: row j of a quad of weight rows), 4 k values each;
+// output D[b][i][j] comes back in lane 4b + j, register i.  Block b takes
+// groups b + 16u of the weight row, so one MFMA step covers one 8-element
+// word of 16 groups for 4 weight rows and 4 routes.
 #pragma once
 
 #include "common.h"
@@ -30,266 +29,429 @@
 
 namespace moe {
 
-constexpr int kU4Routes = 4;     // most routes staged per pass (Dec2Params::rc may be fewer)
-constexpr int kU4Rows = 32;      // output rows (features) per workgroup
-constexpr int kU4LdsMax = 160 * 1024 - 4096;  // LDS bytes available to the staging
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
-// LDS bytes per staged route of row length K: activations plus group sums.
-constexpr int kU4GroupF4 = 9;   // float4 slots per staged group (8 pieces + padding)
-__host__ __device__ constexpr int u4_route_bytes(int K) { return (K / 32) * (kU4GroupF4 * 16 + 4); }
+constexpr int kU4Waves = 8;                     // waves per expert-kernel workgroup
+constexpr int kU4Threads = 64 * kU4Waves;
+constexpr int kU4LdsMax = 160 * 1024 - 4096;    // dynamic LDS an expert kernel may take
+constexpr int kU4StageThreads = 256;
+// groups per lane per step (UG) and row pairs per wave (PW) of the two
+// expert kernels: gate/up 128 features a workgroup, down 256 output rows
+constexpr int kU4UGGateUp = 2, kU4PWGateUp = 4;
+constexpr int kU4UGDown = 1, kU4PWDown = 4;
 
-// Byte n of v as a float, one v_cvt_f32_ubyte{n} (written out: from the
-// shifted-and-masked C expression the compiler emits a bit-field extract
-// and then the byte-0 conversion, two instructions).
-template <int N>
-__device__ __forceinline__ float ubyte_f(uint32_t v) {
-  float f;
-  if constexpr (N == 0) asm("v_cvt_f32_ubyte0 %0, %1" : "=v"(f) : "v"(v));
-  else if constexpr (N == 1) asm("v_cvt_f32_ubyte1 %0, %1" : "=v"(f) : "v"(v));
-  else if constexpr (N == 2) asm("v_cvt_f32_ubyte2 %0, %1" : "=v"(f) : "v"(v));
-  else asm("v_cvt_f32_ubyte3 %0, %1" : "=v"(f) : "v"(v));
-  return f;
+// Staged activation row (one token of x, or one route of h), row length K,
+// G = K / 32 groups.  Value v of the row is multiplied by the row's power of
+// two sigma (largest |v| sigma < 2^15), the odd elements of each 8-element
+// word also by 1/16 (their codes enter as 16 c), and split into f16
+// hi = f16(v') and lo = f16(v' - hi).  Group c takes 128 bytes: word q gives
+// two 16-byte pieces, even elements (0, 4, 2, 6) and odd elements
+// (1, 5, 3, 7), each hi[4] then lo[4]; piece p sits at slot p ^ u4_swz(c).
+// Beside the rows: each group's plain f32 sum, and the row's factor
+// 1 / sigma.
+__host__ __device__ constexpr size_t u4_row_bytes(int G) { return (size_t)G * 128; }
+__device__ __forceinline__ int u4_swz(int c) { return (c ^ (c >> 1)) & 1; }
+
+// Expert-kernel LDS: staged route slot r at r * (RS + 32), RS a multiple of
+// 256 with room for the 96-byte shift of slot 3; the group sums of 4 slots
+// as float4[G]; 16 floats of slot factors; per wave 512 UG bytes for the
+// step's scales and mins.  The group swizzle together with the 32-byte slot
+// shift keeps the A-operand reads (lane 4b + j: slot j, group b + 16u, one
+// piece) on distinct banks for every 8 and 16 lanes.
+__host__ __device__ constexpr int u4_route_stride(int G) { return (G * 128 + 96 + 255) / 256 * 256; }
+__host__ __device__ constexpr int u4_lds_bytes(int K, int UG, int nslot) {
+  return nslot * u4_route_stride(K / 32) + (K / 32) * 16 + 64 + kU4Waves * 512 * UG;
 }
 
-// 8 nibbles of one 32-bit word -> floats, in element order (low nibble
-// first): two masks, one shift and eight byte conversions.
-__device__ __forceinline__ void nib8(uint32_t w, float (&f)[8]) {
-  const uint32_t lo = w & 0x0F0F0F0Fu;          // elements 0, 2, 4, 6 in bytes 0..3
-  const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;   // elements 1, 3, 5, 7
-  f[0] = ubyte_f<0>(lo); f[1] = ubyte_f<0>(hi);
-  f[2] = ubyte_f<1>(lo); f[3] = ubyte_f<1>(hi);
-  f[4] = ubyte_f<2>(lo); f[5] = ubyte_f<2>(hi);
-  f[6] = ubyte_f<3>(lo); f[7] = ubyte_f<3>(hi);
+// (w & mask) | magic in one instruction: the VOP3 form takes no literal, so
+// the mask comes from a scalar register and the magic from a vector one.
+__device__ __forceinline__ uint32_t and_or(uint32_t w, uint32_t mask, uint32_t magic) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(w), "s"(mask), "v"(magic));
+  return r;
 }
 
-// Stage the activations of nr routes (rows[rr], f32 or bf16, length K) and
-// their per-group sums.  Pieces are ordered (route, group, q) over the 256
-// threads, 8 consecutive threads holding one group, so a group's sum is a
-// butterfly over 8 lanes; each thread has kStageUnroll loads in flight.
-constexpr int kStageUnroll = 8;
-__device__ __forceinline__ void u4_stage(f32x4* __restrict__ xs, float* __restrict__ xsum, int nr,
-                                         int K, int act_bf16,
-                                         const void* const (&rows)[kU4Routes]) {
-  const int G = K / 32;
-  const int n = nr * G * 8;
-  for (int base = 0; base < n; base += 256 * kStageUnroll) {
-    f32x4 v[kStageUnroll];
+// Masked nibbles with the exponent of 1024 or-ed in (f16 values 1024 + v,
+// v < 2^10) -> the f16 values v exactly, by one packed f16 subtraction.
+__device__ __forceinline__ f16x4 codes4(uint32_t lo, uint32_t hi) {
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  const f16x2 k = {(_Float16)1024.f, (_Float16)1024.f};
+  const f16x2 a = __builtin_bit_cast(f16x2, lo) - k;
+  const f16x2 b = __builtin_bit_cast(f16x2, hi) - k;
+  return f16x4{a[0], a[1], b[0], b[1]};
+}
+
+// 8 consecutive values of an f32 or bf16 row.
+__device__ __forceinline__ void load8(const void* row, int bf16, size_t off, float (&v)[8]) {
+  if (bf16) {
+    const u32x4 b = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(row) + off);
 #pragma unroll
-    for (int j = 0; j < kStageUnroll; ++j) {
-      const int i = min(base + 256 * j + (int)threadIdx.x, n - 1);  // clamped: loads stay unconditional
-      const int q = i & 7, rc = i >> 3;
-      const int rr = rc / G, c = rc - rr * G;
-      const size_t off = (size_t)c * 32 + (size_t)q * 4;
-      if (act_bf16) {
-        const u32x2 b2 = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(rows[rr]) + off);
-        v[j] = f32x4{bf16lo(b2[0]), bf16hi(b2[0]), bf16lo(b2[1]), bf16hi(b2[1])};
-      } else {
-        v[j] = *reinterpret_cast<const f32x4*>(static_cast<const float*>(rows[rr]) + off);
+    for (int e = 0; e < 4; ++e) { v[2 * e] = bf16lo(b[e]); v[2 * e + 1] = bf16hi(b[e]); }
+  } else {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(static_cast<const float*>(row) + off);
+    const f32x4 c = *reinterpret_cast<const f32x4*>(static_cast<const float*>(row) + off + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { v[e] = a[e]; v[4 + e] = c[e]; }
+  }
+}
+
+__device__ __forceinline__ uint32_t pack_h2(_Float16 a, _Float16 b) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+struct U4Stage {
+  const void* src;     // rows [rows, K], f32 or bf16
+  int src_bf16;
+  int K, rows;
+  uint8_t* stage;      // [rows, G * 128]
+  float* gsum;         // [rows, G]
+  float* fac;          // [rows]
+  // the expert kernels' work list, built by one extra workgroup when qlist
+  // is set: for each active slot s, ceil(count / nslot) entries
+  // s | chunk << 16, in slot order; qn = their number
+  const int32_t* counts;
+  const int32_t* active;
+  const int32_t* n_active;
+  int32_t* qlist;
+  int32_t* qn;
+  int E, qmax, nslot;
+};
+
+// One workgroup per row (plus, with qlist set, one for the work list).
+__global__ __launch_bounds__(kU4StageThreads) void k_u4_stage(U4Stage p) {
+  constexpr int NT = kU4StageThreads;
+  __shared__ float wmax[NT / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int row = blockIdx.x;
+  if (row >= p.rows) {
+    if (!p.qlist || wave != 0) return;
+    const int na = min(max(*p.n_active, 0), p.E + 1);
+    int total = 0;
+    for (int s0 = 0; s0 < na; s0 += 64) {
+      const int s = s0 + lane;
+      int nq = 0;
+      if (s < na) nq = (max(p.counts[ws_group(p.active[s], p.E, false)], 0) + p.nslot - 1) / p.nslot;
+      int inc = nq;  // inclusive scan over the wave
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(inc, o, 64);
+        if (lane >= o) inc += t;
       }
+      const int first = total + inc - nq;
+      for (int q = 0; q < nq; ++q)
+        if (first + q < p.qmax) p.qlist[first + q] = s | (q << 16);
+      total += __shfl(inc, 63, 64);
     }
-#pragma unroll
-    for (int j = 0; j < kStageUnroll; ++j) {
-      const int i = base + 256 * j + (int)threadIdx.x;
-      const bool ok = i < n;
-      const int q = i & 7, rc = i >> 3;
-      const int rr = rc / G, c = rc - rr * G;
-      if (ok) xs[(rr * G + c) * kU4GroupF4 + q] = v[j];
-      float sm = ok ? (v[j][0] + v[j][1]) + (v[j][2] + v[j][3]) : 0.f;
-      sm += __shfl_xor(sm, 1, 64);
-      sm += __shfl_xor(sm, 2, 64);
-      sm += __shfl_xor(sm, 4, 64);
-      if (ok && q == 0) xsum[rr * G + c] = sm;
-    }
+    if (lane == 0) *p.qn = min(total, p.qmax);
+    return;
   }
-}
-
-// Dot products of one 32-element group of two rows (codes v0/v1, scales,
-// mins) with the staged activations of nr routes:
-//   acc[k][r] += sc_k * sum_i c_ki x_ri + mn_k * xsum_r.
-// Each activation read from LDS serves both rows.
-template <bool BATCH>
-__device__ __forceinline__ void u4_group_dot2(const u32x4& v0, uint32_t sm0, const u32x4& v1,
-                                              uint32_t sm1, const f32x4* __restrict__ xs,
-                                              const float* __restrict__ xsum, int G, int c, int nr,
-                                              float (&acc0)[kU4Routes], float (&acc1)[kU4Routes]) {
-  const float sc0 = f16_to_f32((uint16_t)sm0), mn0 = f16_to_f32((uint16_t)(sm0 >> 16));
-  const float sc1 = f16_to_f32((uint16_t)sm1), mn1 = f16_to_f32((uint16_t)(sm1 >> 16));
-  float w0[32], w1[32];
+  const int K = p.K, G = K / 32;
+  const void* src = p.src_bf16 ? static_cast<const void*>(static_cast<const uint16_t*>(p.src) + (size_t)row * K)
+                               : static_cast<const void*>(static_cast<const float*>(p.src) + (size_t)row * K);
+  const int n = G * 4;  // 8-element words
+  float mx = 0.f;
+  for (int i = tid; i < n; i += NT) {
+    float v[8];
+    load8(src, p.src_bf16, (size_t)i * 8, v);
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    float f[8], h[8];
-    nib8(v0[q], f);
-    nib8(v1[q], h);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) { w0[8 * q + j] = f[j]; w1[8 * q + j] = h[j]; }
+    for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(v[e]));
   }
+  mx = wave_max(mx);
+  if (lane == 0) wmax[wave] = mx;
+  __syncthreads();
+  float m = 0.f;
 #pragma unroll
-  for (int r = 0; r < kU4Routes; ++r) {
-    if (r < nr) {
-      // BATCH: the route's 8 LDS reads are all issued before the first
-      // multiply-add (read and use interleaved, each read's latency is
-      // exposed), at the cost of 32 more registers; without it the reads
-      // stream one by one
-      const f32x4* xr = xs + ((size_t)r * G + c) * kU4GroupF4;
-      const float xsr = xsum[r * G + c];
-      float d0 = 0.f, d1 = 0.f;
-      if constexpr (BATCH) {
-        f32x4 x4[8];
+  for (int w = 0; w < NT / 64; ++w) m = fmaxf(m, wmax[w]);
+  int e = 0;  // m < 2^e; rows of zeros or non-finite values keep sigma 2^15
+  if (m > 0.f && m <= 3.4e38f) (void)frexpf(m, &e);
+  e = max(-100, e);
+  const float sg = ldexpf(1.f, 15 - e);
+  if (tid == 0) p.fac[row] = ldexpf(1.f, e - 15);
+  uint8_t* dst = p.stage + (size_t)row * u4_row_bytes(G);
+  for (int base = 0; base < n; base += NT) {  // uniform trip count: all lanes shuffle
+    const int i = base + tid;
+    const bool ok = i < n;
+    const int ii = ok ? i : n - 1;
+    const int c = ii >> 2, q = ii & 3;
+    float v[8];
+    load8(src, p.src_bf16, (size_t)ii * 8, v);
+    float sm = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+    sm += __shfl_xor(sm, 1, 64);  // the group's 4 words are 4 consecutive threads
+    sm += __shfl_xor(sm, 2, 64);
+    if (!ok) continue;
+    const int sw = u4_swz(c);
 #pragma unroll
-        for (int q = 0; q < 8; ++q) x4[q] = xr[q];
+    for (int par = 0; par < 2; ++par) {
+      const float f = par ? sg * 0.0625f : sg;
+      _Float16 hi[4], lo[4];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            d0 = fmaf(w0[4 * q + e], x4[q][e], d0);
-            d1 = fmaf(w1[4 * q + e], x4[q][e], d1);
-          }
-        }
-      } else {
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const f32x4 x4 = xr[q];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            d0 = fmaf(w0[4 * q + e], x4[e], d0);
-            d1 = fmaf(w1[4 * q + e], x4[e], d1);
-          }
-        }
+      for (int k = 0; k < 4; ++k) {
+        const float a = v[par + ((k & 1) << 2) + ((k >> 1) << 1)] * f;  // elements 0, 4, 2, 6
+        hi[k] = (_Float16)a;
+        lo[k] = (_Float16)(a - (float)hi[k]);
       }
-      acc0[r] = fmaf(sc0, d0, fmaf(mn0, xsr, acc0[r]));
-      acc1[r] = fmaf(sc1, d1, fmaf(mn1, xsr, acc1[r]));
+      const u32x4 pc = {pack_h2(hi[0], hi[1]), pack_h2(hi[2], hi[3]), pack_h2(lo[0], lo[1]),
+                        pack_h2(lo[2], lo[3])};
+      *reinterpret_cast<u32x4*>(dst + (size_t)c * 128 + (((2 * q + par) ^ sw) * 16)) = pc;
     }
+    if (q == 0) p.gsum[(size_t)row * G + c] = sm;
   }
 }
 
-// One group of one row: codes (16 bytes) plus the f16 bits of its scale and
-// min.  The loads are unconditional (the group index is clamped; lanes past
-// the row's end skip the group): a load inside a branch, or a conversion of
-// its result inside one, makes the compiler wait for it on the spot.
-__device__ __forceinline__ void u4_load(const MatStack& m, size_t row, int G, int c, u32x4& v,
-                                        uint32_t& sc_mn) {
-  const size_t gi = row * G + min(c, G - 1);
-  v = ld16_stream(m.p + gi * 16);
-  sc_mn = (uint32_t)m.sc[gi] | ((uint32_t)m.mn[gi] << 16);
-}
+// The step's scales and mins for one lane: 8 UG bytes.
+template <int UG> struct U4ScaleVec { typedef u32x2 type; };
+template <> struct U4ScaleVec<2> { typedef u32x4 type; };
 
-// MODE 0: gate/up (K = H, rows = I features, two matrices); 1: down (K = I,
-// rows = H outputs).  LPR lanes share a row (64: the whole wave; 16: four
-// rows side by side, for rows whose group count is not a multiple of 64,
-// e.g. 48 groups at K = 1536 would leave a quarter of a 64-lane wave
-// idle); U groups per lane cover it (LPR*U >= K/32).
-template <int MODE, int ACT, int U, int LPR>
-__global__ __launch_bounds__(256) void k_dec_u4(Dec2Params p) {
-  constexpr int SEGS = 64 / LPR;  // rows side by side in a wave
-  extern __shared__ __attribute__((aligned(16))) float u4lds[];
-  const int s = blockIdx.x;
-  if (s >= *p.n_active) return;
+struct U4Experts {
+  Dec2Params d;
+  const uint8_t* stage;  // staged rows: tokens (gate/up) or routes (down)
+  const float* gsum;
+  const float* fac;
+  const int32_t* qlist;
+  const int32_t* qn;
+  int nslot;             // routes per work-list entry, 1..4
+};
+
+// MODE 0: gate/up (K = H, N = I features; row sets: the gate and the up row
+// of feature j of the quad); MODE 1: down (K = I, N = H outputs; row sets:
+// two quads of output rows).  One workgroup per (work-list entry, block of
+// rows).  UG groups per lane per step, PW row pairs per wave.  SV: the
+// step's scales and mins (16 UG groups of the 8 rows, both arrays) come in as
+// one coalesced load of 8 UG bytes per lane and reach the lanes that use
+// them through a per-wave LDS slot (needs G a multiple of 4 UG); otherwise
+// each lane loads its own 2-byte values.
+template <int MODE, int ACT, int UG, int PW, bool SV>
+__global__ __launch_bounds__(kU4Threads) __attribute__((amdgpu_waves_per_eu(4)))
+void k_u4_mfma(U4Experts ep) {
+  static_assert(!SV || UG == 1 || UG == 2, "vector scale loads cover 1 or 2 groups per lane");
+  constexpr int NT = kU4Threads;
+  constexpr int RPS = MODE == 0 ? 4 : 8;  // weight rows per pair step
+  typedef typename U4ScaleVec<UG>::type SVec;
+  extern __shared__ __attribute__((aligned(16))) uint8_t u4lds[];
+  const Dec2Params& p = ep.d;
+  const int wi = blockIdx.x;
+  if (wi >= *ep.qn) return;
+  const int qe = ep.qlist[wi];
+  const int s = qe & 0xFFFF, chunk = qe >> 16;
   const int R = p.T * p.k;
   const int g = ws_group(p.active[s], p.E, false);
   const int K = MODE == 0 ? p.H : p.I;
   const int N = MODE == 0 ? p.I : p.H;
   const int G = K / 32;
-  const int rb = blockIdx.y * kU4Rows * SEGS;
+  const int rb = blockIdx.y * (kU4Waves * PW * RPS);
   if (rb >= N) return;
   int count = p.counts[g], base = p.offsets[g];
   ws_span(base, count, R);
-  const int rc = p.rc;  // routes per pass (<= kU4Routes), sized to the LDS
-  f32x4* xs = reinterpret_cast<f32x4*>(u4lds);
-  float* xsum = u4lds + (size_t)rc * G * kU4GroupF4 * 4;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int seg = lane / LPR, sl = lane % LPR;  // the lane's row segment, lane in it
-  constexpr int RPW = kU4Rows / 4;  // rows per wave segment
+  const int r0 = ep.nslot * chunk;
+  if (r0 >= count) return;
+  const int nr = min(ep.nslot, count - r0);
+  const int RS = u4_route_stride(G);
+  uint8_t* xs = u4lds;
+  f32x4* xsum4 = reinterpret_cast<f32x4*>(u4lds + ep.nslot * RS);
+  float* rfac = reinterpret_cast<float*>(xsum4 + G);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint8_t* sbuf = reinterpret_cast<uint8_t*>(rfac + 16) + wave * (512 * UG);
+  const int b = lane >> 2, j = lane & 3;
+  const int NU = (G + 15) / 16, NCH = (NU + UG - 1) / UG;
+  const int nsteps = PW * NCH;
+  const MatStack& ma = MODE == 0 ? p.gate : p.down;
+  const MatStack& mb = MODE == 0 ? p.up : p.down;
 
-  for (int r0 = 0; r0 < count; r0 += rc) {
-    const int nr = min(rc, count - r0);
-    __syncthreads();  // the previous pass is done with the staged rows
-    const void* rows[kU4Routes];
+  // staged row of slot i (i < nr)
+  auto srow = [&](int i) __attribute__((always_inline)) -> int {
+    const int route = ws_route(p.perm[base + r0 + i], R);
+    return MODE == 0 ? route / p.k : route;
+  };
+
+  // ---- the slots' staged rows into LDS (plain copies), the first batch
+  // issued before the first step's weights
+  const size_t rowb = u4_row_bytes(G);
+  const int n16 = (int)(rowb / 16);
+  const int ncopy = nr * n16;
+  constexpr int kCopy = 8;  // 16-byte pieces in flight per thread
+  u32x4 cp[kCopy];
+  int cdst[kCopy];
+  auto copy_load = [&](int it) __attribute__((always_inline)) {
 #pragma unroll
-    for (int rr = 0; rr < kU4Routes; ++rr) {
-      const int route = ws_route(p.perm[base + r0 + min(rr, nr - 1)], R);
-      if constexpr (MODE == 0) {
-        const int t = route / p.k;
-        rows[rr] = p.x_bf16 ? static_cast<const void*>(static_cast<const uint16_t*>(p.x) + (size_t)t * K)
-                            : static_cast<const void*>(static_cast<const float*>(p.x) + (size_t)t * K);
-      } else {
-        rows[rr] = p.h + (size_t)route * K;
+    for (int k = 0; k < kCopy; ++k) {
+      const int i = min((it * kCopy + k) * NT + tid, ncopy - 1);  // clamped: loads stay unconditional
+      const int slot = i / n16, pc = i - slot * n16;
+      cp[k] = *reinterpret_cast<const u32x4*>(ep.stage + (size_t)srow(slot) * rowb + (size_t)pc * 16);
+      cdst[k] = slot * (RS + 32) + pc * 16;
+    }
+  };
+  auto copy_store = [&](int it) __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < kCopy; ++k)
+      if ((it * kCopy + k) * NT + tid < ncopy) *reinterpret_cast<u32x4*>(xs + cdst[k]) = cp[k];
+  };
+  copy_load(0);
+
+  auto rows_of = [&](int pw, int jj, int& n0, int& n1) __attribute__((always_inline)) {
+    const int q0 = rb + (wave * PW + pw) * RPS + jj;
+    n0 = q0;
+    n1 = MODE == 0 ? q0 : q0 + 4;
+  };
+  // codes of the step's groups for the lane's two rows (and their scales)
+  auto load = [&](int st, u32x4 (&va)[UG], u32x4 (&vb)[UG], uint32_t (&sa)[UG],
+                  uint32_t (&sb)[UG], SVec& sv) __attribute__((always_inline)) {
+    const int pw = st / NCH, ch = st - pw * NCH;
+    int n0, n1;
+    rows_of(pw, j, n0, n1);
+    const size_t ra = (size_t)g * N + min(n0, N - 1), rbb = (size_t)g * N + min(n1, N - 1);
+#pragma unroll
+    for (int uu = 0; uu < UG; ++uu) {
+      const int c = min(b + 16 * (ch * UG + uu), G - 1);  // clamped groups contribute zero
+      const size_t ga = ra * G + c, gb = rbb * G + c;
+      va[uu] = ld16_stream(ma.p + ga * 16);
+      vb[uu] = ld16_stream(mb.p + gb * 16);
+      if constexpr (!SV) {
+        sa[uu] = (uint32_t)ma.sc[ga] | ((uint32_t)ma.mn[ga] << 16);
+        sb[uu] = (uint32_t)mb.sc[gb] | ((uint32_t)mb.mn[gb] << 16);
       }
     }
-    u4_stage(xs, xsum, nr, K, MODE == 0 ? p.x_bf16 : 0, rows);
-    __syncthreads();
+    if constexpr (SV) {
+      // segment (row set rs, array kind, row jj): 16 UG groups, 4 lanes each
+      const int sg = lane >> 2, part = lane & 3;
+      const int rs = sg >> 3, kind = (sg >> 2) & 1, jj = sg & 3;
+      int m0, m1;
+      rows_of(pw, jj, m0, m1);
+      const int n = min(rs ? m1 : m0, N - 1);
+      const MatStack& m = rs ? mb : ma;
+      const uint16_t* arr = kind ? m.mn : m.sc;
+      int gs = 16 * UG * ch + 4 * UG * part;
+      gs = gs < G ? gs : 0;  // past the row's end: any in-bounds groups (unused)
+      sv = *reinterpret_cast<const SVec*>(arr + ((size_t)g * N + n) * G + gs);
+    }
+  };
+  u32x4 va[UG], vb[UG], nva[UG], nvb[UG];
+  uint32_t sa[UG], sb[UG], nsa[UG], nsb[UG];
+  SVec sv, nsv;
+  load(0, va, vb, sa, sb, sv);
+  copy_store(0);
+  for (int it = 1; it * kCopy * NT < ncopy; ++it) {
+    copy_load(it);
+    copy_store(it);
+  }
+  for (int i = tid; i < G * 4; i += NT) {
+    const int c = i >> 2, r = i & 3;
+    reinterpret_cast<float*>(xsum4)[i] = r < nr ? ep.gsum[(size_t)srow(r) * G + c] : 0.f;
+  }
+  if (tid < 4) rfac[tid] = ep.fac[srow(min(tid, nr - 1))];
+  __syncthreads();
 
-    // Two rows per step: gate and up of feature n (gate/up), or output rows
-    // n and n+1 (down); each activation read from LDS serves both.
-    constexpr int STEPS = MODE == 0 ? RPW : RPW / 2;
-    auto rows_of = [&](int i, size_t& ra, size_t& rb2, int& na, int& nb) {
-      const int r0w = rb + (wave * SEGS + seg) * RPW;
-      if constexpr (MODE == 0) {
-        na = nb = r0w + i;
-      } else {
-        na = r0w + 2 * i;
-        nb = na + 1;
-      }
-      ra = (size_t)g * N + min(na, N - 1);  // rows past N are clamped and never stored
-      rb2 = (size_t)g * N + min(nb, N - 1);
-    };
-    auto load2 = [&](int i, u32x4 (&va)[U], uint32_t (&sa)[U], u32x4 (&vb)[U],
-                     uint32_t (&sb)[U]) {
-      size_t ra, rb2;
-      int na, nb;
-      rows_of(i, ra, rb2, na, nb);
+  const int jr = min(j, nr - 1);  // A rows past the slots repeat the last (never stored)
+  const uint8_t* xa = xs + (size_t)jr * (RS + 32);
+  const int fo = u4_swz(b);       // swizzle of the lane's groups b + 16u
+  float fac[4];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int c = sl + LPR * u;
-        if constexpr (MODE == 0) {
-          u4_load(p.gate, ra, G, c, va[u], sa[u]);
-          u4_load(p.up, rb2, G, c, vb[u], sb[u]);
-        } else {
-          u4_load(p.down, ra, G, c, va[u], sa[u]);
-          u4_load(p.down, rb2, G, c, vb[u], sb[u]);
-        }
-      }
-    };
-    // weights of step i+1 are loaded while step i is multiplied (the copy at
-    // the end of the step waits for them, after the multiplies)
-    u32x4 va[U], vb[U], nva[U], nvb[U];
-    uint32_t sa[U], sb[U], nsa[U], nsb[U];
-    load2(0, va, sa, vb, sb);
+  for (int i = 0; i < 4; ++i) fac[i] = rfac[i];
+  const uint32_t magic = 0x64006400u;
+
+  // per route: sum over groups of s * D (aS) and of m * group sum (aM)
+  float aS0[4], aM0[4], aS1[4], aM1[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { aS0[i] = aM0[i] = aS1[i] = aM1[i] = 0.f; }
 #pragma unroll 1
-    for (int i = 0; i < STEPS; ++i) {
-      load2(min(i + 1, STEPS - 1), nva, nsa, nvb, nsb);
-      float a0[kU4Routes], a1[kU4Routes];
+  for (int st = 0; st < nsteps; ++st) {
+    load(min(st + 1, nsteps - 1), nva, nvb, nsa, nsb, nsv);
+    const int pw = st / NCH, ch = st - pw * NCH;
+    if constexpr (SV) *reinterpret_cast<SVec*>(sbuf + lane * (8 * UG)) = sv;
 #pragma unroll
-      for (int r = 0; r < kU4Routes; ++r) { a0[r] = 0.f; a1[r] = 0.f; }
+    for (int uu = 0; uu < UG; ++uu) {
+      const int c = b + 16 * (ch * UG + uu);
+      const int cc = min(c, G - 1);
+      const uint8_t* xg = xa + (size_t)cc * 128;
+      f32x4 d0 = {0.f, 0.f, 0.f, 0.f}, d1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int c = sl + LPR * u;
-        // gate/up stages more activations (fewer workgroups per CU) and has
-        // registers to spare at its occupancy; down does not
-        if (c < G) u4_group_dot2<MODE == 0>(va[u], sa[u], vb[u], sb[u], xs, xsum, G, c, nr, a0, a1);
+      for (int q = 0; q < 4; ++q) {
+        const u32x4 pe = *reinterpret_cast<const u32x4*>(xg + (((2 * q) ^ fo) << 4));
+        const u32x4 po = *reinterpret_cast<const u32x4*>(xg + (((2 * q + 1) ^ fo) << 4));
+        const uint32_t w0 = va[uu][q], w1 = vb[uu][q];
+        const uint32_t w08 = w0 >> 8, w18 = w1 >> 8;
+        // codes (0, 4, 2, 6) and 16 x codes (1, 5, 3, 7) of word q
+        const f16x4 b0e = codes4(and_or(w0, 0x000F000Fu, magic), and_or(w08, 0x000F000Fu, magic));
+        const f16x4 b0o = codes4(and_or(w0, 0x00F000F0u, magic), and_or(w08, 0x00F000F0u, magic));
+        const f16x4 b1e = codes4(and_or(w1, 0x000F000Fu, magic), and_or(w18, 0x000F000Fu, magic));
+        const f16x4 b1o = codes4(and_or(w1, 0x00F000F0u, magic), and_or(w18, 0x00F000F0u, magic));
+        const f16x4 ahe = __builtin_bit_cast(f16x4, u32x2{pe[0], pe[1]});
+        const f16x4 ale = __builtin_bit_cast(f16x4, u32x2{pe[2], pe[3]});
+        const f16x4 aho = __builtin_bit_cast(f16x4, u32x2{po[0], po[1]});
+        const f16x4 alo = __builtin_bit_cast(f16x4, u32x2{po[2], po[3]});
+        d0 = __builtin_amdgcn_mfma_f32_4x4x4f16(ahe, b0e, d0, 0, 0, 0);
+        d1 = __builtin_amdgcn_mfma_f32_4x4x4f16(ahe, b1e, d1, 0, 0, 0);
+        d0 = __builtin_amdgcn_mfma_f32_4x4x4f16(aho, b0o, d0, 0, 0, 0);
+        d1 = __builtin_amdgcn_mfma_f32_4x4x4f16(aho, b1o, d1, 0, 0, 0);
+        d0 = __builtin_amdgcn_mfma_f32_4x4x4f16(ale, b0e, d0, 0, 0, 0);
+        d1 = __builtin_amdgcn_mfma_f32_4x4x4f16(ale, b1e, d1, 0, 0, 0);
+        d0 = __builtin_amdgcn_mfma_f32_4x4x4f16(alo, b0o, d0, 0, 0, 0);
+        d1 = __builtin_amdgcn_mfma_f32_4x4x4f16(alo, b1o, d1, 0, 0, 0);
       }
-      size_t ra, rb2;
-      int na, nb;
-      rows_of(i, ra, rb2, na, nb);
+      uint32_t scm0, scm1;  // scale | min << 16 of row sets 0 and 1
+      if constexpr (SV) {
+        const uint16_t* sp = reinterpret_cast<const uint16_t*>(sbuf);
+        const int gl = b + 16 * uu;
+        constexpr int SEG = 16 * UG;  // u16 per segment
+        scm0 = (uint32_t)sp[(0 + j) * SEG + gl] | ((uint32_t)sp[(4 + j) * SEG + gl] << 16);
+        scm1 = (uint32_t)sp[(8 + j) * SEG + gl] | ((uint32_t)sp[(12 + j) * SEG + gl] << 16);
+      } else {
+        scm0 = sa[uu];
+        scm1 = sb[uu];
+      }
+      const bool ok = c < G;
+      const float s0 = ok ? f16_to_f32((uint16_t)scm0) : 0.f;
+      const float m0 = ok ? f16_to_f32((uint16_t)(scm0 >> 16)) : 0.f;
+      const float s1 = ok ? f16_to_f32((uint16_t)scm1) : 0.f;
+      const float m1 = ok ? f16_to_f32((uint16_t)(scm1 >> 16)) : 0.f;
+      const f32x4 xsm = xsum4[cc];
 #pragma unroll
-      for (int r = 0; r < kU4Routes; ++r) {
-        if (r < nr) {
-          const float d0 = LPR == 64 ? wave_sum(a0[r]) : group_sum<LPR>(a0[r]);
-          const float d1 = LPR == 64 ? wave_sum(a1[r]) : group_sum<LPR>(a1[r]);
-          if (sl == 0) {
+      for (int i = 0; i < 4; ++i) {
+        aS0[i] = fmaf(s0, d0[i], aS0[i]);
+        aM0[i] = fmaf(m0, xsm[i], aM0[i]);
+        aS1[i] = fmaf(s1, d1[i], aS1[i]);
+        aM1[i] = fmaf(m1, xsm[i], aM1[i]);
+      }
+    }
+    if (ch == NCH - 1) {
+      // the pair's rows are done: sum the 16 blocks (lanes j, j+4, ..., j+60)
+      float t0[4], t1[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float a = fmaf(aS0[i], fac[i], aM0[i]);
+        float c2 = fmaf(aS1[i], fac[i], aM1[i]);
+        a += dpp_f<kDppRowRor4>(a);
+        a += dpp_f<kDppRowRor8>(a);
+        a += __shfl_xor(a, 16, 64);
+        a += __shfl_xor(a, 32, 64);
+        c2 += dpp_f<kDppRowRor4>(c2);
+        c2 += dpp_f<kDppRowRor8>(c2);
+        c2 += __shfl_xor(c2, 16, 64);
+        c2 += __shfl_xor(c2, 32, 64);
+        t0[i] = a;
+        t1[i] = c2;
+        aS0[i] = aM0[i] = aS1[i] = aM1[i] = 0.f;
+      }
+      if (b == 0) {
+        int n0, n1;
+        rows_of(pw, j, n0, n1);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (i < nr) {
             if constexpr (MODE == 0) {
-              const int route = ws_route(p.perm[base + r0 + r], R);
-              if (na < N) p.h[(size_t)route * N + na] = act_f<ACT>(d0) * d1;
+              const int route = ws_route(p.perm[base + r0 + i], R);
+              if (n0 < N) p.h[(size_t)route * N + n0] = act_f<ACT>(t0[i]) * t1[i];
             } else {  // rows of y in the expert-grouped order (position, not route id)
-              const size_t pos = (size_t)(base + r0 + r);
-              if (na < N) p.y[pos * N + na] = d0;
-              if (nb < N) p.y[pos * N + nb] = d1;
+              const size_t pos = (size_t)(base + r0 + i);
+              if (n0 < N) p.y[pos * N + n0] = t0[i];
+              if (n1 < N) p.y[pos * N + n1] = t1[i];
             }
           }
         }
       }
-#pragma unroll
-      for (int u = 0; u < U; ++u) { va[u] = nva[u]; sa[u] = nsa[u]; vb[u] = nvb[u]; sb[u] = nsb[u]; }
     }
+#pragma unroll
+    for (int uu = 0; uu < UG; ++uu) { va[uu] = nva[uu]; sa[uu] = nsa[uu]; vb[uu] = nvb[uu]; sb[uu] = nsb[uu]; }
+    sv = nsv;
   }
 }
 

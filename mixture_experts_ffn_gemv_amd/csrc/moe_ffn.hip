@@ -64,6 +64,12 @@ struct Plan {
   // workspace offsets
   size_t o_sync, o_xn, o_logits, o_ids, o_wts, o_sgate, o_bhist, o_boff, o_counts, o_offsets, o_active,
       o_nactive, o_ntiles, o_perm, o_pos, o_rowtok, o_tgroup, o_tm0, o_h, o_hs, o_y, o_ys, o_slots;
+  // 4-bit path: staged activation rows (tokens, routes), their group sums and
+  // factors, and the expert work list
+  size_t o_u4xs = 0, o_u4xsum = 0, o_u4xfac = 0, o_u4hs = 0, o_u4hsum = 0, o_u4hfac = 0,
+      o_u4q = 0, o_u4qn = 0;
+  int u4slots = 0;         // routes per work-list entry (0: the shapes do not fit)
+  int u4qmax = 0;          // work-list entries (upper bound)
   size_t total = 0;
 };
 
@@ -183,6 +189,26 @@ Plan make_plan(const moe_desc* d, int64_t T) {
   p.o_y = take((size_t)p.R * p.H * es);
   p.o_ys = take((size_t)(p.shared ? T : 0) * p.H * es);
   p.o_slots = take((size_t)kSlotTab * 16);
+  if (d->weight_format == MOE_WEIGHTS_U4_G32) {
+    const int GH = p.H / 32, GI = p.I / 32;
+    // up to 4 routes a workgroup, as many as the larger row leaves LDS for
+    for (int ns = 4; ns >= 1; --ns)
+      if (u4_lds_bytes(p.H, kU4UGGateUp, ns) <= kU4LdsMax && u4_lds_bytes(p.I, kU4UGDown, ns) <= kU4LdsMax) {
+        p.u4slots = ns;
+        break;
+      }
+    const int ns = std::max(p.u4slots, 1);
+    p.o_u4xs = take((size_t)T * GH * 128);
+    p.o_u4xsum = take((size_t)T * GH * 4);
+    p.o_u4xfac = take((size_t)T * 4);
+    p.o_u4hs = take((size_t)p.R * GI * 128);
+    p.o_u4hsum = take((size_t)p.R * GI * 4);
+    p.o_u4hfac = take((size_t)p.R * 4);
+    // sum over touched experts of ceil(count / ns) <= (R + (ns - 1) min(E, R)) / ns
+    p.u4qmax = (int)((p.R + (ns - 1) * std::min<int64_t>(p.E, p.R) + ns - 1) / ns);
+    p.o_u4q = take((size_t)p.u4qmax * 4);
+    p.o_u4qn = take(4);
+  }
   p.total = o;
   return p;
 }
@@ -523,10 +549,6 @@ void launch_dn3(bool one, int u, dim3 grid, hipStream_t s, const Dec2Params& dp)
   else launch_dn3_u<WF, false>(u, grid, s, dp);
 }
 
-// Lanes per row of the 4-bit kernels for rows of G groups: the whole wave,
-// or 16 when G is a multiple of 16 but not of 64 (at most 8 groups a lane).
-int u4_lpr(int G) { return (G % 64 != 0 && G % 16 == 0 && G <= 16 * 8) ? 16 : 64; }
-
 // Raises a kernel's dynamic-LDS limit to the full 160 KB, once per device
 // and kernel (launches then need no attribute call).
 std::mutex g_lds_mu;
@@ -546,57 +568,77 @@ moe_status allow_full_lds(const void* kern, const char* name) {
   return MOE_OK;
 }
 
-template <int MODE, int ACT>
-moe_status launch_u4(const char* name, int G, dim3 grid, size_t lds, hipStream_t s,
-                     const Dec2Params& dp) {
+// One expert kernel of the 4-bit path: the vector-scale form when the row's
+// group count allows it.
+template <int MODE, int ACT, int UG, int PW>
+moe_status launch_u4_experts(const char* name, int qmax, hipStream_t s, const U4Experts& ep) {
+  const int K = MODE == 0 ? ep.d.H : ep.d.I, N = MODE == 0 ? ep.d.I : ep.d.H;
+  const int rows = kU4Waves * PW * (MODE == 0 ? 4 : 8);
+  const dim3 grid(qmax, (N + rows - 1) / rows);
+  const size_t lds = (size_t)u4_lds_bytes(K, UG, ep.nslot);
   auto go = [&](auto kern) -> moe_status {
     MOE_TRY(allow_full_lds(reinterpret_cast<const void*>(kern), name));
-    return launch(name, s, [&] { kern<<<grid, 256, lds, s>>>(dp); });
+    return launch(name, s, [&] { kern<<<grid, kU4Threads, lds, s>>>(ep); });
   };
-  const int lpr = u4_lpr(G);
-  const int u = pick_u(G * 64 / lpr);  // groups per lane, as if the row had 64/lpr times G
-  auto by_u = [&](auto lpr_c) -> moe_status {
-    constexpr int L = decltype(lpr_c)::value;
-    switch (u) {
-      case 1: return go(k_dec_u4<MODE, ACT, 1, L>);
-      case 2: return go(k_dec_u4<MODE, ACT, 2, L>);
-      case 3: return go(k_dec_u4<MODE, ACT, 3, L>);
-      case 4: return go(k_dec_u4<MODE, ACT, 4, L>);
-      case 6: return go(k_dec_u4<MODE, ACT, 6, L>);
-      default: return go(k_dec_u4<MODE, ACT, 8, L>);
-    }
-  };
-  return lpr == 16 ? by_u(std::integral_constant<int, 16>{})
-                   : by_u(std::integral_constant<int, 64>{});
+  if ((K / 32) % (4 * UG) == 0) return go(k_u4_mfma<MODE, ACT, UG, PW, true>);
+  return go(k_u4_mfma<MODE, ACT, UG, PW, false>);
 }
 
-// 4-bit weights, T <= 32: gate/up and down with the routes' activations
-// staged in LDS, then the weighted combine.
+// 4-bit weights: the tokens' rows staged (with the expert work list), gate/up
+// on the MFMA, the routes' h rows staged, down, then the weighted combine.
 moe_status run_experts_u4(const moe_desc* d, const Plan& p, Dec2Params dp, float* out,
-                          const float* residual, void* ws,
-                          hipStream_t s) {
+                          const float* residual, void* ws, hipStream_t s) {
+  if (p.u4slots < 1)
+    return fail(MOE_UNSUPPORTED, "hidden %d / intermediate %d: the 4-bit path stages one route "
+                "row in at most %d bytes of LDS", p.H, p.I, kU4LdsMax);
   dp.y = wsp<float>(ws, p.o_y);
-  auto rc_for = [&](int K) {
-    return (int)std::max<int64_t>(1, std::min<int64_t>({(int64_t)kU4Routes, p.T,
-                                                         (int64_t)(kU4LdsMax / u4_route_bytes(K))}));
-  };
-  {
-    Dec2Params g = dp;
-    g.rc = rc_for(p.H);
-    const size_t lds = (size_t)g.rc * u4_route_bytes(p.H);
-    const int G = p.H / 32, rows = kU4Rows * (64 / u4_lpr(G));
-    dim3 grid(p.max_groups, (p.I + rows - 1) / rows);
-    if (d->activation == MOE_ACT_SILU) MOE_TRY((launch_u4<0, ACT_SILU>("gemv_gateup", G, grid, lds, s, g)));
-    else MOE_TRY((launch_u4<0, ACT_GELU_TANH>("gemv_gateup", G, grid, lds, s, g)));
-  }
-  {
-    Dec2Params g = dp;
-    g.rc = rc_for(p.I);
-    const size_t lds = (size_t)g.rc * u4_route_bytes(p.I);
-    const int G = p.I / 32, rows = kU4Rows * (64 / u4_lpr(G));
-    dim3 grid(p.max_groups, (p.H + rows - 1) / rows);
-    MOE_TRY((launch_u4<1, 0>("gemv_down", G, grid, lds, s, g)));
-  }
+  U4Stage sx{};
+  sx.src = dp.x;
+  sx.src_bf16 = dp.x_bf16;
+  sx.K = p.H;
+  sx.rows = (int)p.T;
+  sx.stage = wsp<uint8_t>(ws, p.o_u4xs);
+  sx.gsum = wsp<float>(ws, p.o_u4xsum);
+  sx.fac = wsp<float>(ws, p.o_u4xfac);
+  sx.counts = dp.counts;
+  sx.active = dp.active;
+  sx.n_active = dp.n_active;
+  sx.qlist = wsp<int32_t>(ws, p.o_u4q);
+  sx.qn = wsp<int32_t>(ws, p.o_u4qn);
+  sx.E = p.E;
+  sx.qmax = p.u4qmax;
+  sx.nslot = p.u4slots;
+  MOE_TRY(launch("stage_x", s, [&] {
+    k_u4_stage<<<(unsigned)p.T + 1, kU4StageThreads, 0, s>>>(sx);
+  }));
+  U4Experts ep{};
+  ep.d = dp;
+  ep.stage = sx.stage;
+  ep.gsum = sx.gsum;
+  ep.fac = sx.fac;
+  ep.qlist = sx.qlist;
+  ep.qn = sx.qn;
+  ep.nslot = p.u4slots;
+  if (d->activation == MOE_ACT_SILU)
+    MOE_TRY((launch_u4_experts<0, ACT_SILU, kU4UGGateUp, kU4PWGateUp>("gemv_gateup", p.u4qmax, s, ep)));
+  else
+    MOE_TRY((launch_u4_experts<0, ACT_GELU_TANH, kU4UGGateUp, kU4PWGateUp>("gemv_gateup", p.u4qmax, s, ep)));
+
+  U4Stage sh{};
+  sh.src = dp.h;
+  sh.K = p.I;
+  sh.rows = (int)p.R;
+  sh.stage = wsp<uint8_t>(ws, p.o_u4hs);
+  sh.gsum = wsp<float>(ws, p.o_u4hsum);
+  sh.fac = wsp<float>(ws, p.o_u4hfac);
+  MOE_TRY(launch("stage_h", s, [&] {
+    k_u4_stage<<<(unsigned)p.R, kU4StageThreads, 0, s>>>(sh);
+  }));
+  U4Experts ed = ep;
+  ed.stage = sh.stage;
+  ed.gsum = sh.gsum;
+  ed.fac = sh.fac;
+  MOE_TRY((launch_u4_experts<1, 0, kU4UGDown, kU4PWDown>("gemv_down", p.u4qmax, s, ed)));
   const size_t nthr = (size_t)p.T * (p.H / 4);
   return launch("combine", s, [&] {
     k_combine<float><<<(unsigned)((nthr + 255) / 256), 256, 0, s>>>(
