@@ -588,9 +588,6 @@ moe_status launch_u4_experts(const char* name, int qmax, hipStream_t s, const U4
 // on the MFMA, the routes' h rows staged, down, then the weighted combine.
 moe_status run_experts_u4(const moe_desc* d, const Plan& p, Dec2Params dp, float* out,
                           const float* residual, void* ws, hipStream_t s) {
-  if (p.u4slots < 1)
-    return fail(MOE_UNSUPPORTED, "hidden %d / intermediate %d: the 4-bit path stages one route "
-                "row in at most %d bytes of LDS", p.H, p.I, kU4LdsMax);
   dp.y = wsp<float>(ws, p.o_y);
   U4Stage sx{};
   sx.src = dp.x;
@@ -868,6 +865,10 @@ moe_status check_common(const moe_desc* d, int64_t T, const void* x, const moe_w
           return fail(MOE_INVALID_ARGUMENT, "a 4-bit weight pointer is NULL");
         if (!aligned16(m->codes)) return fail(MOE_UNSUPPORTED, "4-bit codes must be 16-byte aligned");
       }
+      if (plan->u4slots < 1)
+        return fail(MOE_UNSUPPORTED, "hidden %d / intermediate %d: a 4-bit workgroup stages one "
+                    "activation row in at most %d bytes of LDS", d->hidden, d->intermediate,
+                    kU4LdsMax);
     } else {
       if (!w->gate || !w->up || !w->down)
         return fail(MOE_INVALID_ARGUMENT, "gate/up/down weight pointer is NULL");

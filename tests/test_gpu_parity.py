@@ -106,6 +106,10 @@ SMALL = [
               seed_index=34),
     MoeConfig(name="gemv_u4_many_routes", T=70, H=128, I=64, E=4, k=2, weight_format=WF_U4,
               seed_index=19),
+    # rows long enough that only 3 routes fit a workgroup's LDS (3 per
+    # work-list entry), and a group count (3) below one MFMA block row
+    MoeConfig(name="gemv_u4_three_slots", T=6, H=9216, I=96, E=4, k=2, weight_format=WF_U4,
+              seed_index=503),
     # one token, bf16 weights (gate/up activations straight from x), shared expert
     MoeConfig(name="gemv_bf16_shared_t1", T=1, H=1024, I=320, E=16, k=4, weight_format=WF_BF16,
               router_dtype=DT_BF16, shared=True, Is=192, seed_index=35),
@@ -285,6 +289,21 @@ def test_repeat_runs_bit_identical():
         assert (u == v).all()
     case2 = Case(CONFIGS["decode_geglu_t1"])
     assert (case2.forward()[0] == case2.forward()[0]).all()
+
+
+def test_u4_rows_beyond_lds_are_unsupported_and_enqueue_nothing():
+    # an intermediate row of 34816 4-bit values does not fit one
+    # workgroup's LDS as a staged row: the call is refused before any launch
+    import mixture_experts_ffn_gemv_amd as M
+    cfg = MoeConfig(name="u4_too_long", T=2, H=256, I=34816, E=2, k=1, weight_format=WF_U4,
+                    seed_index=504)
+    case = Case(cfg)
+    out = torch.full((cfg.T, cfg.H), 7.0, device="cuda")
+    with pytest.raises(M.MoeError) as ei:
+        M.moe_ffn_forward(case.desc, case.dev.x, case.weights, out=out)
+    assert ei.value.status == M.MOE_UNSUPPORTED and "LDS" in str(ei.value)
+    torch.cuda.synchronize()
+    assert (out == 7.0).all()
 
 
 def test_error_path_enqueues_nothing():
