@@ -92,30 +92,43 @@ __device__ __forceinline__ void grouped_tile(int L, int ntt, int nnt, int& tt, i
 }
 
 // Prefill router: logits[t, c] = x[t, :] . Wr[c, :] (+ bias[c] for c < E),
-// column E (with a shared expert) the shared gate vector.  Each workgroup
-// computes a 128-column x 128-token tile over K in steps of 64 with
+// column E (with a shared expert) the shared gate vector.  K is split into
+// nsplit equal ranges (grid z): range z writes its partial dot products to
+// logits + z * split_stride (the bias goes with range 0), and the top-k
+// kernel adds the ranges in order, so more workgroups share a short K loop
+// and the sum stays deterministic.  Each workgroup
+// computes a 128-column x 128-token tile over its K range in steps of 64 with
 // v_mfma_f32_32x32x16_bf16; each wave a 64 x 64 sub-tile (2 x 2 blocks of
 // 32x32).  Operand tiles are staged through LDS (double-buffered, the
 // 16-byte chunks of each 128-byte row XOR-swizzled, see swz) from registers
-// loaded one K-step ahead.
+// loaded one K-step ahead; the finished logits leave through LDS as whole
+// rows.
 struct RouterParams {
   const uint16_t* x;       // [T, H]
   const uint16_t* wr;      // [E, H]
   const uint16_t* wsg;     // [H] shared gate vector (column E), or null
   const float* bias;       // [E] or null
-  float* logits;           // [T, ncols]
+  float* logits;           // [nsplit, T, ncols] partial logits
   int T, H, E, ncols;
+  int nsplit;              // K ranges (H / 64 a multiple of it)
+  size_t split_stride;     // floats between the ranges' partial logits
 };
 
+constexpr int kRouterEpStride = kTileW + 4;  // floats per staged logit row
 __global__ __launch_bounds__(256) void k_router_mfma(RouterParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][kTileW * kTileK];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[2][kTileT * kTileK];
+  // the operand tiles, then (after the K loop) half a tile of logits
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * (kTileW + kTileT) * kTileK * 2];
+  static_assert((kTileT / 2) * kRouterEpStride * 4 <= sizeof(smem), "staged logits fit");
+  auto sA = reinterpret_cast<uint16_t (*)[kTileW * kTileK]>(smem);
+  auto sB = reinterpret_cast<uint16_t (*)[kTileT * kTileK]>(smem + 2 * kTileW * kTileK * 2);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int m0 = blockIdx.x * kTileT, n0 = blockIdx.y * kTileW;
   if (m0 >= p.T) return;
   const int K = p.H;
+  const int nk = K / kTileK / p.nsplit;       // K steps of this range
+  const int k0 = blockIdx.z * nk * kTileK;   // its first element
 
   // ---- per-thread global load assignments (4 chunks of A, 4 of B) ----------
   // Rows past the end are clamped to the last valid one (never stored), so
@@ -129,9 +142,9 @@ __global__ __launch_bounds__(256) void k_router_mfma(RouterParams p) {
     const int row = q >> 3, ck = q & 7;
     lds_off[i] = swz(row, ck);
     const int e = min(n0 + row, p.ncols - 1);
-    a_src[i] = ((e < p.E) ? p.wr + (size_t)e * K : p.wsg) + ck * 8;
+    a_src[i] = ((e < p.E) ? p.wr + (size_t)e * K : p.wsg) + k0 + ck * 8;
     const int m = min(m0 + row, p.T - 1);
-    b_src[i] = p.x + (size_t)m * K + ck * 8;
+    b_src[i] = p.x + (size_t)m * K + k0 + ck * 8;
   }
 
   u32x4 ra[4], rb[4];
@@ -167,7 +180,6 @@ __global__ __launch_bounds__(256) void k_router_mfma(RouterParams p) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  const int nk = K / kTileK;
   gload(0);
   lstore(0);
   __syncthreads();
@@ -194,22 +206,35 @@ __global__ __launch_bounds__(256) void k_router_mfma(RouterParams p) {
   }
 
   // ---- epilogue: acc[i][j][4q + v] = column arow[i] + 8q + 4*(lane>>5) + v,
-  //      token brow[j] + (lane & 31) --------------------------------------------
+  //      token brow[j] + (lane & 31).  Each half of the token rows goes
+  //      through LDS (waves 2wt, 2wt+1 hold half wt) and out as whole rows,
+  //      consecutive lanes on consecutive columns.
   const int rsub = 4 * (lane >> 5);
+  float* ep = reinterpret_cast<float*>(smem);
+  const bool add_bias = blockIdx.z == 0 && p.bias;
+  float* outz = p.logits + blockIdx.z * p.split_stride;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int m = m0 + brow[j] + (lane & 31);
-    if (m >= p.T) continue;
-    float* outp = p.logits + (size_t)m * p.ncols;
+  for (int h = 0; h < 2; ++h) {
+    if (wt == h) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int e = n0 + arow[i] + 8 * q + rsub + v;
-          if (e < p.ncols) outp[e] = acc[i][j][4 * q + v] + ((e < p.E && p.bias) ? p.bias[e] : 0.f);
-        }
+          for (int q = 0; q < 4; ++q) {
+            const int r = 32 * j + (lane & 31), c = arow[i] + 8 * q + rsub;
+            *reinterpret_cast<f32x4*>(&ep[r * kRouterEpStride + c]) =
+                f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+          }
+    }
+    __syncthreads();
+    for (int idx = tid; idx < (kTileT / 2) * kTileW; idx += 256) {
+      const int r = idx / kTileW, c = idx - r * kTileW;
+      const int m = m0 + (kTileT / 2) * h + r, e = n0 + c;
+      if (m < p.T && e < p.ncols)
+        outz[(size_t)m * p.ncols + e] = ep[r * kRouterEpStride + c] + ((e < p.E && add_bias) ? p.bias[e] : 0.f);
+    }
+    __syncthreads();
   }
 }
 

@@ -61,6 +61,7 @@ struct Plan {
   int max_tiles = 0;       // grouped-GEMM route tiles (upper bound)
   int bt = 128;            // grouped-GEMM route-tile height
   int max_groups = 0;      // active groups (upper bound)
+  int rsplit = 1;          // prefill router: K ranges (partial logits added by the top-k)
   // workspace offsets
   size_t o_sync, o_xn, o_logits, o_ids, o_wts, o_sgate, o_bhist, o_boff, o_counts, o_offsets, o_active,
       o_nactive, o_ntiles, o_perm, o_pos, o_rowtok, o_tgroup, o_tm0, o_h, o_hs, o_y, o_ys, o_slots;
@@ -168,7 +169,16 @@ Plan make_plan(const moe_desc* d, int64_t T) {
   auto take = [&](size_t bytes) { size_t r = o; o = align_up(o + bytes); return r; };
   p.o_sync = take(kSyncBytes);  // ticket counter(s), kept at zero between calls
   p.o_xn = take(d->pre_norm ? (size_t)T * p.H * (d->act_dtype == MOE_BF16 ? 2 : 4) : 0);
-  p.o_logits = take((size_t)T * p.ncols * 4);
+  if (p.mfma) {
+    // fewer router tiles than compute units: split K until there are about
+    // as many workgroups (each range keeps at least 8 K steps); more tiles
+    // gain nothing from it and would only give the top-k more partial rows
+    const int64_t tiles = ((T + kTileT - 1) / kTileT) * ((p.ncols + kTileW - 1) / kTileW);
+    const int nk = p.H / kTileK;
+    while (tiles * p.rsplit < 256 && nk % (2 * p.rsplit) == 0 && nk / (2 * p.rsplit) >= 8)
+      p.rsplit *= 2;
+  }
+  p.o_logits = take((size_t)p.rsplit * T * p.ncols * 4);
   p.o_ids = take((size_t)p.R * 4);
   p.o_wts = take((size_t)p.R * 4);
   p.o_sgate = take((size_t)T * 4);
@@ -292,8 +302,8 @@ moe_status run_router(const moe_desc* d, const Plan& p, const void* x, const moe
   if (p.mfma) {
     RouterParams rp{static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w->router),
                     static_cast<const uint16_t*>(w->shared_gate_inp), w->router_bias, logits,
-                    T, p.H, p.E, p.ncols};
-    dim3 grid((T + kTileT - 1) / kTileT, (p.ncols + kTileW - 1) / kTileW);
+                    T, p.H, p.E, p.ncols, p.rsplit, (size_t)T * p.ncols};
+    dim3 grid((T + kTileT - 1) / kTileT, (p.ncols + kTileW - 1) / kTileW, p.rsplit);
     return launch("router_mfma", s, [&] { k_router_mfma<<<grid, 256, 0, s>>>(rp); });
   }
   const bool xb = d->act_dtype == MOE_BF16, rb = d->router_dtype == MOE_BF16;
@@ -357,7 +367,8 @@ moe_status run_route_and_group(const moe_desc* d, const Plan& p, const moe_weigh
                                int32_t* user_perm, hipStream_t s) {
   const int T = (int)p.T, R = (int)p.R;
   MOE_TRY(launch("topk", s, [&] {
-    k_topk<<<(T + 3) / 4, 256, 0, s>>>(wsp<float>(ws, p.o_logits), T, p.E, p.k, p.ncols,
+    k_topk<<<(T + 3) / 4, 256, 0, s>>>(wsp<float>(ws, p.o_logits), p.rsplit, (size_t)T * p.ncols,
+                                       T, p.E, p.k, p.ncols,
                                        route_mode(d, w), p.shared ? 1 : 0,
                                        wsp<int32_t>(ws, p.o_ids), wsp<float>(ws, p.o_wts),
                                        user_ids, user_w, wsp<float>(ws, p.o_sgate));

@@ -223,7 +223,15 @@ __device__ __forceinline__ float expert_scale_of(const RouteMode& rm, int e) {
 // One token's routing in one wave: l points at the token's logits (global
 // or LDS), column E holding the shared expert's gate logit when there is
 // one.  Lane j < k writes top-k position j.
-__device__ __forceinline__ void topk_token(const float* l, int t, int E, int k, RouteMode rm,
+// l: the token's logits row, or the first of nsplit partial rows sstride
+// floats apart (added in order).
+__device__ __forceinline__ float split_sum(const float* l, int e, int nsplit, size_t sstride) {
+  float v = l[e];
+  for (int z = 1; z < nsplit; ++z) v += l[z * sstride + e];
+  return v;
+}
+__device__ __forceinline__ void topk_token(const float* l, int nsplit, size_t sstride, int t, int E,
+                                           int k, RouteMode rm,
                                            int has_shared, int32_t* __restrict__ ids,
                                            float* __restrict__ wts, int32_t* __restrict__ user_ids,
                                            float* __restrict__ user_w, float* __restrict__ sgate) {
@@ -233,7 +241,7 @@ __device__ __forceinline__ void topk_token(const float* l, int t, int E, int k, 
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int e = lane + 64 * q;
-    v[q] = (e < E) ? l[e] : -INFINITY;
+    v[q] = (e < E) ? split_sum(l, e, nsplit, sstride) : -INFINITY;
     if (e >= E) taken |= 1u << q;
   }
   int my_id = 0;
@@ -272,17 +280,18 @@ __device__ __forceinline__ void topk_token(const float* l, int t, int E, int k, 
     if (user_ids) user_ids[(size_t)t * k + lane] = my_id;
     if (user_w) user_w[(size_t)t * k + lane] = w;
   }
-  if (has_shared && lane == 0) sgate[t] = sigmoid_f(l[E]);
+  if (has_shared && lane == 0) sgate[t] = sigmoid_f(split_sum(l, E, nsplit, sstride));
 }
 
 __global__ __launch_bounds__(256) void k_topk(
-    const float* __restrict__ logits, int T, int E, int k, int ncols,
+    const float* __restrict__ logits, int nsplit, size_t sstride, int T, int E, int k, int ncols,
     RouteMode rm, int has_shared, int32_t* __restrict__ ids,
     float* __restrict__ wts, int32_t* __restrict__ user_ids,
     float* __restrict__ user_w, float* __restrict__ sgate) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  topk_token(logits + (size_t)t * ncols, t, E, k, rm, has_shared, ids, wts, user_ids, user_w,
+  topk_token(logits + (size_t)t * ncols, nsplit, sstride, t, E, k, rm, has_shared, ids, wts,
+             user_ids, user_w,
              sgate);
 }
 

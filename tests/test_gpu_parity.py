@@ -90,6 +90,10 @@ SMALL = [
               act_dtype=DT_BF16, router_dtype=DT_BF16, shared=True, Is=64, seed_index=502),
     MoeConfig(name="mfma_dense_e1", T=40, H=128, I=64, E=1, k=1, weight_format=WF_BF16,
               act_dtype=DT_BF16, router_dtype=DT_BF16, seed_index=15),
+    # rows long enough that the router splits K in two ranges (partial
+    # logits added by the top-k), shared gate column included
+    MoeConfig(name="mfma_router_split", T=300, H=1024, I=64, E=16, k=4, weight_format=WF_BF16,
+              act_dtype=DT_BF16, router_dtype=DT_BF16, shared=True, Is=64, seed_index=505),
     # GEMV path
     MoeConfig(name="gemv_bf16x_shared", T=8, H=256, I=128, E=16, k=4, weight_format=WF_BF16,
               act_dtype=DT_BF16, router_dtype=DT_BF16, shared=True, Is=64, seed_index=16),
