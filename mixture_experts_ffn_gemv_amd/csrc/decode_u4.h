@@ -398,18 +398,22 @@ void k_u4_mfma(U4Experts ep) {
         scm0 = sa[uu];
         scm1 = sb[uu];
       }
+      // groups past the row's end contribute zero (scale and min +0); the
+      // f16 values enter the FMAs directly (mixed-precision FMA)
       const bool ok = c < G;
-      const float s0 = ok ? f16_to_f32((uint16_t)scm0) : 0.f;
-      const float m0 = ok ? f16_to_f32((uint16_t)(scm0 >> 16)) : 0.f;
-      const float s1 = ok ? f16_to_f32((uint16_t)scm1) : 0.f;
-      const float m1 = ok ? f16_to_f32((uint16_t)(scm1 >> 16)) : 0.f;
+      scm0 = ok ? scm0 : 0u;
+      scm1 = ok ? scm1 : 0u;
+      const _Float16 s0 = __builtin_bit_cast(_Float16, (uint16_t)scm0);
+      const _Float16 m0 = __builtin_bit_cast(_Float16, (uint16_t)(scm0 >> 16));
+      const _Float16 s1 = __builtin_bit_cast(_Float16, (uint16_t)scm1);
+      const _Float16 m1 = __builtin_bit_cast(_Float16, (uint16_t)(scm1 >> 16));
       const f32x4 xsm = xsum4[cc];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        aS0[i] = fmaf(s0, d0[i], aS0[i]);
-        aM0[i] = fmaf(m0, xsm[i], aM0[i]);
-        aS1[i] = fmaf(s1, d1[i], aS1[i]);
-        aM1[i] = fmaf(m1, xsm[i], aM1[i]);
+        aS0[i] = fmaf((float)s0, d0[i], aS0[i]);
+        aM0[i] = fmaf((float)m0, xsm[i], aM0[i]);
+        aS1[i] = fmaf((float)s1, d1[i], aS1[i]);
+        aM1[i] = fmaf((float)m1, xsm[i], aM1[i]);
       }
     }
     if (ch == NCH - 1) {
