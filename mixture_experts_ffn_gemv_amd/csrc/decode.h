@@ -4,9 +4,10 @@
 //   otherwise:                   k_router_route -> k_dec_gateup3        -> k_dec_down3
 //
 // k_router_gemv   router logits only (one workgroup per router row).
-// k_router_route  router logits (one workgroup per router row); the last
-//                 workgroup to finish then does softmax/top-k/renormalise
-//                 for every token and the stable expert grouping (counts,
+// k_router_route  router logits (workgroup = 4 logit columns x one K
+//                 slice, every token); the last workgroup to finish then
+//                 does softmax/top-k/renormalise for every token (one wave
+//                 per token) and the stable expert grouping (counts,
 //                 offsets, list of touched experts, routes grouped by
 //                 expert).
 // k_dec_gateup3   work item = (touched expert, block of 4 features).  Each
@@ -37,7 +38,6 @@
 namespace moe {
 
 constexpr int kSmallMaxTokens = 32;
-constexpr int kSmallRoutes = kSmallMaxTokens * MOE_MAX_TOP_K_DEV;
 
 struct SmallRouteOut {
   int32_t* ids;          // [R]
@@ -64,57 +64,6 @@ struct SmallRouteOut {
 // weight its sigmoid gate).  The down kernel reads it with one load a lane.
 constexpr int kSlotTab = MOE_MAX_TOP_K_DEV + 2;
 
-// Exclusive prefix sums of two per-thread values over the 256 threads of a
-// workgroup (thread order), and their totals.
-__device__ __forceinline__ void block_scan2(int a, int b, int& ea, int& eb, int& ta, int& tb) {
-  __shared__ int s_part[2][4];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int ia = a, ib = b;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int u = __shfl_up(ia, d, 64);
-    const int v = __shfl_up(ib, d, 64);
-    if (lane >= d) { ia += u; ib += v; }
-  }
-  if (lane == 63) { s_part[0][wave] = ia; s_part[1][wave] = ib; }
-  __syncthreads();
-  ta = 0; tb = 0;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    if (w < wave) { ia += s_part[0][w]; ib += s_part[1][w]; }
-    ta += s_part[0][w];
-    tb += s_part[1][w];
-  }
-  ea = ia - a;
-  eb = ib - b;
-  __syncthreads();
-}
-
-// ---------------------------------------------------------------------------
-// Routing of T <= 32 tokens by one workgroup.  The logits of every token go
-// to LDS, the k experts of each token are selected by one of two methods,
-// the softmax denominators are summed by a 16-lane row per token, the
-// weights formed one thread per route, and the grouping is one thread per
-// expert: its routes, in token order, are its stable block.
-//
-// Rank selection (few pairs): pair (t, e) gets the key (order-preserving
-// bits of l[t,e], ~e).  Keys of one token are distinct and order "larger
-// logit first, lower expert index among equal logits", the tie rule of the
-// stable descending sort.  A pair's rank is the number of larger keys of its
-// token; ranks below k are the slots.  All pairs are ranked at once, E
-// comparisons each, where a wave-wide arg-max needs k dependent rounds.
-//
-// Row selection (more pairs): a 16-lane row per token, four tokens per
-// wave; k rounds of a row maximum over the same keys, built from DPP row
-// operations, which need no cross-row readlane.
-// ---------------------------------------------------------------------------
-constexpr int kRankMaxPairs = 1024;
-
-__device__ __forceinline__ bool rank_route_ok(int T, int E) {
-  const int pairs = T * E;
-  return pairs <= kRankMaxPairs && ((pairs + 255) / 256) * E <= 256;
-}
-
 // Order-preserving 32-bit image of a logit (-0 and +0 tie) and its inverse.
 __device__ __forceinline__ uint32_t route_ord(float l) {
   const uint32_t u = __float_as_uint(l == 0.0f ? 0.0f : l);
@@ -123,61 +72,6 @@ __device__ __forceinline__ uint32_t route_ord(float l) {
 __device__ __forceinline__ float ord_logit(uint32_t ord) {
   return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord);
 }
-// Rank key of (logit, expert): larger logit first, then the lower expert.
-__device__ __forceinline__ uint64_t route_key(float l, int e) {
-  return ((uint64_t)route_ord(l) << 32) | (uint32_t)~(uint32_t)e;
-}
-
-typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
-
-template <int CTRL>
-__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xF, 0xF, true);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xF,
-                                                            0xF, true);
-  return ((uint64_t)hi << 32) | lo;
-}
-__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
-
-// k rounds of a 16-lane maximum over the rank keys per token; lane l of a
-// row holds the keys of experts l, l+16, ... (CPL of them, E <= 16*CPL), and
-// the lane holding a round's winner clears it.
-template <int CPL>
-__device__ __forceinline__ void row_select(const float* __restrict__ s_l, int T, int E, int k,
-                                           int8_t* __restrict__ s_sel, int* __restrict__ s_rid) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int l16 = lane & 15;
-  for (int t0 = wave * 4; t0 < T; t0 += 16) {
-    const int t = t0 + (lane >> 4);
-    const bool tok = t < T;
-    uint64_t key[CPL];
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      const int e = l16 + 16 * c;
-      key[c] = (tok && e < E) ? route_key(s_l[t * E + e], e) : 0;
-    }
-    for (int j = 0; j < k; ++j) {
-      uint64_t m[CPL];  // pairwise tree: independent compares can overlap
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) m[c] = key[c];
-#pragma unroll
-      for (int w = CPL / 2; w >= 1; w /= 2)
-#pragma unroll
-        for (int c = 0; c < w; ++c) m[c] = max_u64(m[c], m[c + w]);
-      uint64_t b = m[0];
-      b = max_u64(b, dpp_u64<kDppXor1>(b));
-      b = max_u64(b, dpp_u64<kDppXor2>(b));
-      b = max_u64(b, dpp_u64<kDppHalfMirror>(b));
-      b = max_u64(b, dpp_u64<kDppMirror>(b));
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) key[c] = key[c] == b ? 0 : key[c];
-      const int e = (int)~(uint32_t)b;
-      if (tok && (e & 15) == l16) s_sel[t * E + e] = (int8_t)j;
-      if (tok && l16 == 0) s_rid[t * k + j] = e;
-    }
-  }
-}
-
 constexpr int kDppRowBcast15 = 0x142;  // lane 15 of each row to the next row
 constexpr int kDppRowBcast31 = 0x143;  // lane 31 to rows 2 and 3
 
@@ -193,15 +87,16 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
-// One token's routing in one wave (E <= 64*C): the selection order and
-// weights of route_small_impl at T = 1.  Lane l holds experts l, l+64, ...;
-// each of k rounds takes the wave maximum M of the order images, then the
-// lowest still-live expert whose image is M (ballots over the lanes, the
-// live set a wave-uniform bit mask, since taken and absent experts both read
-// as image 0), which is exactly the maximum of the rank keys.  Lane j < k
-// returns the expert and routing weight of top-k position j; `sel` returns
-// the selected experts as bit masks (expert 64c + b at bit b of sel[c]).
-// Every lane must take part.
+// One token's routing in one wave (E <= 64*C).  Lane l holds experts l,
+// l+64, ...; each of k rounds takes the wave maximum M of the order images,
+// then the lowest live expert whose image is M (one ballot per logit a lane;
+// taken and absent experts read as image 0 and are not live): the larger
+// logit first, the lower expert among equal logits, the order of a stable
+// descending sort.  The live flags stay in the lanes, so a round costs a few
+// scalar operations beyond the wave maximum.  Lane j < k returns the expert
+// and routing weight of top-k position j; `sel` returns the selected experts
+// as bit masks (expert 64c + b at bit b of sel[c]).  Every lane must take
+// part.
 static_assert(MOE_MAX_EXPERTS_DEV <= 4 * 64, "one-token ranking holds at most 4 logits a lane");
 template <int C>
 __device__ __forceinline__ void route_one_token(const float* __restrict__ l, int E, int k,
@@ -210,15 +105,14 @@ __device__ __forceinline__ void route_one_token(const float* __restrict__ l, int
   const int lane = threadIdx.x & 63;
   float lv[C];
   uint32_t ord[C];
-  uint64_t live[C];
+  bool live[C];
 #pragma unroll
   for (int c = 0; c < C; ++c) {
     const int e = lane + 64 * c;
     const bool ok = e < E;
     lv[c] = ok ? l[e] : 0.f;
     ord[c] = ok ? route_ord(lv[c]) : 0u;
-    live[c] = __ballot(ok);
-    sel[c] = 0;
+    live[c] = ok;
   }
   int my_e = 0;
   uint32_t my_ord = 0, top = 0;
@@ -228,22 +122,16 @@ __device__ __forceinline__ void route_one_token(const float* __restrict__ l, int
     for (int c = 1; c < C; ++c) m = max(m, ord[c]);
     const uint32_t M = wave_max_u32(m);
     int e = 0;
-    bool found = false;
 #pragma unroll
-    for (int c = 0; c < C; ++c) {
-      const uint64_t hit = __ballot(ord[c] == M) & live[c];
-      if (!found && hit != 0) {
-        e = 64 * c + __ffsll((unsigned long long)hit) - 1;
-        found = true;
-      }
+    for (int c = C - 1; c >= 0; --c) {
+      const uint64_t hit = __ballot(live[c] && ord[c] == M);
+      e = hit != 0 ? 64 * c + __ffsll((unsigned long long)hit) - 1 : e;
     }
-    const int ce = e >> 6, le = e & 63;
 #pragma unroll
     for (int c = 0; c < C; ++c) {
-      const uint64_t bit = c == ce ? 1ull << le : 0ull;  // selects, no branch
-      live[c] &= ~bit;
-      sel[c] |= bit;
-      ord[c] = (c == ce && lane == le) ? 0u : ord[c];
+      const bool taken = lane + 64 * c == e;
+      live[c] = live[c] && !taken;
+      ord[c] = taken ? 0u : ord[c];
     }
     if (j == 0) top = M;
     if (lane == j) {
@@ -251,6 +139,8 @@ __device__ __forceinline__ void route_one_token(const float* __restrict__ l, int
       my_ord = M;
     }
   }
+#pragma unroll
+  for (int c = 0; c < C; ++c) sel[c] = __ballot(!live[c] && lane + 64 * c < E);
   id = lane < k ? my_e : 0;
   const float li = ord_logit(my_ord);
   const float lmax = ord_logit(top);  // the top logit
@@ -271,224 +161,332 @@ __device__ __forceinline__ void route_one_token(const float* __restrict__ l, int
   w = ex / denom * rm.scale;
 }
 
-struct RouteLds {
+// ---------------------------------------------------------------------------
+// Router logits and routing of T <= 32 tokens in one launch.
+//
+// Logits: workgroup (cb, ks) computes logit columns 4cb .. 4cb+3 (column E,
+// with a shared expert, is its gate vector) of every token over K slice ks.
+// Its 16 waves are (group of 8 tokens) x (K part); lane l of a wave takes 4
+// K elements of each 256-element piece of the slice and accumulates the
+// 8 x 4 products of those elements, so each weight and activation element
+// is loaded once per wave.  A reduce-scatter over the wave leaves each
+// (token, column) sum in two lanes, the K parts are added through LDS in a
+// fixed order, and the slice's partial logits are stored at device scope.
+// The slices keep the grid near one workgroup per CU while a workgroup reads
+// four weight rows and only its slice of the activations.
+//
+// Routing: the workgroup that takes the last ticket adds the slices in order
+// (then the bias) into LDS, ranks each token with one wave
+// (route_one_token), and groups the routes by expert, one thread per expert:
+// its routes, in token order, are its stable block.
+// ---------------------------------------------------------------------------
+constexpr int kRouteThreads = 1024;
+constexpr int kRouteWaves = kRouteThreads / 64;
+constexpr int kRouteCols = 4;       // logit columns per workgroup
+constexpr int kRouteTokGroup = 8;   // tokens per wave
+constexpr int kRouteMaxSlices = 4;  // K slices at most
+static_assert(kRouteTokGroup * kRouteCols == 32, "one reduce-scatter of 32 sums per wave");
+static_assert(MOE_MAX_EXPERTS_DEV <= 4 * 64, "the grouping scan covers the first four waves");
+
+// token groups of a workgroup for T tokens (the wave count is a multiple)
+__host__ __device__ inline int route_tgroups(int T) { return T <= 8 ? 1 : T <= 16 ? 2 : 4; }
+
+// K slices: doubled while the grid stays within one workgroup per CU and
+// each wave of a slice keeps at least one 256-element piece.
+inline int route_slices(int T, int H, int ncols) {
+  const int ncb = (ncols + kRouteCols - 1) / kRouteCols;
+  const int nkw = kRouteWaves / route_tgroups(T);
+  const int pieces = (H / 4 + 63) / 64;
+  int n = 1;
+  while (n < kRouteMaxSlices && ncb * n * 2 <= 256 && pieces / (n * 2) >= nkw) n *= 2;
+  return n;
+}
+// floats from one slice's partial logits to the next (16-byte aligned)
+__host__ __device__ inline size_t route_slice_stride(int T, int ncols) {
+  return ((size_t)T * ncols + 3) & ~(size_t)3;
+}
+
+// four consecutive elements as floats: f32 (one 16-byte load) or bf16 (8 bytes)
+template <bool BF16>
+__device__ __forceinline__ void ld4f(const void* p, float (&v)[4]) {
+  if constexpr (BF16) {
+    const u32x2 u = *reinterpret_cast<const u32x2*>(p);
+    v[0] = bf16lo(u[0]); v[1] = bf16hi(u[0]); v[2] = bf16lo(u[1]); v[3] = bf16hi(u[1]);
+  } else {
+    const u32x4 u = ld16(p);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] = __uint_as_float(u[q]);
+  }
+}
+
+// Reduce-scatter of 32 values a lane over the wave: afterwards lanes 2q and
+// 2q+1 hold the sum over all 64 lanes of value q.  Each level pairs lanes
+// that differ in one bit (bit 5: lane ^ 32, bit 4: lane ^ 16, bit 3: mirror
+// within a 16-lane row, bit 2: mirror within 8 lanes, bit 1: lane ^ 2); a
+// lane keeps the half of its values picked by that bit and adds its
+// partner's copy of the same half.  The last level (lane ^ 1) adds the pair.
+__device__ __forceinline__ float wave_reduce_scatter32(float (&v)[32]) {
+  const int lane = threadIdx.x & 63;
+  {
+    const bool hi = (lane & 32) != 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float send = hi ? v[i] : v[i + 16], keep = hi ? v[i + 16] : v[i];
+      v[i] = keep + __shfl_xor(send, 32, 64);
+    }
+  }
+  {
+    const bool hi = (lane & 16) != 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float send = hi ? v[i] : v[i + 8], keep = hi ? v[i + 8] : v[i];
+      v[i] = keep + __shfl_xor(send, 16, 64);
+    }
+  }
+  {
+    const bool hi = (lane & 8) != 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float send = hi ? v[i] : v[i + 4], keep = hi ? v[i + 4] : v[i];
+      v[i] = keep + dpp_f<kDppMirror>(send);
+    }
+  }
+  {
+    const bool hi = (lane & 4) != 0;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const float send = hi ? v[i] : v[i + 2], keep = hi ? v[i + 2] : v[i];
+      v[i] = keep + dpp_f<kDppHalfMirror>(send);
+    }
+  }
+  {
+    const bool hi = (lane & 2) != 0;
+    const float send = hi ? v[0] : v[1], keep = hi ? v[1] : v[0];
+    v[0] = keep + dpp_f<kDppXor2>(send);
+  }
+  return v[0] + dpp_f<kDppXor1>(v[0]);
+}
+
+// Inclusive prefix sum over the wave's lanes (row shifts, then the row
+// broadcasts that carry row totals forward).
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, kDppRowBcast15, 0xA, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, kDppRowBcast31, 0xC, 0xF, false);
+  return v;
+}
+
+// One workgroup's partial logits (see above); part holds nks slices of
+// [T][ncols] floats, sstride apart.
+template <typename XT, int RDT>
+__device__ __forceinline__ void route_tile(const XT* __restrict__ x, const void* __restrict__ router,
+                                           const void* __restrict__ sgi, float* __restrict__ part,
+                                           int nks, size_t sstride, int T, int H, int E, int ncols,
+                                           int blk, float (*s_red)[32]) {
+  constexpr int RB = RDT ? 2 : 4;  // router element bytes
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ntg = route_tgroups(T), nkw = kRouteWaves / ntg;
+  const int tg = wave % ntg, kw = wave / ntg;
+  const int cb = blk / nks, ks = blk - cb * nks;
+  const int nch = H >> 2;                 // 4-element chunks of a row
+  const int cps = (nch + nks - 1) / nks;  // chunks of a slice
+  const int c0 = ks * cps, c1 = min(c0 + cps, nch);
+  const uint8_t* wr[kRouteCols];
+#pragma unroll
+  for (int j = 0; j < kRouteCols; ++j) {
+    const int c = min(cb * kRouteCols + j, ncols - 1);
+    wr[j] = c < E ? static_cast<const uint8_t*>(router) + (size_t)c * H * RB
+                  : static_cast<const uint8_t*>(sgi);
+  }
+  const XT* xr[kRouteTokGroup];
+#pragma unroll
+  for (int i = 0; i < kRouteTokGroup; ++i)
+    xr[i] = x + (size_t)min(tg * kRouteTokGroup + i, T - 1) * H;
+  float acc[kRouteTokGroup * kRouteCols];  // [token][column]
+#pragma unroll
+  for (int q = 0; q < kRouteTokGroup * kRouteCols; ++q) acc[q] = 0.f;
+  for (int pb = c0 + kw * 64; pb < c1; pb += nkw * 64) {
+    const int ch = pb + lane;
+    const bool ok = ch < c1;
+    const int cc = ok ? ch : pb;  // a chunk of the slice; its products are dropped
+    float w[kRouteCols][4], xv[kRouteTokGroup][4];
+#pragma unroll
+    for (int j = 0; j < kRouteCols; ++j) ld4f<RDT != 0>(wr[j] + (size_t)cc * 4 * RB, w[j]);
+#pragma unroll
+    for (int i = 0; i < kRouteTokGroup; ++i)
+      ld4f<sizeof(XT) == 2>(xr[i] + (size_t)cc * 4, xv[i]);
+#pragma unroll
+    for (int j = 0; j < kRouteCols; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[j][e] = ok ? w[j][e] : 0.f;
+#pragma unroll
+    for (int i = 0; i < kRouteTokGroup; ++i)
+#pragma unroll
+      for (int j = 0; j < kRouteCols; ++j) {
+        float d = acc[i * kRouteCols + j];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) d = fmaf(xv[i][e], w[j][e], d);
+        acc[i * kRouteCols + j] = d;
+      }
+  }
+  const float v = wave_reduce_scatter32(acc);
+  if ((lane & 1) == 0) s_red[wave][lane >> 1] = v;
+  __syncthreads();
+  if (tid < ntg * 32) {
+    const int g = tid >> 5, q = tid & 31;
+    const int t = g * kRouteTokGroup + (q >> 2), c = cb * kRouteCols + (q & 3);
+    if (t < T && c < ncols) {
+      float sm = 0.f;
+      for (int kp = 0; kp < nkw; ++kp) sm += s_red[kp * ntg + g][q];
+      __hip_atomic_store(part + (size_t)ks * sstride + (size_t)t * ncols + c, sm, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+struct RouteTailLds {
   float l[kSmallMaxTokens * MOE_MAX_EXPERTS_DEV];     // logits [T][E]
-  int8_t sel[kSmallMaxTokens * MOE_MAX_EXPERTS_DEV];  // slot of (t, e), or -1
-  int rid[kSmallRoutes];                              // expert of route t*k + j
-  float den[kSmallMaxTokens];                         // softmax denominator per token
-  // rank keys, rows padded to an even length with key 0 (below every real key)
-  __attribute__((aligned(16))) uint64_t key[kRankMaxPairs + kSmallMaxTokens];
+  int8_t pos[kSmallMaxTokens * MOE_MAX_EXPERTS_DEV];  // top-k position of a selected (t, e)
+  uint32_t tok[MOE_MAX_EXPERTS_DEV];                  // bit t: token t selected expert e
+  int part[4];                                        // per-wave scan totals
 };
 
-// TMAX bounds T: the per-token loops are unrolled to TMAX, so the common
-// few-token case runs a short instruction stream.
-template <int TMAX>
-__device__ __forceinline__ void route_small_impl(const float* __restrict__ logits, int T, int E,
-                                                 int k, int ncols, RouteMode rm, int has_shared,
-                                                 const SmallRouteOut& o, RouteLds& L) {
-  float* s_l = L.l;
-  int8_t* s_sel = L.sel;
-  int* s_rid = L.rid;
-  float* s_den = L.den;
-  uint64_t* s_key = L.key;
+// The routing of all T tokens by the last workgroup (E <= 64 * C).
+template <int C>
+__device__ __forceinline__ void route_tail(const float* __restrict__ part, int nks, size_t sstride,
+                                           const float* __restrict__ bias, int T, int E, int k,
+                                           int ncols, RouteMode rm, int has_shared,
+                                           const SmallRouteOut& o, RouteTailLds& L) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int R = T * k;
-  const bool use_rank = rank_route_ok(T, E);
-  const int Ep = (E + 1) & ~1;
-
-  // 1. logits -> LDS; thread e loads column e of every token, all loads at once
-  {
-    const bool eok = tid < E;
-    float lv[TMAX];
+  const int n = T * ncols;
+  // 1. logits: slices added in order, then the bias; a thread takes quads of
+  //    4 entries and issues all its loads before adding
+  constexpr int kQuads = (kSmallMaxTokens * (MOE_MAX_EXPERTS_DEV + 1) + 4 * kRouteThreads - 1) /
+                         (4 * kRouteThreads);
+  u32x4 pv[kQuads][kRouteMaxSlices];
 #pragma unroll
-    for (int t = 0; t < TMAX; ++t)
-      lv[t] = (t < T && eok) ? logits[(size_t)t * ncols + tid] : 0.f;
+  for (int qi = 0; qi < kQuads; ++qi) {
+    const int q = tid + qi * kRouteThreads;
 #pragma unroll
-    for (int t = 0; t < TMAX; ++t) {
-      if (t < T && eok) {
-        s_l[t * E + tid] = lv[t];
-        s_sel[t * E + tid] = -1;
-        if (use_rank) s_key[t * Ep + tid] = route_key(lv[t], tid);
-      }
-    }
-    if (use_rank && (E & 1) && tid < T) s_key[tid * Ep + E] = 0;
+    for (int s = 0; s < kRouteMaxSlices; ++s)
+      pv[qi][s] = (4 * q < n && s < nks) ? ld16(part + s * sstride + 4 * (size_t)q) : u32x4{0, 0, 0, 0};
   }
-  __syncthreads();
-
-  // 2. selection
-  if (use_rank) {
-    for (int q = tid; q < T * E; q += 256) {
-      const int t = q / E, e = q - t * E;
-      const uint64_t mine = s_key[t * Ep + e];
-      const u64x2* row = reinterpret_cast<const u64x2*>(&s_key[t * Ep]);
-      int rank = 0;
-      for (int i = 0; i < Ep / 2; ++i) {
-        const u64x2 kk = row[i];
-        rank += (kk[0] > mine ? 1 : 0) + (kk[1] > mine ? 1 : 0);
-      }
-      if (rank < k) {
-        s_sel[q] = (int8_t)rank;
-        s_rid[t * k + rank] = e;
-      }
-    }
-  } else if (E <= 64) {
-    row_select<4>(s_l, T, E, k, s_sel, s_rid);
-  } else if (E <= 128) {
-    row_select<8>(s_l, T, E, k, s_sel, s_rid);
-  } else {
-    row_select<16>(s_l, T, E, k, s_sel, s_rid);
-  }
-  __syncthreads();
-
-  if constexpr (TMAX <= 4) {
-    // 3+4. weights: wave t handles token t, lane j slot j
-    if (wave < T) {
-      const int t = wave;
-      const float* lt = s_l + t * E;
-      const int id = lane < k ? s_rid[t * k + lane] : 0;
-      const float lmax = lt[s_rid[t * k]];
-      const float ex = lane < k ? (rm.sigmoid ? sigmoid_f(lt[id]) : __expf(lt[id] - lmax)) *
-                                      expert_scale_of(rm, id)
-                                : 0.f;
-      float denom;
-      if (rm.normalize) {
-        denom = wave_sum(ex);
-      } else if (rm.sigmoid) {
-        denom = 1.f;
-      } else {
-        float sum = 0.f;
-        for (int e = lane; e < E; e += 64) sum += __expf(lt[e] - lmax);
-        denom = wave_sum(sum);
-      }
-      if (lane < k) {
-        const int r = t * k + lane;
-        const float w = ex / denom * rm.scale;
-        o.ids[r] = id;
-        o.wts[r] = w;
-        if (o.user_ids) o.user_ids[r] = id;
-        if (o.user_w) o.user_w[r] = w;
-      }
-    }
-  } else {
-    // 3. denominators, a 16-lane row per token: the selected terms
-    //    (renormalised weights), all E terms (plain softmax probabilities),
-    //    or none (plain sigmoid scores)
-    const int l16 = lane & 15;
-    for (int t0 = wave * 4; t0 < T; t0 += 16) {
-      const int t = t0 + (lane >> 4);
-      float sum = 0.f;
-      if (t < T) {
-        const float* lt = s_l + t * E;
-        const float lmax = lt[s_rid[t * k]];
-        for (int e = l16; e < E; e += 16) {
-          const bool sel = s_sel[t * E + e] >= 0;
-          if (rm.sigmoid) {
-            if (sel) sum += sigmoid_f(lt[e]) * expert_scale_of(rm, e);
-          } else if (!rm.normalize) {
-            sum += __expf(lt[e] - lmax);
-          } else if (sel) {
-            sum += __expf(lt[e] - lmax) * expert_scale_of(rm, e);
-          }
+  if (tid < E) L.tok[tid] = 0u;
+#pragma unroll
+  for (int qi = 0; qi < kQuads; ++qi) {
+    const int q = tid + qi * kRouteThreads;
+    int t = 4 * q / ncols, c = 4 * q - t * ncols;
+#pragma unroll
+    for (int e4 = 0; e4 < 4; ++e4) {
+      if (4 * q + e4 < n) {
+        float v = __uint_as_float(pv[qi][0][e4]);
+#pragma unroll
+        for (int s = 1; s < kRouteMaxSlices; ++s)
+          if (s < nks) v += __uint_as_float(pv[qi][s][e4]);
+        if (c < E) {
+          if (bias) v += bias[c];
+          L.l[t * E + c] = v;
+        } else {
+          o.sgate[t] = sigmoid_f(v);
         }
       }
-      sum += dpp_f<kDppXor1>(sum);
-      sum += dpp_f<kDppXor2>(sum);
-      sum += dpp_f<kDppHalfMirror>(sum);
-      sum += dpp_f<kDppMirror>(sum);
-      if (t < T && l16 == 0) s_den[t] = (rm.sigmoid && !rm.normalize) ? 1.f : sum;
+      if (++c == ncols) {
+        c = 0;
+        ++t;
+      }
     }
-    __syncthreads();
-    // 4. ids and weights, one thread per route
-    for (int r = tid; r < R; r += 256) {
-      const int t = r / k;
-      const float* lt = s_l + t * E;
-      const int id = s_rid[r];
-      const float sc = (rm.sigmoid ? sigmoid_f(lt[id]) : __expf(lt[id] - lt[s_rid[t * k]])) *
-                       expert_scale_of(rm, id);
-      const float w = sc / s_den[t] * rm.scale;
+  }
+  __syncthreads();
+
+  // 2. top-k, weights: one wave per token
+  for (int t = wave; t < T; t += kRouteWaves) {
+    int id;
+    float w;
+    uint64_t sel[C];
+    route_one_token<C>(L.l + t * E, E, k, rm, id, w, sel);
+    if (lane < k) {
+      const int r = t * k + lane;
       o.ids[r] = id;
       o.wts[r] = w;
       if (o.user_ids) o.user_ids[r] = id;
       if (o.user_w) o.user_w[r] = w;
+      L.pos[t * E + id] = (int8_t)lane;
+      atomicOr(&L.tok[id], 1u << t);
     }
   }
-  if (has_shared && tid < T) o.sgate[tid] = sigmoid_f(logits[(size_t)tid * ncols + E]);
+  __syncthreads();
 
-  // 5. grouping, one thread per expert
-  int sel[TMAX];
-  int cnt = 0;
-#pragma unroll
-  for (int t = 0; t < TMAX; ++t) {
-    sel[t] = (t < T && tid < E) ? (int)s_sel[t * E + tid] : -1;
-    cnt += sel[t] >= 0 ? 1 : 0;
+  // 3. grouping, one thread per expert: counts and the active flag, packed
+  //    in one word for the scan (counts stay below 2^16)
+  const uint32_t tok = tid < E ? L.tok[tid] : 0u;  // bit t: token t selected this expert
+  const int cnt = __popc(tok);
+  const int mine = cnt | (cnt > 0 ? 1 << 16 : 0);
+  int incl = 0;
+  if (wave < 4) {
+    incl = wave_incl_scan(mine);
+    if (lane == 63) L.part[wave] = incl;
   }
-  const int act = cnt > 0 ? 1 : 0;
-  int off, aoff, total, nact;
-  block_scan2(cnt, act, off, aoff, total, nact);
+  __syncthreads();
   if (tid < E) {
+    int base = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int pw = L.part[w];
+      base += w < wave ? pw : 0;
+      total += pw;
+    }
+    const int ex = incl + base - mine;
+    const int off = ex & 0xFFFF, aoff = ex >> 16;
     o.counts[tid] = cnt;
     o.offsets[tid] = off;
     if (o.user_counts) o.user_counts[tid] = cnt;
     if (o.user_offsets) o.user_offsets[tid] = off;
-    if (act) o.active[aoff] = tid;
+    if (cnt > 0) o.active[aoff] = tid;
     int pos = off;
-#pragma unroll
-    for (int t = 0; t < TMAX; ++t) {
-      if (sel[t] >= 0) {
-        const int r = t * k + sel[t];
-        o.perm[pos] = r;
-        o.pos_of_route[r] = pos;
-        if (o.user_perm) o.user_perm[pos] = r;
-        ++pos;
+    for (uint32_t m = tok; m != 0u; m &= m - 1u) {
+      const int t = __ffs(m) - 1;
+      const int r = t * k + L.pos[t * E + tid];
+      o.perm[pos] = r;
+      o.pos_of_route[r] = pos;
+      if (o.user_perm) o.user_perm[pos] = r;
+      ++pos;
+    }
+    if (tid == 0) {
+      const int R = T * k;
+      o.offsets[E] = R;
+      if (o.user_offsets) o.user_offsets[E] = R;
+      int na = total >> 16;
+      if (has_shared) {
+        o.counts[E] = T;
+        o.active[na++] = E;
       }
+      *o.n_active = na;
     }
-  }
-  if (tid == 0) {
-    o.offsets[E] = R;
-    if (o.user_offsets) o.user_offsets[E] = R;
-    int na = nact;
-    if (has_shared) {
-      o.counts[E] = T;
-      o.active[na++] = E;
-    }
-    *o.n_active = na;
   }
 }
 
-__device__ void route_small_body(const float* __restrict__ logits, int T, int E, int k,
-                                 int ncols, RouteMode rm, int has_shared,
-                                 const SmallRouteOut& o) {
-  __shared__ RouteLds L;
-  if (T <= 4) route_small_impl<4>(logits, T, E, k, ncols, rm, has_shared, o, L);
-  else route_small_impl<kSmallMaxTokens>(logits, T, E, k, ncols, rm, has_shared, o, L);
-}
-
-// Router logits fused with the routing: workgroup e computes router row e
-// (logit column e for every token), then takes a ticket.  The workgroup
-// that takes the last ticket sees every column written, routes all tokens
-// and sets the ticket counter back to zero for the next call.
-// Publication: the logits are stored at device scope and the wave waits
-// for those stores to complete before the ticket is taken; the last
-// workgroup invalidates its caches (device-scope acquire) before reading
-// them.  A device-scope release fence per workgroup would instead write
-// back the whole L2 of its XCD, which costs far more than the GEMV.
-template <typename XT, int RDT, int NC>
-__global__ __launch_bounds__(256) void k_router_route(const XT* __restrict__ x,
-                                                      const void* __restrict__ router,
-                                                      const float* __restrict__ bias,
-                                                      const void* __restrict__ shared_gate_inp,
-                                                      float* __restrict__ logits, int T, int H,
-                                                      int E, int k, int ncols, RouteMode rm,
-                                                      int has_shared, int* __restrict__ ticket,
-                                                      SmallRouteOut o) {
-  if (H / (RDT ? 8 : 4) <= 256 * NC && T <= kRowTokens)
-    router_row_few<XT, RDT, true, NC>(x, router, bias, shared_gate_inp, logits, T, H, E, ncols,
-                                      blockIdx.x);
-  else
-    router_row<XT, RDT, true, NC>(x, router, bias, shared_gate_inp, logits, T, H, E, ncols,
-                                  blockIdx.x);
+// Publication of the partial logits: they are stored at device scope and
+// each wave waits for its stores to complete before the ticket is taken;
+// the last workgroup invalidates its caches (device-scope acquire) before
+// reading them, and sets the counter back to zero for the next call.  A
+// device-scope release fence per workgroup would instead write back the
+// whole L2 of its XCD, which costs far more than the tile.
+template <typename XT, int RDT>
+__global__ __launch_bounds__(kRouteThreads) void k_router_route(
+    const XT* __restrict__ x, const void* __restrict__ router, const float* __restrict__ bias,
+    const void* __restrict__ shared_gate_inp, float* __restrict__ part, int nks, int T, int H,
+    int E, int k, int ncols, RouteMode rm, int has_shared, int* __restrict__ ticket,
+    SmallRouteOut o) {
+  __shared__ float s_red[kRouteWaves][32];
+  __shared__ RouteTailLds L;
   __shared__ int s_last;
-  __builtin_amdgcn_s_waitcnt(0);  // this wave's logit stores have completed
+  const size_t sstride = route_slice_stride(T, ncols);
+  route_tile<XT, RDT>(x, router, shared_gate_inp, part, nks, sstride, T, H, E, ncols, blockIdx.x,
+                      s_red);
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores have completed
   __syncthreads();
   if (threadIdx.x == 0)
     s_last = __hip_atomic_fetch_add(ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
@@ -497,7 +495,14 @@ __global__ __launch_bounds__(256) void k_router_route(const XT* __restrict__ x,
   if (!s_last) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   if (threadIdx.x == 0) __hip_atomic_store(ticket, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  route_small_body(logits, T, E, k, ncols, rm, has_shared, o);
+  if (E <= 64)
+    route_tail<1>(part, nks, sstride, bias, T, E, k, ncols, rm, has_shared, o, L);
+  else if (E <= 128)
+    route_tail<2>(part, nks, sstride, bias, T, E, k, ncols, rm, has_shared, o, L);
+  else if (E <= 192)
+    route_tail<3>(part, nks, sstride, bias, T, E, k, ncols, rm, has_shared, o, L);
+  else
+    route_tail<4>(part, nks, sstride, bias, T, E, k, ncols, rm, has_shared, o, L);
 }
 
 // Routing data read back from the workspace, clamped to the layer's ranges,

@@ -62,6 +62,7 @@ struct Plan {
   int bt = 128;            // grouped-GEMM route-tile height
   int max_groups = 0;      // active groups (upper bound)
   int rsplit = 1;          // prefill router: K ranges (partial logits added by the top-k)
+  int rks = 1;             // few-token router: K slices (partial logits added by the routing)
   // workspace offsets
   size_t o_sync, o_xn, o_logits, o_ids, o_wts, o_sgate, o_bhist, o_boff, o_counts, o_offsets, o_active,
       o_nactive, o_ntiles, o_perm, o_pos, o_rowtok, o_tgroup, o_tm0, o_h, o_hs, o_y, o_ys, o_slots;
@@ -178,7 +179,10 @@ Plan make_plan(const moe_desc* d, int64_t T) {
     while (tiles * p.rsplit < 256 && nk % (2 * p.rsplit) == 0 && nk / (2 * p.rsplit) >= 8)
       p.rsplit *= 2;
   }
-  p.o_logits = take((size_t)p.rsplit * T * p.ncols * 4);
+  // few tokens routed in the router launch: partial logits of its K slices
+  if (p.small) p.rks = route_slices((int)T, p.H, p.ncols);
+  p.o_logits = take(std::max((size_t)p.rsplit * T * p.ncols,
+                             (size_t)p.rks * route_slice_stride((int)T, p.ncols)) * 4);
   p.o_ids = take((size_t)p.R * 4);
   p.o_wts = take((size_t)p.R * 4);
   p.o_sgate = take((size_t)T * 4);
@@ -348,16 +352,19 @@ moe_status run_route_small(const moe_desc* d, const Plan& p, const void* x, cons
   const bool xb = d->act_dtype == MOE_BF16, rb = d->router_dtype == MOE_BF16;
   const int sh = p.shared ? 1 : 0;
   const RouteMode rm = route_mode(d, w);
-  dim3 grid(p.ncols);
-  const int nc = router_nc(p.H / (rb ? 8 : 4));
+  const dim3 grid((p.ncols + kRouteCols - 1) / kRouteCols * p.rks);
   return launch("router_route", s, [&] {
-    auto go = [&](auto xtag, auto rtag, auto nctag) {
+    auto go = [&](auto xtag, auto rtag) {
       using XT = decltype(xtag);
-      constexpr int RDT = decltype(rtag)::value, NC = decltype(nctag)::value;
-      k_router_route<XT, RDT, NC><<<grid, 256, 0, s>>>(static_cast<const XT*>(x), w->router,
-          w->router_bias, w->shared_gate_inp, logits, T, p.H, p.E, p.k, p.ncols, rm, sh, ticket, o);
+      constexpr int RDT = decltype(rtag)::value;
+      k_router_route<XT, RDT><<<grid, kRouteThreads, 0, s>>>(static_cast<const XT*>(x),
+          w->router, w->router_bias, w->shared_gate_inp, logits, p.rks, T, p.H, p.E, p.k,
+          p.ncols, rm, sh, ticket, o);
     };
-    dispatch_router(xb, rb, nc, go);
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    if (xb) { if (rb) go(uint16_t{}, I1{}); else go(uint16_t{}, I0{}); }
+    else { if (rb) go(float{}, I1{}); else go(float{}, I0{}); }
   });
 }
 
