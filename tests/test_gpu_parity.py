@@ -137,10 +137,28 @@ SMALL = [
     MoeConfig(name="gemv_f32_k32", T=2, H=64, I=32, E=256, k=32, seed_index=21),
     MoeConfig(name="gemv_bf16_f32x_t32", T=32, H=2816, I=704, E=128, k=8, act=ACT_GELU_TANH,
               weight_format=WF_BF16, router_dtype=DT_BF16, seed_index=22),
-    # decode routing: row selection (four tokens per wave) at 64 and 200 experts
+    # few-token router launch: 64 and 200 experts (one and four logits a
+    # lane in the per-token ranking)
     MoeConfig(name="gemv_route_rows_e64", T=32, H=128, I=64, E=64, k=6, seed_index=28),
     MoeConfig(name="gemv_route_rows_e200", T=20, H=64, I=32, E=200, k=5, weight_format=WF_BF16,
               router_dtype=DT_BF16, seed_index=29),
+    # few-token router tiles: one, two and four token groups (the last ones
+    # partly or wholly past T), one, two and four K slices, a ragged last
+    # column block (shared gate column included), a router bias, 257 logit
+    # columns (three quads a thread when the slices are added), three
+    # logits a lane in the ranking
+    MoeConfig(name="route_t8_bias_shared", T=8, H=8192, I=64, E=8, k=2, weight_format=WF_BF16,
+              router_dtype=DT_BF16, bias=BIAS_ZIPF, shared=True, Is=64, seed_index=510),
+    MoeConfig(name="route_t17_e41_shared", T=17, H=1024, I=64, E=41, k=5, act_dtype=DT_BF16,
+              shared=True, Is=32, seed_index=511),
+    MoeConfig(name="route_t32_e256_shared", T=32, H=512, I=32, E=256, k=8, weight_format=WF_BF16,
+              router_dtype=DT_BF16, shared=True, Is=32, seed_index=512),
+    MoeConfig(name="route_t25_u4_e192", T=25, H=2048, I=64, E=192, k=6, weight_format=WF_U4,
+              seed_index=513),
+    MoeConfig(name="route_t16_two_slices", T=16, H=4096, I=32, E=12, k=3, router_dtype=DT_BF16,
+              seed_index=514),
+    MoeConfig(name="route_t32_four_slices", T=32, H=4096, I=32, E=16, k=4, weight_format=WF_BF16,
+              act_dtype=DT_BF16, router_dtype=DT_BF16, bias=BIAS_ZIPF, seed_index=515),
     MoeConfig(name="gemv_bf16_large_t_fallback", T=100, H=96, I=64, E=8, k=2,
               weight_format=WF_BF16, act_dtype=DT_BF16, router_dtype=DT_BF16, seed_index=23),
 ]
@@ -499,10 +517,9 @@ def test_one_token_sweep(cfg, route):
 
 
 def _few_token_sweep(n=10, seed=0x5E7):
-    """A fixed, seeded list of 2..32-token decode layers: the router rows
-    with one to four chunks a thread (or longer rows, walked in blocks), and
-    the routing workgroup's three strategies (a wave per token at T <= 4,
-    rank counting, row selection), f32, bf16 and 4-bit weights."""
+    """A fixed, seeded list of 2..32-token decode layers: router rows of 64
+    to 5120 elements (one to four K slices, one, two or four token groups),
+    4 to 200 experts, f32, bf16 and 4-bit weights."""
     rng = np.random.default_rng(seed)
     out = []
     for i in range(n):
