@@ -38,7 +38,7 @@ constexpr int kU4StageThreads = 256;
 // groups per lane per step (UG) and row pairs per wave (PW) of the two
 // expert kernels: gate/up 128 features a workgroup, down 256 output rows
 constexpr int kU4UGGateUp = 2, kU4PWGateUp = 4;
-constexpr int kU4UGDown = 1, kU4PWDown = 4;
+constexpr int kU4UGDown = 1, kU4PWDown = 8;
 
 // Staged activation row (one token of x, or one route of h), row length K,
 // G = K / 32 groups.  Value v of the row is multiplied by the row's power of
