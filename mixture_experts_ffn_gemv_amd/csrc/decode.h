@@ -15,11 +15,12 @@
 //                 split K into 16-byte chunks and issue every weight load of
 //                 those rows before touching the activations.  Only the
 //                 touched experts' weights are read, each byte once.  With
-//                 ONE (one token) every wave ranks the token's logits
-//                 itself (route_one_token: the selection order and weights
-//                 of the routing workgroup) to find its expert, and one
-//                 wave of workgroup (0,0) writes the routing (and the slot
-//                 table k_dec_down3<ONE> reads) for the down kernel and the
+//                 ONE (one token) the workgroups of column s < k take the
+//                 expert at top-k position s, and each of their waves runs
+//                 the first s + 1 rounds of the ranking itself to find it;
+//                 one wave of column k - 1 ranks in full (route_one_token)
+//                 and writes the routing (and the slot table
+//                 k_dec_down3<ONE> reads) for the down kernel and the
 //                 caller: one token's top-k costs a wave less than a
 //                 grid-wide handoff inside the router launch does.
 // k_dec_down3     work item = block of output features; the 4 waves split
@@ -99,13 +100,9 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 // part.
 static_assert(MOE_MAX_EXPERTS_DEV <= 4 * 64, "one-token ranking holds at most 4 logits a lane");
 template <int C>
-__device__ __forceinline__ void route_one_token(const float* __restrict__ l, int E, int k,
-                                                RouteMode rm, int& id, float& w,
-                                                uint64_t (&sel)[C]) {
+__device__ __forceinline__ void rank_load(const float* __restrict__ l, int E, float (&lv)[C],
+                                          uint32_t (&ord)[C], bool (&live)[C]) {
   const int lane = threadIdx.x & 63;
-  float lv[C];
-  uint32_t ord[C];
-  bool live[C];
 #pragma unroll
   for (int c = 0; c < C; ++c) {
     const int e = lane + 64 * c;
@@ -114,25 +111,55 @@ __device__ __forceinline__ void route_one_token(const float* __restrict__ l, int
     ord[c] = ok ? route_ord(lv[c]) : 0u;
     live[c] = ok;
   }
+}
+// One round: the wave maximum M of the images and the lowest live expert e
+// whose image is M, which is then taken (wave-uniform results).
+template <int C>
+__device__ __forceinline__ int rank_round(uint32_t (&ord)[C], bool (&live)[C], uint32_t& M) {
+  const int lane = threadIdx.x & 63;
+  uint32_t m = ord[0];
+#pragma unroll
+  for (int c = 1; c < C; ++c) m = max(m, ord[c]);
+  M = wave_max_u32(m);
+  int e = 0;
+#pragma unroll
+  for (int c = C - 1; c >= 0; --c) {
+    const uint64_t hit = __ballot(live[c] && ord[c] == M);
+    e = hit != 0 ? 64 * c + __ffsll((unsigned long long)hit) - 1 : e;
+  }
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    const bool taken = lane + 64 * c == e;
+    live[c] = live[c] && !taken;
+    ord[c] = taken ? 0u : ord[c];
+  }
+  return e;
+}
+// The expert at top-k position n - 1 (n >= 1): the first n rounds alone.
+template <int C>
+__device__ __forceinline__ int rank_nth(const float* __restrict__ l, int E, int n) {
+  float lv[C];
+  uint32_t ord[C], M;
+  bool live[C];
+  rank_load<C>(l, E, lv, ord, live);
+  int e = 0;
+  for (int j = 0; j < n; ++j) e = rank_round<C>(ord, live, M);
+  return e;
+}
+template <int C>
+__device__ __forceinline__ void route_one_token(const float* __restrict__ l, int E, int k,
+                                                RouteMode rm, int& id, float& w,
+                                                uint64_t (&sel)[C]) {
+  const int lane = threadIdx.x & 63;
+  float lv[C];
+  uint32_t ord[C];
+  bool live[C];
+  rank_load<C>(l, E, lv, ord, live);
   int my_e = 0;
   uint32_t my_ord = 0, top = 0;
   for (int j = 0; j < k; ++j) {
-    uint32_t m = ord[0];
-#pragma unroll
-    for (int c = 1; c < C; ++c) m = max(m, ord[c]);
-    const uint32_t M = wave_max_u32(m);
-    int e = 0;
-#pragma unroll
-    for (int c = C - 1; c >= 0; --c) {
-      const uint64_t hit = __ballot(live[c] && ord[c] == M);
-      e = hit != 0 ? 64 * c + __ffsll((unsigned long long)hit) - 1 : e;
-    }
-#pragma unroll
-    for (int c = 0; c < C; ++c) {
-      const bool taken = lane + 64 * c == e;
-      live[c] = live[c] && !taken;
-      ord[c] = taken ? 0u : ord[c];
-    }
+    uint32_t M;
+    const int e = rank_round<C>(ord, live, M);
     if (j == 0) top = M;
     if (lane == j) {
       my_e = e;
@@ -637,40 +664,32 @@ constexpr int kRCMax = 4;    // routes per LDS pass (gate/up with several routes
 constexpr int kGUWaves = 4;  // features per gate/up workgroup (one per wave)
 
 // One token, routed in the gate/up kernel: every wave ranks the router
-// logits itself (route_one_token: the same result in each), so the weight
-// stream waits for no routing launch.  Slot s is the s-th smallest selected
-// expert, its route the expert's top-k position; slot k is the shared
-// expert.
+// logits itself, so the weight stream waits for no routing launch.
+// Workgroup column s < k takes the expert at top-k position s (its route
+// s) and needs only the first s + 1 rounds of the ranking; column k is the
+// shared expert (no ranking).  One wave of column k - 1, which needs all k
+// rounds anyway, ranks in full (route_one_token) and writes the routing.
 struct OneRoute {
   int id;           // lane j < k: the expert of top-k position j
   float w;          // and its routing weight
   uint64_t sel[4];  // selected experts, expert 64c + b at bit b of sel[c]
 };
 template <int C>
-__device__ __forceinline__ void route_slot(const Dec2Params& p, int s, int& na, int& slot_g,
-                                           int& route_r, OneRoute& rt) {
-  const int lane = threadIdx.x & 63;
-  uint64_t sel[C];
-  route_one_token<C>(p.logits, p.E, p.k, p.rm, rt.id, rt.w, sel);
-#pragma unroll
-  for (int c = 0; c < 4; ++c) rt.sel[c] = c < C ? sel[c] : 0ull;
+__device__ __forceinline__ void route_slot(const Dec2Params& p, int s, bool writer, int& na,
+                                           int& slot_g, int& route_r, OneRoute& rt) {
   na = p.k + (p.Is > 0 ? 1 : 0);
   slot_g = p.E;
   route_r = 0;
-  if (s < p.k) {  // the s-th set bit of sel, on the scalar unit
-    int rem = s;
+  if (writer) {
+    uint64_t sel[C];
+    route_one_token<C>(p.logits, p.E, p.k, p.rm, rt.id, rt.w, sel);
 #pragma unroll
-    for (int c = 0; c < C; ++c) {
-      uint64_t m = sel[c];
-      const int n = __popcll(m);
-      if (rem >= 0 && rem < n) {
-        for (int i = 0; i < rem; ++i) m &= m - 1;
-        slot_g = 64 * c + __ffsll((unsigned long long)m) - 1;
-      }
-      rem -= n;
-    }
-    const uint64_t at = __ballot(lane < p.k && rt.id == slot_g);
-    route_r = __builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)at) - 1);
+    for (int c = 0; c < 4; ++c) rt.sel[c] = c < C ? sel[c] : 0ull;
+    slot_g = __builtin_amdgcn_readlane(rt.id, s);
+    route_r = s;
+  } else if (s < p.k) {
+    slot_g = rank_nth<C>(p.logits, p.E, s + 1);
+    route_r = s;
   }
 }
 
@@ -748,9 +767,11 @@ __global__ __launch_bounds__(256) void k_dec_gateup3(Dec2Params p) {
   // follow while they are in flight.
   int na, slot_g, route_r = 0;
   OneRoute rt;
+  // the wave that writes the routing (column k - 1 holds a routed expert)
+  const bool writer = ONE && s == p.k - 1 && blockIdx.y == 0 && threadIdx.x < 64;
   if constexpr (ONE) {
-    if (p.E <= 128) route_slot<2>(p, s, na, slot_g, route_r, rt);
-    else route_slot<4>(p, s, na, slot_g, route_r, rt);
+    if (p.E <= 128) route_slot<2>(p, s, writer, na, slot_g, route_r, rt);
+    else route_slot<4>(p, s, writer, na, slot_g, route_r, rt);
   } else {
     na = *p.n_active;
     slot_g = p.active[s];
@@ -788,8 +809,7 @@ __global__ __launch_bounds__(256) void k_dec_gateup3(Dec2Params p) {
         load_chunk<WF, true>(Mg, row, p.H, c, ok, wg[u], sg[u], mg[u]);
         load_chunk<WF, true>(Mu, row, p.H, c, ok, wu[u], su[u], mu[u]);
       }
-      // workgroup (0, 0) holds slot 0, a routed expert, and feature 0
-      if (kb == 0 && blockIdx.x == 0 && blockIdx.y == 0 && wave == 0) route_write(p, rt);
+      if (kb == 0 && writer) route_write(p, rt);
       if (kb == 0 && !shared) {  // the expert's one route, and its token
         r = route_r;
         t = r / p.k;
