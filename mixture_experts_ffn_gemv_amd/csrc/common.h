@@ -114,6 +114,21 @@ __device__ __forceinline__ void wave_argmax(float& bv, int& bi) {
   bi = i;
 }
 
+constexpr int kDppRowBcast15 = 0x142;  // lane 15 of each row to the next row
+constexpr int kDppRowBcast31 = 0x143;  // lane 31 to rows 2 and 3
+
+// Inclusive prefix sum over the wave's lanes (row shifts, then the row
+// broadcasts that carry row totals forward).
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, kDppRowBcast15, 0xA, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, kDppRowBcast31, 0xC, 0xF, false);
+  return v;
+}
+
 __device__ __forceinline__ uint64_t lanemask_lt() {
   const int l = threadIdx.x & 63;
   return l == 0 ? 0ull : (~0ull >> (64 - l));

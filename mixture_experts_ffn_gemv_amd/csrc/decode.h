@@ -73,8 +73,6 @@ __device__ __forceinline__ uint32_t route_ord(float l) {
 __device__ __forceinline__ float ord_logit(uint32_t ord) {
   return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord);
 }
-constexpr int kDppRowBcast15 = 0x142;  // lane 15 of each row to the next row
-constexpr int kDppRowBcast31 = 0x143;  // lane 31 to rows 2 and 3
 
 // Maximum of v over the wave, wave-uniform: the row maximum by four DPP
 // steps, then two row broadcasts carry it to lane 63.
@@ -292,18 +290,6 @@ __device__ __forceinline__ float wave_reduce_scatter32(float (&v)[32]) {
     v[0] = keep + dpp_f<kDppXor2>(send);
   }
   return v[0] + dpp_f<kDppXor1>(v[0]);
-}
-
-// Inclusive prefix sum over the wave's lanes (row shifts, then the row
-// broadcasts that carry row totals forward).
-__device__ __forceinline__ int wave_incl_scan(int v) {
-  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);  // row_shr:1
-  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);  // row_shr:2
-  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);  // row_shr:4
-  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);  // row_shr:8
-  v += __builtin_amdgcn_update_dpp(0, v, kDppRowBcast15, 0xA, 0xF, false);
-  v += __builtin_amdgcn_update_dpp(0, v, kDppRowBcast31, 0xC, 0xF, false);
-  return v;
 }
 
 // One workgroup's partial logits (see above); part holds nks slices of

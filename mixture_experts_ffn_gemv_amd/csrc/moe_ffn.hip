@@ -395,11 +395,11 @@ moe_status run_route_and_group(const moe_desc* d, const Plan& p, const moe_weigh
   so.user_counts = user_counts;
   so.user_offsets = user_offsets;
   MOE_TRY(launch("perm_scan", s, [&] {
-    k_perm_scan<<<1, 256, 0, s>>>(wsp<int32_t>(ws, p.o_bhist), p.nblk, p.E, T, p.shared ? 1 : 0,
+    k_perm_scan<<<1, 256 * kScanParts, 0, s>>>(wsp<int32_t>(ws, p.o_bhist), p.nblk, p.E, T, p.shared ? 1 : 0,
                                   p.bt, p.mfma ? 1 : 0, so);
   }));
   return launch("perm_scatter", s, [&] {
-    k_perm_scatter<<<p.nblk, 64, 0, s>>>(wsp<int32_t>(ws, p.o_ids), R, p.E, p.k,
+    k_perm_scatter<<<p.nblk, 64 * kScatterWaves, 0, s>>>(wsp<int32_t>(ws, p.o_ids), R, p.E, p.k,
                                          wsp<int32_t>(ws, p.o_boff), wsp<int32_t>(ws, p.o_perm),
                                          wsp<int32_t>(ws, p.o_pos), wsp<int32_t>(ws, p.o_rowtok),
                                          user_perm);

@@ -239,80 +239,96 @@ struct ScanOut {
   int32_t* user_offsets;  // [E+1] or null
 };
 
-// One workgroup of 256 threads; thread e owns expert e (E <= 256).  The
-// per-block counts of a column are read kScanBatch at a time, every load of
-// a batch issued before any is added (indices clamped, so the loads need no
-// branch): read one by one, each load's latency would add up over the
-// blocks.
+// One workgroup of 1024 threads: thread (part, e) = (tid / 256, tid % 256)
+// owns expert e (E <= 256) over a quarter of the blocks (a contiguous
+// range), so each thread reads a quarter of the column of per-block counts;
+// the quarters' sums meet in LDS.  Every quarter's four waves then scan the
+// expert totals themselves (DPP wave scans, one exchange of wave totals), so
+// each thread has its expert's offset without a further barrier, and writes
+// the starting positions of its blocks.  The per-block counts of a range
+// are read kScanBatch at a time, every load of a batch issued before any is
+// added (indices clamped, so the loads need no branch).
 constexpr int kScanBatch = 16;
-__global__ __launch_bounds__(256) void k_perm_scan(const int32_t* __restrict__ block_hist,
-                                                   int nblk, int E, int T, int has_shared,
-                                                   int tile_rows, int build_tiles, ScanOut o) {
-  __shared__ int sc[256];
-  __shared__ int sa[256];
-  __shared__ int st[256];
-  const int e = threadIdx.x;
+constexpr int kScanParts = 4;
+__global__ __launch_bounds__(256 * kScanParts) void k_perm_scan(
+    const int32_t* __restrict__ block_hist, int nblk, int E, int T, int has_shared, int tile_rows,
+    int build_tiles, ScanOut o) {
+  __shared__ int s_cnt[kScanParts][256];
+  __shared__ int s_tot[kScanParts][4][3];
+  const int tid = threadIdx.x, e = tid & 255, part = tid >> 8;
+  const int lane = tid & 63, w4 = (tid >> 6) & 3;
   const int ec = min(e, E - 1);
-  auto batch = [&](int b0, int (&v)[kScanBatch]) {
+  const int per = (nblk + kScanParts - 1) / kScanParts;
+  const int b0 = part * per, b1 = min(b0 + per, nblk);
+  auto batch = [&](int bb, int (&v)[kScanBatch]) {
 #pragma unroll
-    for (int j = 0; j < kScanBatch; ++j) v[j] = block_hist[(size_t)min(b0 + j, nblk - 1) * E + ec];
+    for (int j = 0; j < kScanBatch; ++j)
+      v[j] = block_hist[(size_t)min(bb + j, nblk - 1) * E + ec];
   };
-  int cnt = 0;
-  for (int b0 = 0; b0 < nblk; b0 += kScanBatch) {
+  int mine = 0;  // this quarter's routes to expert e
+  for (int bb = b0; bb < b1; bb += kScanBatch) {
     int v[kScanBatch];
-    batch(b0, v);
+    batch(bb, v);
 #pragma unroll
-    for (int j = 0; j < kScanBatch; ++j) cnt += (b0 + j < nblk) ? v[j] : 0;
+    for (int j = 0; j < kScanBatch; ++j) mine += (bb + j < b1) ? v[j] : 0;
+  }
+  s_cnt[part][e] = mine;
+  __syncthreads();
+  int cnt = 0, before = 0;  // expert total; routes of the quarters before this one
+#pragma unroll
+  for (int q = 0; q < kScanParts; ++q) {
+    const int v = s_cnt[q][e];
+    cnt += v;
+    before += q < part ? v : 0;
   }
   if (e >= E) cnt = 0;
   const int act = (e < E && cnt > 0) ? 1 : 0;
   const int tiles = (e < E) ? (cnt + tile_rows - 1) / tile_rows : 0;
-  sc[e] = cnt;
-  sa[e] = act;
-  st[e] = tiles;
-  __syncthreads();
-  // inclusive Hillis-Steele scans over 256 entries
-  for (int o2 = 1; o2 < 256; o2 <<= 1) {
-    int a = (e >= o2) ? sc[e - o2] : 0;
-    int b = (e >= o2) ? sa[e - o2] : 0;
-    int c = (e >= o2) ? st[e - o2] : 0;
-    __syncthreads();
-    sc[e] += a;
-    sa[e] += b;
-    st[e] += c;
-    __syncthreads();
+  const int ic = wave_incl_scan(cnt), ia = wave_incl_scan(act), it = wave_incl_scan(tiles);
+  if (lane == 63) {
+    s_tot[part][w4][0] = ic;
+    s_tot[part][w4][1] = ia;
+    s_tot[part][w4][2] = it;
   }
-  const int off = sc[e] - cnt;  // exclusive
-  const int aoff = sa[e] - act;
-  const int toff = st[e] - tiles;
-  const int total = sc[255];
-  const int nact = sa[255];
-  const int ntile = st[255];
+  __syncthreads();
+  int off = ic - cnt, aoff = ia - act, toff = it - tiles, total = 0, nact = 0, ntile = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const int tc = s_tot[part][w][0], ta = s_tot[part][w][1], tt = s_tot[part][w][2];
+    off += w < w4 ? tc : 0;
+    aoff += w < w4 ? ta : 0;
+    toff += w < w4 ? tt : 0;
+    total += tc;
+    nact += ta;
+    ntile += tt;
+  }
   if (e < E) {
-    o.counts[e] = cnt;
-    o.offsets[e] = off;
-    if (o.user_counts) o.user_counts[e] = cnt;
-    if (o.user_offsets) o.user_offsets[e] = off;
-    if (act) o.active[aoff] = e;
-    int run = off;
-    for (int b0 = 0; b0 < nblk; b0 += kScanBatch) {
+    if (part == 0) {
+      o.counts[e] = cnt;
+      o.offsets[e] = off;
+      if (o.user_counts) o.user_counts[e] = cnt;
+      if (o.user_offsets) o.user_offsets[e] = off;
+      if (act) o.active[aoff] = e;
+      if (build_tiles)
+        for (int i = 0; i < tiles; ++i) {
+          o.tile_group[toff + i] = e;
+          o.tile_m0[toff + i] = i * tile_rows;
+        }
+    }
+    int run = off + before;
+    for (int bb = b0; bb < b1; bb += kScanBatch) {
       int v[kScanBatch];
-      batch(b0, v);
+      batch(bb, v);
 #pragma unroll
       for (int j = 0; j < kScanBatch; ++j) {
-        if (b0 + j < nblk) {
-          o.block_off[(size_t)(b0 + j) * E + e] = run;
+        if (bb + j < b1) {
+          o.block_off[(size_t)(bb + j) * E + e] = run;
           run += v[j];
         }
       }
     }
-    if (build_tiles)
-      for (int i = 0; i < tiles; ++i) {
-        o.tile_group[toff + i] = e;
-        o.tile_m0[toff + i] = i * tile_rows;
-      }
   }
-  if (e == 0) {
+  if (tid == 0) {
     o.offsets[E] = total;
     if (o.user_offsets) o.user_offsets[E] = total;
     int na = nact, nt = ntile;
@@ -333,44 +349,72 @@ __global__ __launch_bounds__(256) void k_perm_scan(const int32_t* __restrict__ b
   }
 }
 
-// One wave per block, 64 routes per step.  Lanes with the same expert find
-// each other with eight ballots over the expert id bits; a lane's rank is
-// the number of lower lanes in its group.
-__global__ __launch_bounds__(64) void k_perm_scatter(const int32_t* __restrict__ ids, int R,
-                                                     int E, int k,
-                                                     const int32_t* __restrict__ block_off,
-                                                     int32_t* __restrict__ perm,
-                                                     int32_t* __restrict__ pos_of_route,
-                                                     int32_t* __restrict__ row_token,
-                                                     int32_t* __restrict__ user_perm) {
-  __shared__ int run[MOE_MAX_EXPERTS_DEV];
-  const int lane = threadIdx.x;
-  for (int e = lane; e < E; e += 64) run[e] = block_off[(size_t)blockIdx.x * E + e];
-  __syncthreads();
-  const int r0 = blockIdx.x * kPermBlock;
-  const int r1 = min(R, r0 + kPermBlock);
-  for (int base = r0; base < r1; base += 64) {
-    const int r = base + lane;
-    const bool valid = r < r1;
-    const int e = valid ? ids[r] : 0;
-    uint64_t mask = __ballot(valid);
+// Four waves per block; wave w places the routes of the block's w-th
+// quarter, 64 at a time.  Lanes with the same expert find each other with
+// eight ballots over the expert id bits; a lane's rank is the number of
+// lower lanes in its group.  The waves first count their quarter's routes
+// per expert, and each starts from the block's offset plus the counts of the
+// quarters before it, so the block stays stable.
+constexpr int kScatterWaves = 4;
+constexpr int kScatterSteps = kPermBlock / (64 * kScatterWaves);
+__global__ __launch_bounds__(64 * kScatterWaves) void k_perm_scatter(
+    const int32_t* __restrict__ ids, int R, int E, int k, const int32_t* __restrict__ block_off,
+    int32_t* __restrict__ perm, int32_t* __restrict__ pos_of_route,
+    int32_t* __restrict__ row_token, int32_t* __restrict__ user_perm) {
+  __shared__ int run[kScatterWaves][MOE_MAX_EXPERTS_DEV];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i < kScatterWaves * MOE_MAX_EXPERTS_DEV; i += 64 * kScatterWaves)
+    (&run[0][0])[i] = 0;
+  const int r0 = blockIdx.x * kPermBlock + wave * (kPermBlock / kScatterWaves);
+  int ev[kScatterSteps];
+  bool valid[kScatterSteps];
+#pragma unroll
+  for (int s = 0; s < kScatterSteps; ++s) {
+    const int r = r0 + 64 * s + lane;
+    valid[s] = r < R;
+    ev[s] = ids[min(r, R - 1)];
+  }
+  uint64_t grp[kScatterSteps];  // lanes of the same expert in step s
+#pragma unroll
+  for (int s = 0; s < kScatterSteps; ++s) {
+    const int e = valid[s] ? ev[s] : 0;
+    uint64_t mask = __ballot(valid[s]);
 #pragma unroll
     for (int bit = 0; bit < 8; ++bit) {
       const bool set = (e >> bit) & 1;
       const uint64_t b = __ballot(set);
       mask &= set ? b : ~b;
     }
-    const int rank = __popcll(mask & lanemask_lt());
-    const int pos = valid ? run[e] + rank : 0;
-    __syncthreads();
-    if (valid) {
-      if ((mask >> lane) == 1ull) run[e] += __popcll(mask);  // highest lane of its group
+    grp[s] = mask;
+  }
+  __syncthreads();
+  // counts of the wave's quarter: the highest lane of each group adds its size
+#pragma unroll
+  for (int s = 0; s < kScatterSteps; ++s)
+    if (valid[s] && (grp[s] >> lane) == 1ull) run[wave][ev[s]] += __popcll(grp[s]);
+  __syncthreads();
+  for (int e = tid; e < E; e += 64 * kScatterWaves) {
+    int b = block_off[(size_t)blockIdx.x * E + e];
+#pragma unroll
+    for (int w = 0; w < kScatterWaves; ++w) {
+      const int c = run[w][e];
+      run[w][e] = b;
+      b += c;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int s = 0; s < kScatterSteps; ++s) {
+    const int r = r0 + 64 * s + lane;
+    const int e = valid[s] ? ev[s] : 0;
+    const int pos = run[wave][e] + __popcll(grp[s] & lanemask_lt());  // read by every lane ...
+    if (valid[s]) {
+      if ((grp[s] >> lane) == 1ull) run[wave][e] += __popcll(grp[s]);  // ... before the update
       perm[pos] = r;
       pos_of_route[r] = pos;
       row_token[pos] = r / k;
       if (user_perm) user_perm[pos] = r;
     }
-    __syncthreads();
   }
 }
 
