@@ -96,23 +96,6 @@ __device__ __forceinline__ float wave_sum(float v) {
   v += dpp_f<kDppMirror>(v);
   return (readlane_f(v, 0) + readlane_f(v, 16)) + (readlane_f(v, 32) + readlane_f(v, 48));
 }
-// (value, index) arg-max over the wave: larger value wins, the lower index
-// on equal values.  Wave-uniform result.
-__device__ __forceinline__ void argmax_step(float& bv, int& bi, float pv, int pi) {
-  if (pv > bv || (pv == bv && pi < bi)) { bv = pv; bi = pi; }
-}
-__device__ __forceinline__ void wave_argmax(float& bv, int& bi) {
-  argmax_step(bv, bi, dpp_f<kDppXor1>(bv), dpp_i<kDppXor1>(bi));
-  argmax_step(bv, bi, dpp_f<kDppXor2>(bv), dpp_i<kDppXor2>(bi));
-  argmax_step(bv, bi, dpp_f<kDppHalfMirror>(bv), dpp_i<kDppHalfMirror>(bi));
-  argmax_step(bv, bi, dpp_f<kDppMirror>(bv), dpp_i<kDppMirror>(bi));
-  float v = readlane_f(bv, 0);
-  int i = __builtin_amdgcn_readlane(bi, 0);
-#pragma unroll
-  for (int r = 16; r < 64; r += 16) argmax_step(v, i, readlane_f(bv, r), __builtin_amdgcn_readlane(bi, r));
-  bv = v;
-  bi = i;
-}
 
 constexpr int kDppRowBcast15 = 0x142;  // lane 15 of each row to the next row
 constexpr int kDppRowBcast31 = 0x143;  // lane 31 to rows 2 and 3

@@ -65,27 +65,6 @@ struct SmallRouteOut {
 // weight its sigmoid gate).  The down kernel reads it with one load a lane.
 constexpr int kSlotTab = MOE_MAX_TOP_K_DEV + 2;
 
-// Order-preserving 32-bit image of a logit (-0 and +0 tie) and its inverse.
-__device__ __forceinline__ uint32_t route_ord(float l) {
-  const uint32_t u = __float_as_uint(l == 0.0f ? 0.0f : l);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-__device__ __forceinline__ float ord_logit(uint32_t ord) {
-  return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord);
-}
-
-// Maximum of v over the wave, wave-uniform: the row maximum by four DPP
-// steps, then two row broadcasts carry it to lane 63.
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-  v = max(v, (uint32_t)dpp_i<kDppXor1>((int)v));
-  v = max(v, (uint32_t)dpp_i<kDppXor2>((int)v));
-  v = max(v, (uint32_t)dpp_i<kDppHalfMirror>((int)v));
-  v = max(v, (uint32_t)dpp_i<kDppMirror>((int)v));
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, kDppRowBcast15, 0xA, 0xF, false));
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, kDppRowBcast31, 0xC, 0xF, false));
-  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
-}
-
 // One token's routing in one wave (E <= 64*C).  Lane l holds experts l,
 // l+64, ...; each of k rounds takes the wave maximum M of the order images,
 // then the lowest live expert whose image is M (one ballot per logit a lane;
@@ -96,54 +75,6 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 // and routing weight of top-k position j; `sel` returns the selected experts
 // as bit masks (expert 64c + b at bit b of sel[c]).  Every lane must take
 // part.
-static_assert(MOE_MAX_EXPERTS_DEV <= 4 * 64, "one-token ranking holds at most 4 logits a lane");
-template <int C>
-__device__ __forceinline__ void rank_load(const float* __restrict__ l, int E, float (&lv)[C],
-                                          uint32_t (&ord)[C], bool (&live)[C]) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int c = 0; c < C; ++c) {
-    const int e = lane + 64 * c;
-    const bool ok = e < E;
-    lv[c] = ok ? l[e] : 0.f;
-    ord[c] = ok ? route_ord(lv[c]) : 0u;
-    live[c] = ok;
-  }
-}
-// One round: the wave maximum M of the images and the lowest live expert e
-// whose image is M, which is then taken (wave-uniform results).
-template <int C>
-__device__ __forceinline__ int rank_round(uint32_t (&ord)[C], bool (&live)[C], uint32_t& M) {
-  const int lane = threadIdx.x & 63;
-  uint32_t m = ord[0];
-#pragma unroll
-  for (int c = 1; c < C; ++c) m = max(m, ord[c]);
-  M = wave_max_u32(m);
-  int e = 0;
-#pragma unroll
-  for (int c = C - 1; c >= 0; --c) {
-    const uint64_t hit = __ballot(live[c] && ord[c] == M);
-    e = hit != 0 ? 64 * c + __ffsll((unsigned long long)hit) - 1 : e;
-  }
-#pragma unroll
-  for (int c = 0; c < C; ++c) {
-    const bool taken = lane + 64 * c == e;
-    live[c] = live[c] && !taken;
-    ord[c] = taken ? 0u : ord[c];
-  }
-  return e;
-}
-// The expert at top-k position n - 1 (n >= 1): the first n rounds alone.
-template <int C>
-__device__ __forceinline__ int rank_nth(const float* __restrict__ l, int E, int n) {
-  float lv[C];
-  uint32_t ord[C], M;
-  bool live[C];
-  rank_load<C>(l, E, lv, ord, live);
-  int e = 0;
-  for (int j = 0; j < n; ++j) e = rank_round<C>(ord, live, M);
-  return e;
-}
 template <int C>
 __device__ __forceinline__ void route_one_token(const float* __restrict__ l, int E, int k,
                                                 RouteMode rm, int& id, float& w,

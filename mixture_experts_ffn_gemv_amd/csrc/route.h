@@ -119,6 +119,79 @@ __device__ __forceinline__ float expert_scale_of(const RouteMode& rm, int e) {
 }
 
 // --------------------------------------------------------------------------
+// Ranking of one token's logits by one wave.
+// --------------------------------------------------------------------------
+// Order-preserving 32-bit image of a logit (-0 and +0 tie) and its inverse.
+__device__ __forceinline__ uint32_t route_ord(float l) {
+  const uint32_t u = __float_as_uint(l == 0.0f ? 0.0f : l);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float ord_logit(uint32_t ord) {
+  return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord);
+}
+
+// Maximum of v over the wave, wave-uniform: the row maximum by four DPP
+// steps, then two row broadcasts carry it to lane 63.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)dpp_i<kDppXor1>((int)v));
+  v = max(v, (uint32_t)dpp_i<kDppXor2>((int)v));
+  v = max(v, (uint32_t)dpp_i<kDppHalfMirror>((int)v));
+  v = max(v, (uint32_t)dpp_i<kDppMirror>((int)v));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, kDppRowBcast15, 0xA, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, kDppRowBcast31, 0xC, 0xF, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+static_assert(MOE_MAX_EXPERTS_DEV <= 4 * 64, "one-token ranking holds at most 4 logits a lane");
+template <int C>
+__device__ __forceinline__ void rank_load(const float* __restrict__ l, int E, float (&lv)[C],
+                                          uint32_t (&ord)[C], bool (&live)[C]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    const int e = lane + 64 * c;
+    const bool ok = e < E;
+    lv[c] = ok ? l[e] : 0.f;
+    ord[c] = ok ? route_ord(lv[c]) : 0u;
+    live[c] = ok;
+  }
+}
+// One round: the wave maximum M of the images and the lowest live expert e
+// whose image is M, which is then taken (wave-uniform results).
+template <int C>
+__device__ __forceinline__ int rank_round(uint32_t (&ord)[C], bool (&live)[C], uint32_t& M) {
+  const int lane = threadIdx.x & 63;
+  uint32_t m = ord[0];
+#pragma unroll
+  for (int c = 1; c < C; ++c) m = max(m, ord[c]);
+  M = wave_max_u32(m);
+  int e = 0;
+#pragma unroll
+  for (int c = C - 1; c >= 0; --c) {
+    const uint64_t hit = __ballot(live[c] && ord[c] == M);
+    e = hit != 0 ? 64 * c + __ffsll((unsigned long long)hit) - 1 : e;
+  }
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    const bool taken = lane + 64 * c == e;
+    live[c] = live[c] && !taken;
+    ord[c] = taken ? 0u : ord[c];
+  }
+  return e;
+}
+// The expert at top-k position n - 1 (n >= 1): the first n rounds alone.
+template <int C>
+__device__ __forceinline__ int rank_nth(const float* __restrict__ l, int E, int n) {
+  float lv[C];
+  uint32_t ord[C], M;
+  bool live[C];
+  rank_load<C>(l, E, lv, ord, live);
+  int e = 0;
+  for (int j = 0; j < n; ++j) e = rank_round<C>(ord, live, M);
+  return e;
+}
+
+// --------------------------------------------------------------------------
 // Softmax (or sigmoid) -> top-k -> renormalise, one wave per token.
 // Selection is on the logits: softmax is monotone, so the k most probable
 // experts are the k largest logits, with the lower index first on a tie.
@@ -140,34 +213,35 @@ __device__ __forceinline__ float split_sum(const float* l, int e, int nsplit, si
   for (int z = 1; z < nsplit; ++z) v += l[z * sstride + e];
   return v;
 }
+template <int C>
 __device__ __forceinline__ void topk_token(const float* l, int nsplit, size_t sstride, int t, int E,
-                                           int k, RouteMode rm,
-                                           int has_shared, int32_t* __restrict__ ids,
-                                           float* __restrict__ wts, int32_t* __restrict__ user_ids,
+                                           int k, RouteMode rm, int has_shared,
+                                           int32_t* __restrict__ ids, float* __restrict__ wts,
+                                           int32_t* __restrict__ user_ids,
                                            float* __restrict__ user_w, float* __restrict__ sgate) {
   const int lane = threadIdx.x & 63;
-  float v[4];
-  unsigned taken = 0;  // bit q: candidate q of this lane is used up (or absent)
+  float v[C];
+  uint32_t ord[C];
+  bool live[C];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
+  for (int q = 0; q < C; ++q) {
     const int e = lane + 64 * q;
-    v[q] = (e < E) ? split_sum(l, e, nsplit, sstride) : -INFINITY;
-    if (e >= E) taken |= 1u << q;
+    live[q] = e < E;
+    v[q] = live[q] ? split_sum(l, e, nsplit, sstride) : 0.f;
+    ord[q] = live[q] ? route_ord(v[q]) : 0u;
   }
   int my_id = 0;
-  float my_val = -INFINITY;
+  uint32_t my_ord = 0, top = 0;
   for (int j = 0; j < k; ++j) {
-    float bv = -INFINITY;
-    int bi = 0x7FFFFFFF;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      if (!((taken >> q) & 1u) && (v[q] > bv || bi == 0x7FFFFFFF)) { bv = v[q]; bi = lane + 64 * q; }
+    uint32_t M;
+    const int e = rank_round<C>(ord, live, M);
+    if (j == 0) top = M;
+    if (lane == j) {
+      my_id = e;
+      my_ord = M;
     }
-    wave_argmax(bv, bi);
-    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-    if (lane == j) { my_id = bi; my_val = bv; }
   }
-  const float lmax = __shfl(my_val, 0, 64);
+  const float my_val = ord_logit(my_ord), lmax = ord_logit(top);
   const float ex = (lane < k) ? (rm.sigmoid ? sigmoid_f(my_val) : __expf(my_val - lmax)) *
                                     expert_scale_of(rm, my_id)
                               : 0.f;
@@ -179,7 +253,7 @@ __device__ __forceinline__ void topk_token(const float* l, int nsplit, size_t ss
   } else {
     float s = 0.f;
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int q = 0; q < C; ++q)
       if (lane + 64 * q < E) s += __expf(v[q] - lmax);
     denom = wave_sum(s);
   }
@@ -200,9 +274,15 @@ __global__ __launch_bounds__(256) void k_topk(
     float* __restrict__ user_w, float* __restrict__ sgate) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  topk_token(logits + (size_t)t * ncols, nsplit, sstride, t, E, k, rm, has_shared, ids, wts,
-             user_ids, user_w,
-             sgate);
+  const float* l = logits + (size_t)t * ncols;
+  if (E <= 64)
+    topk_token<1>(l, nsplit, sstride, t, E, k, rm, has_shared, ids, wts, user_ids, user_w, sgate);
+  else if (E <= 128)
+    topk_token<2>(l, nsplit, sstride, t, E, k, rm, has_shared, ids, wts, user_ids, user_w, sgate);
+  else if (E <= 192)
+    topk_token<3>(l, nsplit, sstride, t, E, k, rm, has_shared, ids, wts, user_ids, user_w, sgate);
+  else
+    topk_token<4>(l, nsplit, sstride, t, E, k, rm, has_shared, ids, wts, user_ids, user_w, sgate);
 }
 
 // --------------------------------------------------------------------------
