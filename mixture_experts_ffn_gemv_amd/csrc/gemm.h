@@ -91,8 +91,11 @@ __device__ __forceinline__ void grouped_tile(int L, int ntt, int nnt, int& tt, i
   nt = r / gt;
 }
 
-// Prefill router: logits[t, c] = x[t, :] . Wr[c, :] (+ bias[c] for c < E),
-// column E (with a shared expert) the shared gate vector.  K is split into
+// Prefill router: logits[t, c] = x[t, :] . Wr[c, :] (+ bias[c] for c < E)
+// for the first nw columns of rows ncols floats apart; column E (with a
+// shared expert) would be the shared gate vector, but the top-k kernel takes
+// that one dot product per token itself, so nw = E and no column tile is
+// spent on it.  K is split into
 // nsplit equal ranges (grid z): range z writes its partial dot products to
 // logits + z * split_stride (the bias goes with range 0), and the top-k
 // kernel adds the ranges in order, so more workgroups share a short K loop
@@ -110,6 +113,7 @@ struct RouterParams {
   const float* bias;       // [E] or null
   float* logits;           // [nsplit, T, ncols] partial logits
   int T, H, E, ncols;
+  int nw;                  // logit columns computed (the first nw of each row)
   int nsplit;              // K ranges (H / 64 a multiple of it)
   size_t split_stride;     // floats between the ranges' partial logits
 };
@@ -141,7 +145,7 @@ __global__ __launch_bounds__(256) void k_router_mfma(RouterParams p) {
     const int q = tid + 256 * i;
     const int row = q >> 3, ck = q & 7;
     lds_off[i] = swz(row, ck);
-    const int e = min(n0 + row, p.ncols - 1);
+    const int e = min(n0 + row, p.nw - 1);
     a_src[i] = ((e < p.E) ? p.wr + (size_t)e * K : p.wsg) + k0 + ck * 8;
     const int m = min(m0 + row, p.T - 1);
     b_src[i] = p.x + (size_t)m * K + k0 + ck * 8;
@@ -231,7 +235,7 @@ __global__ __launch_bounds__(256) void k_router_mfma(RouterParams p) {
     for (int idx = tid; idx < (kTileT / 2) * kTileW; idx += 256) {
       const int r = idx / kTileW, c = idx - r * kTileW;
       const int m = m0 + (kTileT / 2) * h + r, e = n0 + c;
-      if (m < p.T && e < p.ncols)
+      if (m < p.T && e < p.nw)
         outz[(size_t)m * p.ncols + e] = ep[r * kRouterEpStride + c] + ((e < p.E && add_bias) ? p.bias[e] : 0.f);
     }
     __syncthreads();

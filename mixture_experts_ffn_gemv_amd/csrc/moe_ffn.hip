@@ -174,7 +174,7 @@ Plan make_plan(const moe_desc* d, int64_t T) {
     // fewer router tiles than compute units: split K until there are about
     // as many workgroups (each range keeps at least 8 K steps); more tiles
     // gain nothing from it and would only give the top-k more partial rows
-    const int64_t tiles = ((T + kTileT - 1) / kTileT) * ((p.ncols + kTileW - 1) / kTileW);
+    const int64_t tiles = ((T + kTileT - 1) / kTileT) * ((p.E + kTileW - 1) / kTileW);
     const int nk = p.H / kTileK;
     while (tiles * p.rsplit < 256 && nk % (2 * p.rsplit) == 0 && nk / (2 * p.rsplit) >= 8)
       p.rsplit *= 2;
@@ -306,8 +306,8 @@ moe_status run_router(const moe_desc* d, const Plan& p, const void* x, const moe
   if (p.mfma) {
     RouterParams rp{static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w->router),
                     static_cast<const uint16_t*>(w->shared_gate_inp), w->router_bias, logits,
-                    T, p.H, p.E, p.ncols, p.rsplit, (size_t)T * p.ncols};
-    dim3 grid((T + kTileT - 1) / kTileT, (p.ncols + kTileW - 1) / kTileW, p.rsplit);
+                    T, p.H, p.E, p.ncols, p.E, p.rsplit, (size_t)T * p.ncols};
+    dim3 grid((T + kTileT - 1) / kTileT, (p.E + kTileW - 1) / kTileW, p.rsplit);
     return launch("router_mfma", s, [&] { k_router_mfma<<<grid, 256, 0, s>>>(rp); });
   }
   const bool xb = d->act_dtype == MOE_BF16, rb = d->router_dtype == MOE_BF16;
@@ -368,8 +368,11 @@ moe_status run_route_small(const moe_desc* d, const Plan& p, const void* x, cons
   });
 }
 
-moe_status run_route_and_group(const moe_desc* d, const Plan& p, const moe_weights* w, void* ws,
-                               int32_t* user_ids,
+// x: the rows the router read; with the MFMA router the top-k kernel takes
+// the shared gate's logit from them (the router computes the E expert
+// columns only).
+moe_status run_route_and_group(const moe_desc* d, const Plan& p, const void* x,
+                               const moe_weights* w, void* ws, int32_t* user_ids,
                                float* user_w, int32_t* user_counts, int32_t* user_offsets,
                                int32_t* user_perm, hipStream_t s) {
   const int T = (int)p.T, R = (int)p.R;
@@ -377,6 +380,8 @@ moe_status run_route_and_group(const moe_desc* d, const Plan& p, const moe_weigh
     k_topk<<<(T + 3) / 4, 256, 0, s>>>(wsp<float>(ws, p.o_logits), p.rsplit, (size_t)T * p.ncols,
                                        T, p.E, p.k, p.ncols,
                                        route_mode(d, w), p.shared ? 1 : 0,
+                                       p.mfma && p.shared ? static_cast<const uint16_t*>(x) : nullptr,
+                                       static_cast<const uint16_t*>(w->shared_gate_inp), p.H,
                                        wsp<int32_t>(ws, p.o_ids), wsp<float>(ws, p.o_wts),
                                        user_ids, user_w, wsp<float>(ws, p.o_sgate));
   }));
@@ -944,7 +949,7 @@ moe_status forward_body(const moe_desc* desc, const Plan& p, int64_t num_tokens,
     return run_experts_small(desc, p, x, weights, out, residual, ws, s);
   }
   MOE_TRY(run_router(desc, p, x, weights, ws, s));
-  MOE_TRY(run_route_and_group(desc, p, weights, ws, topk_ids_out, topk_w_out, nullptr, nullptr,
+  MOE_TRY(run_route_and_group(desc, p, x, weights, ws, topk_ids_out, topk_w_out, nullptr, nullptr,
                               nullptr, s));
   if (p.mfma) return run_experts_mfma(desc, p, x, weights, out, residual, ws, s);
   return run_experts_gemv(desc, p, x, weights, out, residual, ws, s);
@@ -1038,7 +1043,7 @@ moe_status moe_route(const moe_desc* desc, int64_t num_tokens, const void* x,
     return run_route_small(desc, p, x, weights, ws, topk_ids, topk_w, expert_counts,
                            expert_offsets, route_perm, s);
   MOE_TRY(run_router(desc, p, x, weights, ws, s));
-  return run_route_and_group(desc, p, weights, ws, topk_ids, topk_w, expert_counts,
+  return run_route_and_group(desc, p, x, weights, ws, topk_ids, topk_w, expert_counts,
                              expert_offsets, route_perm, s);
 }
 

@@ -213,9 +213,14 @@ __device__ __forceinline__ float split_sum(const float* l, int e, int nsplit, si
   for (int z = 1; z < nsplit; ++z) v += l[z * sstride + e];
   return v;
 }
+// The shared expert's gate logit is column E of the logits, or, when gx is
+// set (bf16 rows x and gate vector gw of length H, a multiple of 8), the dot
+// product taken here by the wave: lane l takes 8-element chunks l, l + 64, ...
 template <int C>
 __device__ __forceinline__ void topk_token(const float* l, int nsplit, size_t sstride, int t, int E,
                                            int k, RouteMode rm, int has_shared,
+                                           const uint16_t* __restrict__ gx,
+                                           const uint16_t* __restrict__ gw, int H,
                                            int32_t* __restrict__ ids, float* __restrict__ wts,
                                            int32_t* __restrict__ user_ids,
                                            float* __restrict__ user_w, float* __restrict__ sgate) {
@@ -264,25 +269,55 @@ __device__ __forceinline__ void topk_token(const float* l, int nsplit, size_t ss
     if (user_ids) user_ids[(size_t)t * k + lane] = my_id;
     if (user_w) user_w[(size_t)t * k + lane] = w;
   }
-  if (has_shared && lane == 0) sgate[t] = sigmoid_f(split_sum(l, E, nsplit, sstride));
+  if (has_shared) {
+    float g;
+    if (gx) {
+      const uint16_t* xr = gx + (size_t)t * H;
+      float d = 0.f;
+      constexpr int U = 4;  // chunks a lane loads at once (clamped, so no load is behind a branch)
+      for (int c0 = lane * 8; c0 < H; c0 += U * 64 * 8) {
+        u32x4 a[U], b[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int c = min(c0 + u * 64 * 8, H - 8);
+          a[u] = ld16(xr + c);
+          b[u] = ld16(gw + c);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          if (c0 + u * 64 * 8 < H) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              d = fmaf(bf16lo(a[u][q]), bf16lo(b[u][q]), d);
+              d = fmaf(bf16hi(a[u][q]), bf16hi(b[u][q]), d);
+            }
+          }
+        }
+      }
+      g = wave_sum(d);
+    } else {
+      g = split_sum(l, E, nsplit, sstride);
+    }
+    if (lane == 0) sgate[t] = sigmoid_f(g);
+  }
 }
 
 __global__ __launch_bounds__(256) void k_topk(
     const float* __restrict__ logits, int nsplit, size_t sstride, int T, int E, int k, int ncols,
-    RouteMode rm, int has_shared, int32_t* __restrict__ ids,
+    RouteMode rm, int has_shared, const uint16_t* __restrict__ gx,
+    const uint16_t* __restrict__ gw, int H, int32_t* __restrict__ ids,
     float* __restrict__ wts, int32_t* __restrict__ user_ids,
     float* __restrict__ user_w, float* __restrict__ sgate) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const float* l = logits + (size_t)t * ncols;
-  if (E <= 64)
-    topk_token<1>(l, nsplit, sstride, t, E, k, rm, has_shared, ids, wts, user_ids, user_w, sgate);
-  else if (E <= 128)
-    topk_token<2>(l, nsplit, sstride, t, E, k, rm, has_shared, ids, wts, user_ids, user_w, sgate);
-  else if (E <= 192)
-    topk_token<3>(l, nsplit, sstride, t, E, k, rm, has_shared, ids, wts, user_ids, user_w, sgate);
-  else
-    topk_token<4>(l, nsplit, sstride, t, E, k, rm, has_shared, ids, wts, user_ids, user_w, sgate);
+#define MOE_TOPK(C) \
+  topk_token<C>(l, nsplit, sstride, t, E, k, rm, has_shared, gx, gw, H, ids, wts, user_ids, user_w, sgate)
+  if (E <= 64) MOE_TOPK(1);
+  else if (E <= 128) MOE_TOPK(2);
+  else if (E <= 192) MOE_TOPK(3);
+  else MOE_TOPK(4);
+#undef MOE_TOPK
 }
 
 // --------------------------------------------------------------------------
