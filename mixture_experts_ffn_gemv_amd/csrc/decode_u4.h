@@ -63,11 +63,25 @@ __host__ __device__ constexpr int u4_lds_bytes(int K, int UG, int nslot) {
   return nslot * u4_route_stride(K / 32) + (K / 32) * 16 + 64 + kU4Waves * 512 * UG;
 }
 
-// (w & mask) | magic in one instruction: the VOP3 form takes no literal, so
-// the mask comes from a scalar register and the magic from a vector one.
+// (w & mask) | magic: one v_and_or_b32.  It is plain code, not inline
+// assembly, so that the compiler knows which registers it writes and keeps
+// the wait states the MFMAs need around them (an asm block that overwrote a
+// register an MFMA still reads would go unseen).  The VOP3 form takes no
+// literal: the two constants come from registers the compiler cannot fold
+// (opaque_s, opaque_v), the mask scalar and the magic vector.
 __device__ __forceinline__ uint32_t and_or(uint32_t w, uint32_t mask, uint32_t magic) {
+  return (w & mask) | magic;
+}
+// A constant in a scalar or vector register, hidden from constant folding.
+// Only ALU instructions read these, so the asm blocks meet no MFMA hazard.
+__device__ __forceinline__ uint32_t opaque_s(uint32_t v) {
   uint32_t r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(w), "s"(mask), "v"(magic));
+  asm volatile("s_mov_b32 %0, %1" : "=s"(r) : "i"(v));
+  return r;
+}
+__device__ __forceinline__ uint32_t opaque_v(uint32_t v) {
+  uint32_t r;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "i"(v));
   return r;
 }
 
@@ -346,7 +360,8 @@ void k_u4_mfma(U4Experts ep) {
   float fac[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) fac[i] = rfac[i];
-  const uint32_t magic = 0x64006400u;
+  const uint32_t magic = opaque_v(0x64006400u);
+  const uint32_t mlo = opaque_s(0x000F000Fu), mhi = opaque_s(0x00F000F0u);
 
   // per route: sum over groups of s * D (aS) and of m * group sum (aM)
   float aS0[4], aM0[4], aS1[4], aM1[4];
@@ -370,10 +385,10 @@ void k_u4_mfma(U4Experts ep) {
         const uint32_t w0 = va[uu][q], w1 = vb[uu][q];
         const uint32_t w08 = w0 >> 8, w18 = w1 >> 8;
         // codes (0, 4, 2, 6) and 16 x codes (1, 5, 3, 7) of word q
-        const f16x4 b0e = codes4(and_or(w0, 0x000F000Fu, magic), and_or(w08, 0x000F000Fu, magic));
-        const f16x4 b0o = codes4(and_or(w0, 0x00F000F0u, magic), and_or(w08, 0x00F000F0u, magic));
-        const f16x4 b1e = codes4(and_or(w1, 0x000F000Fu, magic), and_or(w18, 0x000F000Fu, magic));
-        const f16x4 b1o = codes4(and_or(w1, 0x00F000F0u, magic), and_or(w18, 0x00F000F0u, magic));
+        const f16x4 b0e = codes4(and_or(w0, mlo, magic), and_or(w08, mlo, magic));
+        const f16x4 b0o = codes4(and_or(w0, mhi, magic), and_or(w08, mhi, magic));
+        const f16x4 b1e = codes4(and_or(w1, mlo, magic), and_or(w18, mlo, magic));
+        const f16x4 b1o = codes4(and_or(w1, mhi, magic), and_or(w18, mhi, magic));
         const f16x4 ahe = __builtin_bit_cast(f16x4, u32x2{pe[0], pe[1]});
         const f16x4 ale = __builtin_bit_cast(f16x4, u32x2{pe[2], pe[3]});
         const f16x4 aho = __builtin_bit_cast(f16x4, u32x2{po[0], po[1]});
