@@ -35,6 +35,11 @@ Prints one JSON line.  Fields beyond the common contract:
                 replays, the gate/up GEMM's TFLOP/s and the fractions of
                 the bf16 MFMA and HBM peaks, for the GEMM and the step
   cpu_baseline  the float64 CPU oracle timed on a bounded sample of tokens
+  measured_peaks
+                what this GPU sustains with library routines, as context for
+                the fractions (which use the published peaks): a 1 GiB
+                device copy (GB/s, bytes read plus written) and a bf16
+                8192^3 matrix product through torch (TFLOP/s)
 """
 from __future__ import annotations
 
@@ -92,10 +97,49 @@ def parse():
                     help="prefill workloads timed after the main one, reported under "
                          "prefill_t<T> keys ('none': skip)")
     ap.add_argument("--prefill-steps", type=int, default=10)
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the copy and bf16 matrix product peak measurements")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="first run one plain device copy of this many MiB (a kernel of known "
                          "traffic, to scale hardware byte counters)")
     return ap.parse_args()
+
+
+def measured_peaks(dev, iters=20):
+    """Sustained bandwidth and bf16 matrix throughput of this GPU measured
+    with library routines (a device copy, a matrix product), each the mean
+    over `iters` back-to-back calls bracketed by events."""
+    import torch
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / iters
+
+    nb = 1 << 30
+    a = torch.ones(nb // 4, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    copy_s = timed(lambda: b.copy_(a))
+    del a, b
+    m = 8192
+    x = torch.randn(m, m, device=dev, dtype=torch.bfloat16)
+    y = torch.randn(m, m, device=dev, dtype=torch.bfloat16)
+    z = torch.empty(m, m, device=dev, dtype=torch.bfloat16)
+    mm_s = timed(lambda: torch.matmul(x, y, out=z))
+    del x, y, z
+    torch.cuda.empty_cache()
+    return {"copy_gbs": round(2 * nb / copy_s / 1e9, 1),
+            "bf16_gemm_tflops": round(2 * m ** 3 / mm_s / 1e12, 1),
+            "how": "1 GiB f32 device copy (bytes read + written) and bf16 8192x8192x8192 "
+                   "torch.matmul, mean of 20 back-to-back calls each"}
 
 
 def bytes_per_weight(wf):
@@ -570,6 +614,8 @@ def main():
         for name in args.prefill.split(","):
             pf = bench_prefill(M, name, args.prefill_steps, 2, dev)
             line[f"prefill_t{CONFIGS[name].T}"] = pf
+    if not args.no_peaks:
+        line["measured_peaks"] = measured_peaks(dev)
     print(json.dumps(line), flush=True)
 
 
