@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define MOE_FFN_ABI_VERSION 7
+#define MOE_FFN_ABI_VERSION 8
 
 /* Leading workspace bytes that must be zero before a workspace's first use. */
 #define MOE_WORKSPACE_ZERO_BYTES 256
@@ -135,6 +135,11 @@ typedef struct moe_desc {
                                   * norm_weight, rounded to act_dtype;
                                   0: on x as given                          */
   float norm_eps;              /* > 0 when pre_norm, else ignored            */
+  int32_t out_dtype;           /* moe_dtype of out: MOE_F32, the fp32 output
+                                  of mlx-native's weighted-sum accumulator
+                                  and of hf2q's layer (MOE_BF16 is
+                                  UNSUPPORTED: no reduced-precision output
+                                  is built)                                 */
 } moe_desc;
 
 typedef struct moe_u4_matrix {

@@ -52,7 +52,7 @@ class Desc(ctypes.Structure):
         "act_dtype", "router_dtype", "normalize_topk", "has_shared_expert",
         "shared_intermediate", "group_size", "gating")] + [
         ("routed_scale", ctypes.c_float), ("pre_norm", ctypes.c_int32),
-        ("norm_eps", ctypes.c_float)]
+        ("norm_eps", ctypes.c_float), ("out_dtype", ctypes.c_int32)]
 
 
 class U4Matrix(ctypes.Structure):
@@ -127,12 +127,13 @@ def _check(status: int):
 def make_desc(hidden, intermediate, num_experts, top_k, activation=ACT_SILU,
               weight_format=WEIGHTS_BF16, act_dtype=DT_F32, router_dtype=DT_F32,
               normalize_topk=True, shared_intermediate=0, group_size=32,
-              gating=GATING_SOFTMAX, routed_scale=1.0, norm_eps=None) -> Desc:
-    """``norm_eps`` (a float) turns on the pre-FFN RMSNorm (weights need norm_weight)."""
+              gating=GATING_SOFTMAX, routed_scale=1.0, norm_eps=None, out_dtype=DT_F32) -> Desc:
+    """``norm_eps`` (a float) turns on the pre-FFN RMSNorm (weights need norm_weight);
+    ``out_dtype``: the output's dtype (only DT_F32 is supported)."""
     return Desc(hidden, intermediate, num_experts, top_k, activation, weight_format, act_dtype,
                 router_dtype, int(bool(normalize_topk)), int(shared_intermediate > 0),
                 shared_intermediate, group_size, gating, routed_scale,
-                int(norm_eps is not None), 0.0 if norm_eps is None else norm_eps)
+                int(norm_eps is not None), 0.0 if norm_eps is None else norm_eps, out_dtype)
 
 
 def _ptr(t) -> Optional[int]:

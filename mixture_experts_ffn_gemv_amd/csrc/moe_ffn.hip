@@ -108,6 +108,10 @@ moe_status check_desc(const moe_desc* d) {
     return fail(MOE_INVALID_ARGUMENT, "routed_scale must be finite");
   if (d->pre_norm != 0 && d->pre_norm != 1)
     return fail(MOE_INVALID_ARGUMENT, "pre_norm must be 0 or 1");
+  if (d->out_dtype != MOE_F32 && d->out_dtype != MOE_BF16)
+    return fail(MOE_INVALID_ARGUMENT, "unknown out_dtype %d", d->out_dtype);
+  if (d->out_dtype != MOE_F32)
+    return fail(MOE_UNSUPPORTED, "only f32 output (out_dtype MOE_F32) is built");
   if (d->pre_norm && !(std::isfinite(d->norm_eps) && d->norm_eps > 0.f))
     return fail(MOE_INVALID_ARGUMENT, "norm_eps must be finite and positive");
   if (d->has_shared_expert != 0 && d->has_shared_expert != 1)

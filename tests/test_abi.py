@@ -35,7 +35,7 @@ def test_header_declares_the_bound_functions():
 def test_library_exports_every_declared_symbol(lib):
     for name in _declared_functions():
         assert hasattr(lib, name), name
-    assert lib.moe_abi_version() == 7
+    assert lib.moe_abi_version() == 8
 
 
 def _desc(name="decode_geglu_t1", **over):
@@ -59,7 +59,7 @@ def test_workspace_size_grows_affinely(lib):
     ("hidden", 0), ("intermediate", -32), ("num_experts", 0), ("num_experts", 257),
     ("top_k", 0), ("top_k", 129), ("activation", 5), ("weight_format", 7), ("act_dtype", 3),
     ("normalize_topk", 2), ("gating", 2), ("gating", -1), ("routed_scale", float("inf")),
-    ("routed_scale", float("nan")), ("pre_norm", 2)])
+    ("routed_scale", float("nan")), ("pre_norm", 2), ("out_dtype", 2), ("out_dtype", -1)])
 def test_bad_descriptor_is_invalid_argument(lib, field, value):
     d = _desc()
     setattr(d, field, value)          # raw field: bypass make_desc's coercions
@@ -67,6 +67,14 @@ def test_bad_descriptor_is_invalid_argument(lib, field, value):
     st = lib.moe_workspace_size(ctypes.byref(d), 1, ctypes.byref(n))
     assert st == M.MOE_INVALID_ARGUMENT
     assert lib.moe_last_error().decode() != ""
+
+
+def test_bf16_output_unsupported(lib):
+    d = _desc()
+    d.out_dtype = M.DT_BF16
+    n = ctypes.c_size_t(0)
+    assert lib.moe_workspace_size(ctypes.byref(d), 1, ctypes.byref(n)) == M.MOE_UNSUPPORTED
+    assert "out_dtype" in lib.moe_last_error().decode()
 
 
 def test_top_k_above_32_rejected(lib):
