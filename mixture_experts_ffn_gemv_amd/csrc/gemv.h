@@ -301,7 +301,7 @@ __global__ __launch_bounds__(256) void k_combine_bf16x8(const uint16_t* __restri
     for (int jj = 0; jj < 8; ++jj) {
       const int j = min(j0 + jj, k - 1);
       const size_t pos = pos_of_route[(size_t)t * k + j];
-      v[jj] = *reinterpret_cast<const u32x4*>(y + pos * H + c);
+      v[jj] = ld16_stream(y + pos * H + c);  // each y row is read once
       w[jj] = (j0 + jj < k) ? wts[(size_t)t * k + j] : 0.f;
     }
 #pragma unroll
