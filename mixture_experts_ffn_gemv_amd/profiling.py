@@ -13,6 +13,11 @@ Usage:
       --out profiles/traffic.json
   python -m mixture_experts_ffn_gemv_amd.profiling stats --csv FILE
   python -m mixture_experts_ffn_gemv_amd.profiling counters --dir DIR
+  python -m mixture_experts_ffn_gemv_amd.profiling parity --log FILE
+
+parity: the GPU parity tests append one JSON line per compared case to the
+file MOE_PARITY_LOG names; this prints them as a table (largest error
+relative to its tolerance first).
 """
 from __future__ import annotations
 
@@ -183,6 +188,26 @@ def cmd_counters(a) -> None:
             print(f"| `{k}` | " + " | ".join(f"{d[x]:.4g}" if x in d else "" for x in keys) + " |")
 
 
+def cmd_parity(a) -> None:
+    """Markdown table of the per-case errors a GPU parity run logged."""
+    rows = []
+    with open(a.log) as fh:
+        for line in fh:
+            if line.strip():
+                rows.append(json.loads(line))
+    rows.sort(key=lambda r: -(r["out_err"] / r["tol"]))
+    worst = rows[0]["out_err"] / rows[0]["tol"] if rows else float("nan")
+    print(f"{len(rows)} comparisons, {len({r['case'] for r in rows})} cases; "
+          f"largest error / tolerance {worst:.3g}")
+    print()
+    print("| case | T | tokens compared | max rel err | tolerance | err / tol | routing weight err |")
+    print("|---|---|---|---|---|---|---|")
+    for r in rows:
+        w = r.get("w_err")
+        print(f"| {r['case']} | {r['T']} | {r['tokens']} | {r['out_err']:.3g} | {r['tol']:g} | "
+              f"{r['out_err'] / r['tol']:.3g} | {'' if w is None else f'{w:.2g}'} |")
+
+
 def main() -> None:
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -198,8 +223,11 @@ def main() -> None:
     c = sub.add_parser("counters")
     c.add_argument("--dir", required=True, help="output directory of one --pmc pass")
     c.add_argument("--cus", type=int, default=256, help="compute units of the GPU")
+    q = sub.add_parser("parity")
+    q.add_argument("--log", required=True, help="the MOE_PARITY_LOG file of a GPU test run")
     a = ap.parse_args()
-    {"traffic": cmd_traffic, "stats": cmd_stats, "counters": cmd_counters}[a.cmd](a)
+    {"traffic": cmd_traffic, "stats": cmd_stats, "counters": cmd_counters,
+     "parity": cmd_parity}[a.cmd](a)
 
 
 if __name__ == "__main__":
