@@ -12,7 +12,8 @@
 // two 32 KB LDS slots; the weight operand two or three (RA): three when its
 // bytes stream from HBM once per launch (experts average fewer routes than a
 // tile holds), so that two of its K-steps are in flight while one is
-// multiplied.
+// multiplied.  Weight loads carry the streaming (nt) cache policy, route
+// loads the default one, so that L2 keeps the gathered token rows.
 //
 // Each load instruction of a wave fills 1 KB of LDS, lane i writing bytes
 // 16i..16i+15 of it.  A swizzled layout (16-byte chunk c of row r at slot
@@ -200,12 +201,12 @@ __global__ __launch_bounds__(kDmaThreads, 1) void k_gemm_dma(GemmParams p) {
   auto issue_a = [&](int kt, int slot) {
     const uint32_t sb = lds0 + (uint32_t)(slot * REGION);
     const size_t koa = (size_t)kt * a_step;
-#pragma unroll
     // Weight loads are streaming: they are read once a launch (RA = 3) or
     // shared only by the workgroups that run a weight tile together, while
     // the gathered route rows are re-read by every weight tile of their
     // group.  Measured: 4k tokens 525 -> 492 us a step, 16k 12.6 -> 12.45 ms
     // (streaming route loads as well: 572 us and 15.8 ms).
+#pragma unroll
     for (int h = 0; h < NH; ++h)
       lds_dma16<true>(a_off[h], a_base[h] + koa, sb + (wave + NW * h) * 1024);
   };
